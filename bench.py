@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = one attn_fwd call over the whole workload (every query row of
+every head), inputs already resident in HBM.  Default workload: long-context
+causal GQA-4, B=1, H_q=32, H_kv=8, N=32768, D=128, bf16 i.i.d. N(0,1).
+
+Prints ONE JSON line with the throughput in attention TFLOP/s
+(4*B*H_q*N^2*D, halved for causal), the roofline of the kernel (MFMA-bound:
+achieved TFLOP/s per launch from HIP events on the launch stream, against the
+2.5 PFLOP/s dense bf16 peak), a CPU baseline (the float64 oracle on a bounded
+sample of the same workload, on the host's cores) and a sampled-row parity
+check of the timed output against the oracle.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd TFLOPS and % of MI355X bf16 MFMA peak (GQA causal, N=1K–32K)"
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_02_amd", "csrc", f)
+                  for f in ("attn_fwd_kernel.hpp", "attn_abi.hip")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_b or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+# ---------------------------------------------------------------- CPU baseline
+def _oracle_unit(args):
+    from threadpoolctl import threadpool_limits
+    import oracle
+    q, k, v, b, h, rows, causal, scale = args
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oracle.attention_rows(q, k, v, b, h, rows, is_causal=causal, sm_scale=scale)
+        return time.perf_counter() - t0
+
+
+_G = {}
+
+
+def _init_worker(q, k, v):
+    _G["qkv"] = (q, k, v)
+
+
+def _oracle_unit_shared(args):
+    q, k, v = _G["qkv"]
+    return _oracle_unit((q, k, v) + tuple(args))
+
+
+def cpu_baseline(w, q64, k64, v64, budget_s=15.0):
+    """Time the oracle on random 512-row blocks of random heads until about
+    budget_s of wall time is used, over a process pool of one worker per core."""
+    cores = len(os.sched_getaffinity(0))
+    cores = max(1, min(cores, 16))
+    rng = np.random.default_rng(12345)
+    blk = 512
+    n_blocks = (w.N + blk - 1) // blk
+    flops = 0.0
+    done = 0
+    t0 = time.perf_counter()
+    ctx = __import__("multiprocessing").get_context("fork")
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx, initializer=_init_worker,
+                                initargs=(q64, k64, v64)) as ex:
+        pending = set()
+        submitted = 0
+
+        def submit():
+            nonlocal submitted
+            b = int(rng.integers(w.B))
+            h = int(rng.integers(w.H_q))
+            r0 = int(rng.integers(n_blocks)) * blk
+            rows = np.arange(r0, min(r0 + blk, w.N))
+            f = ex.submit(_oracle_unit_shared, (b, h, rows, w.causal, w.sm_scale))
+            vis = (rows + 1).sum() if w.causal else rows.size * w.N
+            pending.add((f, 4.0 * w.D * float(vis)))
+            submitted += 1
+
+        for _ in range(2 * cores):
+            submit()
+        while pending:
+            fs = {f for f, _ in pending}
+            finished, _ = cf.wait(fs, return_when=cf.FIRST_COMPLETED)
+            for item in list(pending):
+                if item[0] in finished:
+                    item[0].result()
+                    flops += item[1]
+                    done += 1
+                    pending.discard(item)
+                    if time.perf_counter() - t0 < budget_s:
+                        submit()
+    wall = time.perf_counter() - t0
+    return {
+        "value": round(flops / wall / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{done} blocks of {blk} query rows at random (b, h, row offset) of the "
+                   f"{w.name} workload, float64 NumPy oracle, {cores} worker processes with "
+                   f"one BLAS thread each, {wall:.1f} s wall; FLOPs counted as 4*D per visible "
+                   f"(query, key) pair, the same convention as the GPU figure"),
+    }
+
+
+# ---------------------------------------------------------------- GPU timing
+def time_workload(ea, torch, w, steps, warmup):
+    dev = torch.device("cuda", 0)
+    q, k, v = workloads.workload_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty(w.q_shape(), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        ea.attn_fwd(qd, kd, vd, out, lse, is_causal=w.causal, sm_scale=w.sm_scale)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        ea.attn_fwd(qd, kd, vd, out, lse, is_causal=w.causal, sm_scale=w.sm_scale)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    res = {"wall_ms_per_step": wall * 1e3 / steps, "event_ms": ev_ms}
+    return res, (q, k, v, out, lse)
+
+
+def sampled_parity(w, q, k, v, out, lse):
+    """Part of the CPU-baseline leg: the timed GPU output on sampled rows
+    against the oracle on the same bf16 inputs."""
+    import oracle
+    q64, k64, v64 = (workloads.to_float64(t) for t in (q, k, v))
+    o = out.cpu()
+    l = lse.cpu()
+    rng = np.random.default_rng(7)
+    max_o = max_l = 0.0
+    ok = bool(torch_isfinite_all(o) and torch_isfinite_all(l))
+    for h in sorted({0, w.H_q - 1, int(rng.integers(w.H_q))}):
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, w.N // 2, w.N - 1],
+                                         rng.choice(w.N, 10, replace=False)]))
+        Or, Lr = oracle.attention_rows(q64, k64, v64, 0, h, rows, is_causal=w.causal,
+                                       sm_scale=w.sm_scale)
+        og = o[0, h, rows].double().numpy()
+        lg = l[0, h, rows].double().numpy()
+        eo = np.abs(og - Or)
+        ok &= bool(np.all(eo <= 2e-2 + 2e-2 * np.abs(Or)))
+        el = np.abs(lg - Lr)
+        ok &= bool(np.all(el <= 1e-3))
+        max_o, max_l = max(max_o, float(eo.max())), max(max_l, float(el.max()))
+    return {"sampled_rows_pass": ok, "max_abs_err_O": max_o, "max_abs_err_LSE": max_l}
+
+
+def torch_isfinite_all(t):
+    import torch
+    return bool(torch.isfinite(t.float()).all())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time every workload and print a table to stderr")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of 512 MiB three times "
+                         "(reference for scaling HBM byte counters) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this attention forward has no multi-GPU path "
+              "(sharding by batch or kv-head group needs no communication and is not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_02_amd as ea
+    ea.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    if args.copy_calibration:
+        n = 512 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
+        return
+
+    w = workloads.WORKLOADS[args.workload]
+    log(f"[bench] timing {w.name}: steps={args.steps} warmup={args.warmup}")
+    res, (q, k, v, out, lse) = time_workload(ea, torch, w, args.steps, args.warmup)
+    ev = res["event_ms"]
+    avg_ms = float(np.mean(ev))
+    flops = w.flops()
+    value = flops / (res["wall_ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    log(f"[bench] wall {res['wall_ms_per_step']:.3f} ms/step, event avg {avg_ms:.3f} ms "
+        f"(min {min(ev):.3f}, median {float(np.median(ev)):.3f}), {achieved:.1f} TFLOP/s")
+
+    if args.sweep:
+        for name, ww in workloads.WORKLOADS.items():
+            r, _ = time_workload(ea, torch, ww, 10, 3)
+            e = r["event_ms"]
+            tf = ww.flops() / (float(np.median(e)) * 1e-3) / 1e12
+            log(f"[sweep] {name:24s} median {float(np.median(e)):9.4f} ms  min {min(e):9.4f} ms  "
+                f"{tf:8.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:5.1f}% of peak")
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        # the only part of the benchmark that runs the oracle
+        log("[bench] cpu_baseline: oracle on a bounded sample")
+        parity = sampled_parity(w, q, k, v, out, lse)
+        log(f"[bench] parity {parity}")
+        q64, k64, v64 = (workloads.to_float64(t) for t in (q, k, v))
+        cpu = cpu_baseline(w, q64, k64, v64, budget_s=args.cpu_budget)
+        log(f"[bench] cpu_baseline {cpu}")
+
+    traffic = read_traffic(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["wall_ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "N": w.N,
+                   "D": w.D, "causal": w.causal, "seed": w.seed},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "attn_fwd_kernel", "avg_launch_ms": round(avg_ms, 4),
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": w.algorithmic_bytes()},
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP attention forward against the float64 CPU oracle.
+
+Every case draws seeded bf16 inputs, runs attn_fwd through the C ABI (via the
+ctypes binding) and compares element by element with the oracle on the same
+bf16 values.  Tolerances: |O - O_ref| <= 2e-2 + 2e-2 |O_ref| (the bf16
+atol = rtol = 2e-2 of the page "Attention Kernel 实现与正确性验证", section 1.3)
+and |LSE - LSE_ref| <= 1e-3; no NaN or Inf anywhere.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+O_ATOL = 2e-2
+O_RTOL = 2e-2
+LSE_ATOL = 1e-3
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def ea():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_02_amd as m
+    m.load_library()
+    return m
+
+
+def _run(ea, q, k, v, causal, scale, poison=True):
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    B, H_q, N, D = q.shape
+    out = torch.empty((B, H_q, N, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H_q, N), dtype=torch.float32, device=dev)
+    if poison:
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    ea.attn_fwd(qd, kd, vd, out, lse, is_causal=causal, sm_scale=scale)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def _check(o_gpu, l_gpu, O_ref, L_ref, what=""):
+    o = o_gpu.to(torch.float64).numpy() if isinstance(o_gpu, torch.Tensor) else o_gpu
+    l = l_gpu.to(torch.float64).numpy() if isinstance(l_gpu, torch.Tensor) else l_gpu
+    assert np.all(np.isfinite(o)), f"{what}: non-finite O"
+    assert np.all(np.isfinite(l)), f"{what}: non-finite LSE"
+    err_o = np.abs(o - O_ref)
+    bound = O_ATOL + O_RTOL * np.abs(O_ref)
+    bad = err_o > bound
+    err_l = np.abs(l - L_ref)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} O elements out of tolerance; "
+                           f"max abs err {err_o.max():.3e} at {np.unravel_index(err_o.argmax(), err_o.shape)}")
+    assert err_l.max(initial=0.0) <= LSE_ATOL, f"{what}: max LSE err {err_l.max():.3e}"
+    return float(err_o.max(initial=0.0)), float(err_l.max(initial=0.0))
+
+
+def _full_case(ea, B, H_q, H_kv, N, D, causal, seed, scale=None, dist="normal", mutate=None):
+    q, k, v = workloads.make_inputs(B, H_q, H_kv, N, D, seed, dist=dist)
+    if mutate is not None:
+        q, k, v = mutate(q, k, v)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    o, l = _run(ea, q, k, v, causal, scale)
+    O_ref, L_ref = oracle.attention_forward(workloads.to_float64(q), workloads.to_float64(k),
+                                            workloads.to_float64(v), is_causal=causal,
+                                            sm_scale=scale)
+    return _check(o, l, O_ref, L_ref, what=f"B{B} Hq{H_q} Hkv{H_kv} N{N} D{D} c{int(causal)}")
+
+
+# ------------------------------------------------------------ small workloads, full compare
+SMALL = ["tiny_mha_n256_d64", "gqa4_b2_n1024", "mha_n512", "mqa_n512"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("flip", [False, True], ids=["as_named", "causal_flipped"])
+def test_small_workloads_full(ea, name, flip):
+    w = workloads.WORKLOADS[name]
+    causal = w.causal != flip
+    _full_case(ea, w.B, w.H_q, w.H_kv, w.N, w.D, causal, w.seed)
+
+
+def test_pages_shapes_listed():
+    """The four shapes the first page checks are all among the parity cases."""
+    with open(os.path.join(GOLDEN, "pages_numerical_shapes.json")) as f:
+        shapes = json.load(f)["shapes"]
+    have = {(w.B, w.H_q, w.H_kv, w.N, w.D) for w in workloads.WORKLOADS.values()}
+    for s in shapes:
+        assert (s["B"], s["H_q"], s["H_kv"], s["N"], s["D"]) in have
+
+
+# ------------------------------------------------------------ full-size workloads, sampled
+LARGE = ["gqa8_n4096_causal", "gqa8_n4096_full", "gqa4_n8192_causal", "gqa4_n16384_causal",
+         "gqa4_n32768_causal"]
+
+
+def _sample_rows(N, rng, extra=6):
+    base = {0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 255, 256, N // 2, N - 2, N - 1}
+    rows = sorted(r for r in base if 0 <= r < N)
+    rows += sorted(rng.choice(N, size=extra, replace=False).tolist())
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_large_workloads_sampled(ea, name):
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.workload_inputs(w)
+    o, l = _run(ea, q, k, v, w.causal, w.sm_scale)
+    assert torch.isfinite(o).all() and torch.isfinite(l).all(), "non-finite output"
+    q64, k64, v64 = (workloads.to_float64(t) for t in (q, k, v))
+    rng = np.random.default_rng(w.seed)
+    heads = sorted({0, w.H_q - 1, int(rng.integers(w.H_q)), int(rng.integers(w.H_q))})
+    for b in range(w.B):
+        for h in heads:
+            rows = _sample_rows(w.N, rng)
+            O_ref, L_ref = oracle.attention_rows(q64, k64, v64, b, h, rows, is_causal=w.causal,
+                                                 sm_scale=w.sm_scale)
+            _check(o[b, h, rows], l[b, h, rows], O_ref, L_ref, what=f"{name} b{b} h{h}")
+
+
+def test_gqa8_n4096_some_heads_full(ea):
+    """Two heads of different kv groups, every row, at the full GQA-8 shape."""
+    w = workloads.WORKLOADS["gqa8_n4096_causal"]
+    q, k, v = workloads.workload_inputs(w)
+    q64, k64, v64 = (workloads.to_float64(t) for t in (q, k, v))
+    for causal in (True, False):
+        o, l = _run(ea, q, k, v, causal, w.sm_scale)
+        for h in (5, 42):
+            O_ref, L_ref = oracle.attention_rows(q64, k64, v64, 0, h, np.arange(w.N),
+                                                 is_causal=causal, sm_scale=w.sm_scale)
+            _check(o[0, h], l[0, h], O_ref, L_ref, what=f"gqa8 h{h} c{int(causal)}")
+
+
+# ------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("N", [1, 2, 31, 33, 63, 65, 100, 129, 257, 1000])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_lengths(ea, N, D, causal):
+    _full_case(ea, 1, 4, 2, N, D, causal, seed=7000 + N + D)
+
+
+@pytest.mark.parametrize("H_q,H_kv", [(3, 3), (6, 2), (6, 1), (8, 4), (16, 2), (32, 2), (12, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_groupings(ea, H_q, H_kv, causal):
+    _full_case(ea, 2, H_q, H_kv, 96, 128, causal, seed=100 * H_q + H_kv)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.088, 0.5, 2.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_values(ea, scale, causal):
+    """Zero (uniform weights), negative and large scales (peaked softmax)."""
+    _full_case(ea, 1, 4, 1, 200, 128, causal, seed=31, scale=scale)
+
+
+def test_identical_keys(ea):
+    def same_keys(q, k, v):
+        return q, k[:, :, :1].expand_as(k).contiguous(), v
+    _full_case(ea, 1, 4, 2, 130, 128, True, seed=41, mutate=same_keys)
+
+
+def test_growing_scores_force_rescaling(ea):
+    """Keys whose norm grows along the sequence push the running max up on
+    every tile, so each tile rescales the accumulator."""
+    def ramp(q, k, v):
+        g = torch.linspace(0.2, 3.0, k.shape[2]).view(1, 1, -1, 1)
+        return q, (k.float() * g).to(torch.bfloat16), v
+    for causal in (False, True):
+        _full_case(ea, 1, 4, 4, 700, 128, causal, seed=43, mutate=ramp)
+
+
+def test_uniform_inputs_d64(ea):
+    _full_case(ea, 2, 8, 2, 300, 64, True, seed=44, dist="uniform")
+
+
+# ------------------------------------------------------------ hygiene
+def test_empty_inputs(ea):
+    dev = torch.device("cuda", 0)
+    q = torch.empty((0, 4, 16, 128), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((0, 2, 16, 128), dtype=torch.bfloat16, device=dev)
+    out, lse = ea.fwd(q, k, k, is_causal=True)
+    assert out.shape == q.shape and lse.shape == (0, 4, 16)
+    q = torch.empty((1, 4, 0, 64), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((1, 4, 0, 64), dtype=torch.bfloat16, device=dev)
+    out, lse = ea.fwd(q, k, k)
+    assert out.numel() == 0
+
+
+def test_deterministic_and_no_overrun(ea):
+    """Two runs agree bit for bit; bytes just past out and lse stay untouched."""
+    dev = torch.device("cuda", 0)
+    q, k, v = workloads.make_inputs(1, 8, 2, 333, 128, seed=51)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    n_o, n_l = q.numel(), q.numel() // 128
+    res = []
+    for _ in range(2):
+        ob = torch.full((n_o + 4096,), 7.0, dtype=torch.bfloat16, device=dev)
+        lb = torch.full((n_l + 1024,), 7.0, dtype=torch.float32, device=dev)
+        out = ob[:n_o].view(q.shape)
+        lse = lb[:n_l].view(1, 8, 333)
+        ea.attn_fwd(qd, kd, vd, out, lse, is_causal=True)
+        torch.cuda.synchronize()
+        assert torch.all(ob[n_o:] == 7.0) and torch.all(lb[n_l:] == 7.0), "overrun"
+        res.append((out.clone(), lse.clone()))
+    assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
+    assert torch.equal(res[0][1], res[1][1])
+
+
+def test_side_stream(ea):
+    dev = torch.device("cuda", 0)
+    q, k, v = workloads.make_inputs(1, 4, 4, 256, 128, seed=52)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    ref_o, ref_l = ea.fwd(qd, kd, vd, is_causal=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o, l = ea.fwd(qd, kd, vd, is_causal=True)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)) and torch.equal(l, ref_l)
+
+
+def test_status_error_raises(ea):
+    dev = torch.device("cuda", 0)
+    q = torch.zeros((1, 4, 16, 96), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ea.AttnError) as e:
+        ea.fwd(q, q, q)
+    assert e.value.status == 3
