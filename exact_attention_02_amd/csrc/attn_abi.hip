@@ -3,6 +3,7 @@
 // The library allocates nothing, keeps no state and never synchronises.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 
@@ -13,8 +14,7 @@ namespace {
 
 using ea02::FwdParams;
 
-constexpr int kNW = 4;   // waves per workgroup
-constexpr int kBN = 64;  // keys per tile
+constexpr int kNW = 4;  // waves per workgroup (32 query rows each)
 
 int gcd_int(int a, int b) {
   while (b) {
@@ -32,8 +32,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 template <int D, int HW>
 hipError_t launch(const FwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kBN, kNW, HW>), dim3(grid), dim3(kNW * 64), 0,
-                     stream, p);
+  hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, HW>), dim3(grid), dim3(kNW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -92,7 +91,10 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
   p.n_row_blocks = static_cast<int>(n_row_blocks);
   p.n_head_groups = static_cast<int>(n_head_groups);
   p.n_heads_wg = static_cast<int>(n_heads_wg);
-  p.scale_log2 = std::fabs(sm_scale) * ea02::kLog2e;
+  // A zero scale becomes the smallest normal float: finite scores times it
+  // round to 0 in the exponent (uniform weights, as for a zero scale), while
+  // masked scores (-inf) stay -inf instead of turning into NaN.
+  p.scale_log2 = std::fmax(std::fabs(sm_scale) * ea02::kLog2e, FLT_MIN);
   p.q_sign = (sm_scale < 0.f) ? 0x80008000u : 0u;
   p.causal = is_causal;
 

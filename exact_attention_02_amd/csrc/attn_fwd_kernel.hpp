@@ -13,24 +13,32 @@
 // MI355X mapping (not taken from the pages):
 //  * Transposed products.  Each wave computes S^T = K Q^T and O^T = V^T P^T
 //    with v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane
-//    holds one column and 16 rows, so here a lane owns ONE query and 16 keys
-//    per 32-key block: the row max and row sum are lane-local plus a single
-//    exchange between the two wave halves (v_permlane32_swap), and the per-row
-//    rescale factor is a lane scalar.  The S^T accumulator, rounded to bf16,
-//    is directly the B operand of the PV product; the key order this implies
-//    is absorbed by storing V^T in LDS with keys permuted to match.
-//  * Query fragments live in VGPRs for the whole kernel (B operand of S^T).
-//  * K tiles are stored [key][d] in LDS with a 16-byte-chunk XOR swizzle;
-//    V tiles are transposed on the way in to V^T[d][key'] (also swizzled),
-//    so both MFMA A operands are single 128-bit LDS reads.
-//  * Tiles are double-buffered: the global loads of tile t+1 are issued
-//    before the math of tile t and written to the other LDS buffer after it;
-//    one barrier per tile.
-//  * GQA/MQA: the waves of a workgroup take different query heads of the same
-//    kv group over the same rows, so each K/V tile in LDS serves all of them.
+//    holds one column and 16 rows, so a lane owns ONE query and 16 keys per
+//    32-key block: the row max and row sum are lane-local plus one exchange
+//    between the wave halves (v_permlane32_swap), and the rescale factor is a
+//    lane scalar.  The S^T accumulator rounded to bf16 is directly the B
+//    operand of the PV product.
+//  * Query fragments stay in VGPRs for the whole kernel (B operand of S^T).
+//  * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
+//    staging registers), each 16-byte chunk of a row XOR-swizzled by the row
+//    index.  K fragments are 128-bit LDS reads; V^T fragments come from the
+//    LDS transpose read ds_read_b64_tr_b16 on the untransposed V tile, two per
+//    MFMA, in the key order the S^T accumulator layout implies.
+//  * Two LDS buffers: the loads of tile t+1 are issued right after the barrier
+//    that opens tile t and land while tile t is computed; one barrier per tile.
+//  * Lazy rescaling: the max used in the exponent is raised only when some
+//    row's true max exceeds it by more than 2^8 (a wave-uniform branch), so
+//    P <= 256 and the accumulator is rescaled on a few tiles only.  The final
+//    O = acc / l and LSE use the same max, so the result is exact up to
+//    rounding.
+//  * GQA/MQA: the waves of a workgroup take different query heads of one kv
+//    group over the same rows, so each K/V tile in LDS serves all of them.
 //  * Causal: the tile loop ends at the workgroup's last row; only tiles that
 //    cross a wave's diagonal (or the ragged end of the sequence) run the
 //    masked variant; tiles wholly above a wave's rows are skipped by it.
+//  * Rows past the end of the sequence are clamped to the last row on load
+//    (their keys are masked, their outputs not stored), so loads need no
+//    bounds branches.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,10 +47,15 @@
 namespace ea02 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct FwdParams {
   const uint16_t* q;
@@ -55,71 +68,79 @@ struct FwdParams {
   int n_row_blocks;   // ceil(N / rows per workgroup)
   int n_head_groups;  // G / heads per workgroup
   int n_heads_wg;     // B * H_kv * n_head_groups: workgroups per row block
-  float scale_log2;   // |sm_scale| * log2(e)
+  float scale_log2;   // max(|sm_scale| * log2(e), FLT_MIN): strictly positive, so
+                      // a masked score (-inf) never meets a zero factor
   uint32_t q_sign;    // 0x80008000 when sm_scale < 0 (Q is negated on load), else 0
   int causal;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays <= 2^8
+constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 for gfx9 (untyped dword access)
+
+// instruction classes for __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-__device__ __forceinline__ float wave_half_swap_max(float x) {
-  // v_permlane32_swap exchanges lanes 32..63 of the first operand with lanes
-  // 0..31 of the second; with both operands = x the two results hold x of
-  // this lane and of lane l^32, in some order.
+// v_permlane32_swap exchanges lanes 32..63 of the first operand with lanes
+// 0..31 of the second; with both operands x, the two results hold x of this
+// lane and of lane l^32.
+__device__ __forceinline__ float half_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-__device__ __forceinline__ float wave_half_swap_sum(float x) {
+__device__ __forceinline__ float half_swap_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Position of key `key` (0 <= key < BN) inside a V^T row: within every group
-// of 16 keys the quads are stored in the order 0,2,1,3, so that the 8 keys a
-// lane needs for one PV k-step are contiguous (see the S^T accumulator layout).
-__device__ __forceinline__ int vt_pos(int key) {
-  const int quad = (key >> 2) & 3;
-  const int pq = ((quad & 1) << 1) | (quad >> 1);  // 0,2,1,3
-  return (key & ~15) | (pq << 2) | (key & 3);
-}
-
-template <int D, int BN, int NW, int HW>
+template <int D>
 struct Cfg {
-  static constexpr int QW = 32;                 // query rows per wave
-  static constexpr int NT = NW * 64;            // threads per workgroup
-  static constexpr int BM = QW * NW / HW;       // query rows per workgroup
-  static constexpr int DC = D / 8;              // 16-byte chunks per K row
-  static constexpr int KC = BN * DC / NT;       // K chunks loaded per thread
-  static constexpr int VU = (BN / 4) * DC;      // V units (4 keys x 8 d)
-  static constexpr int VUT = (VU + NT - 1) / NT;
-  static constexpr int VC = BN / 8;             // 16-byte chunks per V^T row
-  static constexpr int K_ELEMS = BN * D;        // u16 per K buffer
-  static constexpr int V_ELEMS = D * BN;        // u16 per V^T buffer
-  static constexpr int LDS_ELEMS = 2 * (K_ELEMS + V_ELEMS);
-  static_assert(BN == 64, "key tile of 64");
+  static constexpr int BN = 64;                  // keys per tile
+  static constexpr int NW = 4;                   // waves per workgroup
+  static constexpr int NT = NW * 64;
+  static constexpr int QW = 32;                  // query rows per wave
+  static constexpr int DC = D / 8;               // 16-byte chunks per row
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;       // one K or V tile
+  static constexpr int LOADS = TILE_BYTES / 1024;         // 1 KiB load instructions per tile
+  static constexpr int LOADS_PER_WAVE = LOADS / NW;
+  static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES;        // K0 K1 V0 V1
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
-  static_assert((BN * DC) % NT == 0, "K tile split evenly");
+  static_assert(LOADS % NW == 0, "tile loads split evenly over waves");
 };
 
-// XOR swizzles of 16-byte chunk indices (conflict-light 128-bit LDS access).
-template <int DC>
-__device__ __forceinline__ int k_swz(int key, int chunk) { return chunk ^ (key & (DC - 1)); }
-__device__ __forceinline__ int vt_swz(int d, int chunk) { return chunk ^ ((d ^ (d >> 3)) & 7); }
+// 16-byte chunk swizzles.  K: the 16 (D=128) or 8 (D=64) chunks of a row are
+// permuted so that the 16 keys read together by 16 lanes at one chunk index
+// hit 16 different bank groups.  V: chosen so that a transpose read (4 rows x
+// 4 chunks per 16 lanes, two such groups per half wave) spreads 8 rows over
+// all banks.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  if constexpr (D == 128) return row & 15;
+  else return (row >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  if constexpr (D == 128) return 4 * (row & 3);
+  else return 4 * ((row >> 1) & 1);
+}
 
-template <int D, int BN, int NW, int HW>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
-  using C = Cfg<D, BN, NW, HW>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  uint16_t* const k_lds = lds;                       // [2][BN][D]
-  uint16_t* const v_lds = lds + 2 * C::K_ELEMS;      // [2][D][BN]
+template <int D, int HW>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(FwdParams p) {
+  using C = Cfg<D>;
+  constexpr int BN = C::BN;
+  constexpr int BM = C::QW * C::NW / HW;  // query rows per workgroup
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -134,192 +155,178 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
   const int hh = wave % HW;
   const int rsub = wave / HW;
   const int h = g * p.G + hs * HW + hh;
-  const int R0 = rb * C::BM;
+  const int R0 = rb * BM;
   const int wr0 = R0 + rsub * C::QW;
   const int N = p.N;
 
-  const int kv_end = p.causal ? min(R0 + C::BM, N) : N;
+  const int kv_end = p.causal ? min(R0 + BM, N) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
 
   const size_t kv_base = ((size_t)b * p.H_kv + g) * (size_t)N * D;
   const size_t q_base = ((size_t)b * p.H_q + h) * (size_t)N * D;
-  const uint16_t* __restrict__ kg = p.k + kv_base;
-  const uint16_t* __restrict__ vg = p.v + kv_base;
+  // K and V of this kv head as buffer resources (base in SGPRs, 32-bit offsets)
+  const int head_bytes = N * C::ROW_BYTES;
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kv_base), (short)0, head_bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kv_base), (short)0, head_bytes, kBufferFlags);
 
-  // ---- query fragments (B operand of S^T = K Q^T): lane holds query col,
-  //      d = 16*ks + 8*half .. +8
+  // ---- query fragments (B operand of S^T = K Q^T): lane holds query `col`,
+  //      d = 16*ks + 8*half .. +8.  Rows past the end are clamped.
   const int my_row = wr0 + col;
+  const int q_row = min(my_row, N - 1);
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (my_row < N) x = *reinterpret_cast<const u32x4*>(p.q + q_base + (size_t)my_row * D + ks * 16 + half * 8);
+    u32x4 x = *reinterpret_cast<const u32x4*>(p.q + q_base + (size_t)q_row * D + ks * 16 + half * 8);
     x ^= p.q_sign;
     qf[ks] = as_bf16x8(x);
   }
 
-  // ---- tile staging through registers
-  u32x4 kreg[C::KC];
-  u32x4 vreg[C::VUT][4];
-
-  auto load_tile = [&](int key0) {
+  // ---- direct HBM -> LDS tile loads.  Load instruction i of a tile fills
+  //      bytes [1024 i, 1024 i + 1024): lane -> (row, stored chunk j), and it
+  //      fetches global chunk j ^ swz(row).
+  const int ld_row_in = lane / C::DC;
+  const int ld_chunk = lane % C::DC;
+  auto issue_tile = [&](int key0, int buf) {
 #pragma unroll
-    for (int i = 0; i < C::KC; ++i) {
-      const int c = tid + i * C::NT;
-      const int key = c / C::DC, dc = c % C::DC;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key0 + key < N) x = *reinterpret_cast<const u32x4*>(kg + (size_t)(key0 + key) * D + dc * 8);
-      kreg[i] = x;
-    }
-#pragma unroll
-    for (int i = 0; i < C::VUT; ++i) {
-      const int u = tid + i * C::NT;
-      if (u < C::VU) {
-        const int dc = u % C::DC, kgp = u / C::DC;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + kgp * 4 + r;
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (key < N) x = *reinterpret_cast<const u32x4*>(vg + (size_t)key * D + dc * 8);
-          vreg[i][r] = x;
-        }
-      }
+    for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+      const int li = wave * C::LOADS_PER_WAVE + i;
+      const int r = li * C::ROWS_PER_LOAD + ld_row_in;
+      const int grow_bytes = min(key0 + r, N - 1) * C::ROW_BYTES;
+      const int koff = grow_bytes + ((ld_chunk ^ k_swz<D>(r)) << 4);
+      const int voff = grow_bytes + ((ld_chunk ^ v_swz<D>(r)) << 4);
+      uint8_t* kd = lds + buf * C::TILE_BYTES + li * 1024;
+      uint8_t* vd = lds + (2 + buf) * C::TILE_BYTES + li * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)kd, 16, koff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void*)vd, 16, voff, 0, 0, 0);
     }
   };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* kb = k_lds + buf * C::K_ELEMS;
-    uint16_t* vb = v_lds + buf * C::V_ELEMS;
+  // per-lane LDS byte offsets of the MFMA operand reads (tile-relative)
+  // K (A operand of S^T): key c*32+col, chunk 2ks+half (swizzled)
+  // V^T (A operand of O^T, transpose read): 16-lane group G = lane>>4, L = lane&15
+  //   reads rows k0 + L/4 (k0 = 16 s + 4 half + 8 part), d = db*32 + 16(G&1) + 4(L&3)
+  const int L = lane & 15;
+  const int vt_row = 4 * half + (L >> 2);
+  int vt_off[D / 32];
 #pragma unroll
-    for (int i = 0; i < C::KC; ++i) {
-      const int c = tid + i * C::NT;
-      const int key = c / C::DC, dc = c % C::DC;
-      *reinterpret_cast<u32x4*>(kb + key * D + k_swz<C::DC>(key, dc) * 8) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::VUT; ++i) {
-      const int u = tid + i * C::NT;
-      if (u < C::VU) {
-        const int dc = u % C::DC, kgp = u / C::DC;
-        const int pos = vt_pos(kgp * 4);
-        const int chunk = pos >> 3, sub = pos & 7;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // element e of each row: 16-bit lane e of the 128-bit register
-          const int w = e >> 1, sh = (e & 1) * 16;
-          const uint32_t a0 = (vreg[i][0][w] >> sh) & 0xffffu;
-          const uint32_t a1 = (vreg[i][1][w] >> sh) & 0xffffu;
-          const uint32_t a2 = (vreg[i][2][w] >> sh) & 0xffffu;
-          const uint32_t a3 = (vreg[i][3][w] >> sh) & 0xffffu;
-          u32x2 pk = {a0 | (a1 << 16), a2 | (a3 << 16)};
-          const int d = dc * 8 + e;
-          *reinterpret_cast<u32x2*>(vb + d * BN + vt_swz(d, chunk) * 8 + sub) = pk;
-        }
-      }
-    }
-  };
+  for (int db = 0; db < D / 32; ++db) {
+    const int d = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+    const int chunk = (d >> 3) ^ v_swz<D>(vt_row);
+    vt_off[db] = vt_row * C::ROW_BYTES + chunk * 16 + (d & 7) * 2;
+  }
 
   // ---- running state (one query per lane)
-  float m_run = -INFINITY;  // running max, log2-scaled units
-  float l_run = 0.f;        // this lane's partial running sum (its 16 keys per block)
+  float m_used = -INFINITY;  // max used in the exponent (log2-scaled units)
+  float l_run = 0.f;         // this lane's partial sum over its keys
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-
   const float sl2 = p.scale_log2;
 
-  auto process_tile = [&](int buf, int key0, bool masked) {
-    const uint16_t* kb = k_lds + buf * C::K_ELEMS;
-    const uint16_t* vb = v_lds + buf * C::V_ELEMS;
-    // S^T[key][query] for the BN/32 key blocks
+  auto k_read = [&](const uint8_t* kb, int i) {
+    const int c = i / (D / 16), ks = i % (D / 16);
+    const int key = c * 32 + col;
+    return *reinterpret_cast<const u32x4*>(kb + key * C::ROW_BYTES +
+                                           (((2 * ks + half) ^ k_swz<D>(key)) << 4));
+  };
+  auto v_read = [&](const uint8_t* vb, int i) {
+    const int st = i / (D / 32), db = i % (D / 32);
+    const uint8_t* a0 = vb + vt_off[db] + (16 * st) * C::ROW_BYTES;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * C::ROW_BYTES));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  constexpr int NS = (BN / 32) * (D / 16);  // S^T MFMAs per tile
+  constexpr int NP = (BN / 16) * (D / 32);  // O^T MFMAs per tile
+
+  if (n_tiles > 0) issue_tile(0, 0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int key0 = t * BN;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile t landed
+    __syncthreads();                                    // all waves' loads landed; tile t-1 done
+    if (t + 1 < n_tiles) issue_tile(key0 + BN, (t + 1) & 1);
+    // tiles wholly above this wave's rows: nothing visible
+    if (p.causal && key0 > wr0 + C::QW - 1) continue;
+    const uint8_t* kb = lds + (t & 1) * C::TILE_BYTES;
+    const uint8_t* vb = lds + (2 + (t & 1)) * C::TILE_BYTES;
+
+    // S^T[key][query] for the two 32-key blocks; each MFMA is fed by one
+    // 128-bit LDS read issued two steps ahead
     f32x16 s[BN / 32];
 #pragma unroll
-    for (int c = 0; c < BN / 32; ++c) {
-      s[c] = f32x16{};
-      const int key = c * 32 + col;
+    for (int c = 0; c < BN / 32; ++c) s[c] = f32x16{};
+    {
+      u32x4 kx[3];
+      kx[0] = k_read(kb, 0);
+      kx[1] = k_read(kb, 1);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 kx = *reinterpret_cast<const u32x4*>(kb + key * D + k_swz<C::DC>(key, 2 * ks + half) * 8);
-        s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx), qf[ks], s[c], 0, 0, 0);
+      for (int i = 0; i < NS; ++i) {
+        if (i + 2 < NS) kx[(i + 2) % 3] = k_read(kb, i + 2);
+        const int c = i / (D / 16), ks = i % (D / 16);
+        s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx[i % 3]), qf[ks], s[c], 0, 0, 0);
       }
     }
-    if (masked) {
+    // diagonal or ragged tile: mask.  Element (c, r) holds key
+    // key0 + 4 half + [c*32 + 8(r/4) + r%4]; it is visible when the bracket is
+    // below lim (a compare against a compile-time constant per element).
+    if ((p.causal && key0 + BN - 1 > wr0) || key0 + BN > N) {
+      const int lim = (p.causal ? min(my_row + 1, N) : N) - key0 - 4 * half;
 #pragma unroll
       for (int c = 0; c < BN / 32; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + c * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key < N && (!p.causal || key <= my_row);
-          s[c][r] = vis ? s[c][r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          s[c][r] = (c * 32 + 8 * (r >> 2) + (r & 3) < lim) ? s[c][r] : -INFINITY;
     }
-    // online softmax (exp2 form)
-    float mx = -INFINITY;
+    // tile row max of the raw scores, shared by the two wave halves.  The
+    // exponent scale sl2 is > 0, so a fully masked row stays at -inf.
+    float mx = s[0][0];
 #pragma unroll
     for (int c = 0; c < BN / 32; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
-    mx = wave_half_swap_max(mx);
-    // (-inf) * 0 would be NaN when sm_scale is 0: keep a fully masked row at -inf
-    const float m_new = fmaxf(m_run, mx == -INFINITY ? -INFINITY : mx * sl2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float rs = 0.f;
-    bf16x8 pb[BN / 16];
+      for (int r = (c == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[c][r]);
+    mx = half_swap_max(mx);
+    const float mt = mx * sl2;
+    if (__builtin_amdgcn_ballot_w64(mt > m_used + kRescaleSlack)) {
+      const float m_new = fmaxf(m_used, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int c = 0; c < BN / 32; ++c) {
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      m_used = m_new;
+    }
+    const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
+
+    // P = 2^(S sl2 - m) (rounded to bf16: the B operand of O^T = V^T P^T) and
+    // O^T += V^T P^T; k-step st covers keys 16 st .. 16 st + 15, i.e. the
+    // accumulator elements s[st/2][8(st%2) .. +8]
+    {
+      bf16x8 vx[3];
+      vx[0] = v_read(vb, 0);
+      vx[1] = v_read(vb, 1);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int st = 0; st < BN / 16; ++st) {
+        const int c = st >> 1, t8 = (st & 1) * 8;
         f32x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * t + e], sl2, -m_use));
-          // a masked score is -inf; with sm_scale = 0 the product above is NaN
-          if (masked) pe = (s[c][8 * t + e] == -INFINITY) ? 0.f : pe;
-          pf[e] = pe;
-          rs += pe;
+          pf[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][t8 + e], sl2, -m_sub));
+          l_run += pf[e];
         }
-        pb[2 * c + t] = __builtin_convertvector(pf, bf16x8);
+        const bf16x8 pb = __builtin_convertvector(pf, bf16x8);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int i = st * (D / 32) + db;
+          if (i + 2 < NP) vx[(i + 2) % 3] = v_read(vb, i + 2);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx[i % 3], pb, acc[db], 0, 0, 0);
+        }
       }
     }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int d = db * 32 + col;
-#pragma unroll
-      for (int st = 0; st < BN / 16; ++st) {
-        const int chunk = 2 * st + half;
-        const u32x4 vx = *reinterpret_cast<const u32x4*>(vb + d * BN + vt_swz(d, chunk) * 8);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vx), pb[st], acc[db], 0, 0, 0);
-      }
-    }
-  };
-
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-  }
-  for (int t = 0; t < n_tiles; ++t) {
-    const int key0 = t * BN;
-    const bool more = t + 1 < n_tiles;
-    if (more) load_tile(key0 + BN);
-    const bool skip = p.causal && key0 > wr0 + C::QW - 1;
-    if (!skip) {
-      const bool masked = (p.causal && key0 + BN - 1 > wr0) || (key0 + BN > N);
-      if (masked) process_tile(t & 1, key0, true);
-      else process_tile(t & 1, key0, false);
-    }
-    if (more) store_tile((t + 1) & 1);
-    __syncthreads();
   }
 
   // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log
-  const float l_tot = wave_half_swap_sum(l_run);
+  const float l_tot = half_swap_sum(l_run);
   const float inv = 1.f / l_tot;
   if (my_row < N) {
     uint16_t* orow = p.o + q_base + (size_t)my_row * D;
@@ -328,14 +335,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = db * 32 + 8 * g4 + 4 * half;
-        typedef float f32x4v __attribute__((ext_vector_type(4)));
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        f32x4v f = {acc[db][4 * g4 + 0] * inv, acc[db][4 * g4 + 1] * inv,
-                    acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv};
-        bf16x4 bv = __builtin_convertvector(f, bf16x4);
+        f32x4 f = {acc[db][4 * g4 + 0] * inv, acc[db][4 * g4 + 1] * inv,
+                   acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv};
+        const bf16x4 bv = __builtin_convertvector(f, bf16x4);
         *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, bv);
       }
-    if (half == 0) p.lse[((size_t)b * p.H_q + h) * (size_t)N + my_row] = (m_run + __log2f(l_tot)) * kLn2;
+    if (half == 0) p.lse[((size_t)b * p.H_q + h) * (size_t)N + my_row] = (m_used + __log2f(l_tot)) * kLn2;
   }
 }
 
