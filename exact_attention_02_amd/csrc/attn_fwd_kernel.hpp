@@ -55,6 +55,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct FwdParams {
@@ -95,6 +96,32 @@ __device__ __forceinline__ float half_swap_max(float x) {
 __device__ __forceinline__ float half_swap_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Raw buffer resource: 48-bit base, no stride, num_records bytes.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4 r;
+  r[0] = (uint32_t)a;
+  r[1] = (uint32_t)(a >> 32) & 0xffffu;
+  r[2] = bytes;
+  r[3] = (uint32_t)kBufferFlags;
+  return r;
+}
+
+// 16 bytes per lane from the buffer at byte offset voff straight into LDS at
+// lds_addr + 16 * lane.  Written as inline asm so that the compiler does not
+// track it: it would otherwise wait for these loads before every later LDS
+// read.  The caller waits (s_waitcnt vmcnt(0)) before a barrier instead.
+__device__ __forceinline__ void dma_16B(u32x4 rsrc, int voff, uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+
+// x *= a in place (tied operand), so the rescale of the accumulator keeps the
+// accumulator's registers and needs no copies around the branch.
+__device__ __forceinline__ void mul_inplace(float& x, float a) {
+  asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(a));
 }
 
 template <int D>
@@ -165,11 +192,9 @@ void attn_fwd_kernel(FwdParams p) {
   const size_t kv_base = ((size_t)b * p.H_kv + g) * (size_t)N * D;
   const size_t q_base = ((size_t)b * p.H_q + h) * (size_t)N * D;
   // K and V of this kv head as buffer resources (base in SGPRs, 32-bit offsets)
-  const int head_bytes = N * C::ROW_BYTES;
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kv_base), (short)0, head_bytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kv_base), (short)0, head_bytes, kBufferFlags);
+  const uint32_t head_bytes = (uint32_t)N * C::ROW_BYTES;
+  const u32x4 k_rsrc = make_rsrc(p.k + kv_base, head_bytes);
+  const u32x4 v_rsrc = make_rsrc(p.v + kv_base, head_bytes);
 
   // ---- query fragments (B operand of S^T = K Q^T): lane holds query `col`,
   //      d = 16*ks + 8*half .. +8.  Rows past the end are clamped.
@@ -186,6 +211,7 @@ void attn_fwd_kernel(FwdParams p) {
   // ---- direct HBM -> LDS tile loads.  Load instruction i of a tile fills
   //      bytes [1024 i, 1024 i + 1024): lane -> (row, stored chunk j), and it
   //      fetches global chunk j ^ swz(row).
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
   const int ld_row_in = lane / C::DC;
   const int ld_chunk = lane % C::DC;
   auto issue_tile = [&](int key0, int buf) {
@@ -196,10 +222,10 @@ void attn_fwd_kernel(FwdParams p) {
       const int grow_bytes = min(key0 + r, N - 1) * C::ROW_BYTES;
       const int koff = grow_bytes + ((ld_chunk ^ k_swz<D>(r)) << 4);
       const int voff = grow_bytes + ((ld_chunk ^ v_swz<D>(r)) << 4);
-      uint8_t* kd = lds + buf * C::TILE_BYTES + li * 1024;
-      uint8_t* vd = lds + (2 + buf) * C::TILE_BYTES + li * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)kd, 16, koff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void*)vd, 16, voff, 0, 0, 0);
+      const uint32_t kd = lds_base + buf * C::TILE_BYTES + li * 1024;
+      const uint32_t vd = lds_base + (2 + buf) * C::TILE_BYTES + li * 1024;
+      dma_16B(k_rsrc, koff, kd);
+      dma_16B(v_rsrc, voff, vd);
     }
   };
 
@@ -247,8 +273,12 @@ void attn_fwd_kernel(FwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile t landed
     __syncthreads();                                    // all waves' loads landed; tile t-1 done
     if (t + 1 < n_tiles) issue_tile(key0 + BN, (t + 1) & 1);
-    // tiles wholly above this wave's rows: nothing visible
-    if (p.causal && key0 > wr0 + C::QW - 1) continue;
+    // tiles wholly above this wave's rows: nothing visible.  When every wave
+    // of the workgroup has the same rows (HW == NW) the loop bound already
+    // excludes them.
+    if constexpr (HW < C::NW) {
+      if (p.causal && key0 > wr0 + C::QW - 1) continue;
+    }
     const uint8_t* kb = lds + (t & 1) * C::TILE_BYTES;
     const uint8_t* vb = lds + (2 + (t & 1)) * C::TILE_BYTES;
 
@@ -293,7 +323,13 @@ void attn_fwd_kernel(FwdParams p) {
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = acc[db][r];
+          mul_inplace(x, alpha);
+          acc[db][r] = x;
+        }
       m_used = m_new;
     }
     const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
