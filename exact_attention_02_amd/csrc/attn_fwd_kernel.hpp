@@ -48,6 +48,7 @@ namespace ea02 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -73,6 +74,11 @@ struct FwdParams {
                       // a masked score (-inf) never meets a zero factor
   uint32_t q_sign;    // 0x80008000 when sm_scale < 0 (Q is negated on load), else 0
   int causal;
+};
+
+template <bool V>
+struct BoolTag {
+  static constexpr bool value = V;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -210,22 +216,27 @@ void attn_fwd_kernel(FwdParams p) {
 
   // ---- direct HBM -> LDS tile loads.  Load instruction i of a tile fills
   //      bytes [1024 i, 1024 i + 1024): lane -> (row, stored chunk j), and it
-  //      fetches global chunk j ^ swz(row).
+  //      fetches global chunk j ^ swz(row).  LDS holds K0 K1 V0 V1; tile j
+  //      uses K buffer j%2 and V buffer j%2.
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
   const int ld_row_in = lane / C::DC;
   const int ld_chunk = lane % C::DC;
-  auto issue_tile = [&](int key0, int buf) {
+  auto issue_k = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
       const int li = wave * C::LOADS_PER_WAVE + i;
       const int r = li * C::ROWS_PER_LOAD + ld_row_in;
-      const int grow_bytes = min(key0 + r, N - 1) * C::ROW_BYTES;
-      const int koff = grow_bytes + ((ld_chunk ^ k_swz<D>(r)) << 4);
-      const int voff = grow_bytes + ((ld_chunk ^ v_swz<D>(r)) << 4);
-      const uint32_t kd = lds_base + buf * C::TILE_BYTES + li * 1024;
-      const uint32_t vd = lds_base + (2 + buf) * C::TILE_BYTES + li * 1024;
-      dma_16B(k_rsrc, koff, kd);
-      dma_16B(v_rsrc, voff, vd);
+      const int off = min(tile * BN + r, N - 1) * C::ROW_BYTES + ((ld_chunk ^ k_swz<D>(r)) << 4);
+      dma_16B(k_rsrc, off, lds_base + (tile & 1) * C::TILE_BYTES + li * 1024);
+    }
+  };
+  auto issue_v = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+      const int li = wave * C::LOADS_PER_WAVE + i;
+      const int r = li * C::ROWS_PER_LOAD + ld_row_in;
+      const int off = min(tile * BN + r, N - 1) * C::ROW_BYTES + ((ld_chunk ^ v_swz<D>(r)) << 4);
+      dma_16B(v_rsrc, off, lds_base + (2 + (tile & 1)) * C::TILE_BYTES + li * 1024);
     }
   };
 
@@ -242,22 +253,15 @@ void attn_fwd_kernel(FwdParams p) {
     const int chunk = (d >> 3) ^ v_swz<D>(vt_row);
     vt_off[db] = vt_row * C::ROW_BYTES + chunk * 16 + (d & 7) * 2;
   }
-
-  // ---- running state (one query per lane)
-  float m_used = -INFINITY;  // max used in the exponent (log2-scaled units)
-  float l_run = 0.f;         // this lane's partial sum over its keys
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-  const float sl2 = p.scale_log2;
-
-  auto k_read = [&](const uint8_t* kb, int i) {
+  auto k_read = [&](int tile, int i) {
+    const uint8_t* kb = lds + (tile & 1) * C::TILE_BYTES;
     const int c = i / (D / 16), ks = i % (D / 16);
     const int key = c * 32 + col;
     return *reinterpret_cast<const u32x4*>(kb + key * C::ROW_BYTES +
                                            (((2 * ks + half) ^ k_swz<D>(key)) << 4));
   };
-  auto v_read = [&](const uint8_t* vb, int i) {
+  auto v_read = [&](int tile, int i) {
+    const uint8_t* vb = lds + (2 + (tile & 1)) * C::TILE_BYTES;
     const int st = i / (D / 32), db = i % (D / 32);
     const uint8_t* a0 = vb + vt_off[db] + (16 * st) * C::ROW_BYTES;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
@@ -266,98 +270,172 @@ void attn_fwd_kernel(FwdParams p) {
   };
   constexpr int NS = (BN / 32) * (D / 16);  // S^T MFMAs per tile
   constexpr int NP = (BN / 16) * (D / 32);  // O^T MFMAs per tile
+  constexpr int NV = BN / 2;                // scores per lane per tile (16 per 32-key block)
+  constexpr int EPM = NV / NS;              // exponentials per S^T MFMA (2 at D=128, 4 at D=64)
+  constexpr int MPM = NV / NP;              // max operations per O^T MFMA
+  static_assert(EPM * NS == NV && MPM * NP == NV, "score work splits evenly over the MFMAs");
 
-  if (n_tiles > 0) issue_tile(0, 0);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int key0 = t * BN;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile t landed
-    __syncthreads();                                    // all waves' loads landed; tile t-1 done
-    if (t + 1 < n_tiles) issue_tile(key0 + BN, (t + 1) & 1);
-    // tiles wholly above this wave's rows: nothing visible.  When every wave
-    // of the workgroup has the same rows (HW == NW) the loop bound already
-    // excludes them.
-    if constexpr (HW < C::NW) {
-      if (p.causal && key0 > wr0 + C::QW - 1) continue;
-    }
-    const uint8_t* kb = lds + (t & 1) * C::TILE_BYTES;
-    const uint8_t* vb = lds + (2 + (t & 1)) * C::TILE_BYTES;
+  // ---- running state (one query per lane)
+  float m_used = -INFINITY;  // max used in the exponent (log2-scaled units)
+  float l_run = 0.f;         // this lane's partial sum of P over its keys
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  const float sl2 = p.scale_log2;
 
-    // S^T[key][query] for the two 32-key blocks; each MFMA is fed by one
-    // 128-bit LDS read issued two steps ahead
-    f32x16 s[BN / 32];
+  // S^T = K Q^T of one tile with no other work interleaved (prologue only)
+  auto s_tile = [&](int tile, f32x16* s) {
 #pragma unroll
     for (int c = 0; c < BN / 32; ++c) s[c] = f32x16{};
-    {
-      u32x4 kx[3];
-      kx[0] = k_read(kb, 0);
-      kx[1] = k_read(kb, 1);
+    u32x4 kx[3];
+    kx[0] = k_read(tile, 0);
+    kx[1] = k_read(tile, 1);
 #pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        if (i + 2 < NS) kx[(i + 2) % 3] = k_read(kb, i + 2);
-        const int c = i / (D / 16), ks = i % (D / 16);
-        s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx[i % 3]), qf[ks], s[c], 0, 0, 0);
-      }
+    for (int i = 0; i < NS; ++i) {
+      if (i + 2 < NS) kx[(i + 2) % 3] = k_read(tile, i + 2);
+      s[i / (D / 16)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx[i % 3]), qf[i % (D / 16)],
+                                                                s[i / (D / 16)], 0, 0, 0);
     }
-    // diagonal or ragged tile: mask.  Element (c, r) holds key
-    // key0 + 4 half + [c*32 + 8(r/4) + r%4]; it is visible when the bracket is
-    // below lim (a compare against a compile-time constant per element).
-    if ((p.causal && key0 + BN - 1 > wr0) || key0 + BN > N) {
-      const int lim = (p.causal ? min(my_row + 1, N) : N) - key0 - 4 * half;
-#pragma unroll
-      for (int c = 0; c < BN / 32; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[c][r] = (c * 32 + 8 * (r >> 2) + (r & 3) < lim) ? s[c][r] : -INFINITY;
-    }
-    // tile row max of the raw scores, shared by the two wave halves.  The
-    // exponent scale sl2 is > 0, so a fully masked row stays at -inf.
-    float mx = s[0][0];
+  };
+  // diagonal or ragged tile: element (c, r) holds key tile*BN + 4 half +
+  // [c*32 + 8(r/4) + r%4]; it is visible when the bracket is below lim
+  auto needs_mask = [&](int tile) {
+    const int key0 = tile * BN;
+    return (p.causal && key0 + BN - 1 > wr0) || key0 + BN > N;
+  };
+  auto apply_mask = [&](int tile, f32x16* s) {
+    const int lim = (p.causal ? min(my_row + 1, N) : N) - tile * BN - 4 * half;
 #pragma unroll
     for (int c = 0; c < BN / 32; ++c)
 #pragma unroll
-      for (int r = (c == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[c][r]);
-    mx = half_swap_max(mx);
-    const float mt = mx * sl2;
+      for (int r = 0; r < 16; ++r)
+        s[c][r] = (c * 32 + 8 * (r >> 2) + (r & 3) < lim) ? s[c][r] : -INFINITY;
+  };
+  // raise the exponent's max when the tile max exceeds it by more than the
+  // slack (wave-uniform branch; rare after the first tile)
+  auto update_max = [&](float mx_lane) {
+    const float mt = half_swap_max(mx_lane) * sl2;  // sl2 > 0: a masked row stays -inf
     if (__builtin_amdgcn_ballot_w64(mt > m_used + kRescaleSlack)) {
       const float m_new = fmaxf(m_used, mt);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = acc[db][r];
-          mul_inplace(x, alpha);
-          acc[db][r] = x;
-        }
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
       m_used = m_new;
     }
-    const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
+  };
+  auto lane_max = [&](const f32x16* s) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int c = 0; c < BN / 32; ++c)
+#pragma unroll
+      for (int r = (c == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[c][r]);
+    return mx;
+  };
 
-    // P = 2^(S sl2 - m) (rounded to bf16: the B operand of O^T = V^T P^T) and
-    // O^T += V^T P^T; k-step st covers keys 16 st .. 16 st + 15, i.e. the
-    // accumulator elements s[st/2][8(st%2) .. +8]
-    {
-      bf16x8 vx[3];
-      vx[0] = v_read(vb, 0);
-      vx[1] = v_read(vb, 1);
+  // One pipelined step over tile t (its scores already in sc, masked, max
+  // applied): P(t) = 2^(S(t) sl2 - m) interleaved with S(t+1) = K(t+1) Q^T
+  // into sn (when HAS_NEXT), then O += V(t) P(t) interleaved with the lane max
+  // of S(t+1).
+  auto step = [&](int t, f32x16* sc, f32x16* sn, auto has_next_tag) {
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
+    bf16x8 pb[BN / 16];
+    f32x8 pf;
+    if constexpr (HAS_NEXT) {
 #pragma unroll
-      for (int st = 0; st < BN / 16; ++st) {
-        const int c = st >> 1, t8 = (st & 1) * 8;
-        f32x8 pf;
+      for (int c = 0; c < BN / 32; ++c) sn[c] = f32x16{};
+      u32x4 kx[3];
+      kx[0] = k_read(t + 1, 0);
+      kx[1] = k_read(t + 1, 1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pf[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][t8 + e], sl2, -m_sub));
-          l_run += pf[e];
-        }
-        const bf16x8 pb = __builtin_convertvector(pf, bf16x8);
+      for (int i = 0; i < NS; ++i) {
+        if (i + 2 < NS) kx[(i + 2) % 3] = k_read(t + 1, i + 2);
+        sn[i / (D / 16)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(kx[i % 3]), qf[i % (D / 16)], sn[i / (D / 16)], 0, 0, 0);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int i = st * (D / 32) + db;
-          if (i + 2 < NP) vx[(i + 2) % 3] = v_read(vb, i + 2);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx[i % 3], pb, acc[db], 0, 0, 0);
+        for (int e = 0; e < EPM; ++e) {
+          const int j = i * EPM + e;  // element j of this lane's BN scores
+          pf[j & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j >> 4][j & 15], sl2, -m_sub));
+          l_run += pf[j & 7];
+          if ((j & 7) == 7) pb[j >> 3] = __builtin_convertvector(pf, bf16x8);
         }
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        pf[j & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j >> 4][j & 15], sl2, -m_sub));
+        l_run += pf[j & 7];
+        if ((j & 7) == 7) pb[j >> 3] = __builtin_convertvector(pf, bf16x8);
+      }
+    }
+    // O^T += V^T P^T; k-step st covers keys 16 st .. 16 st + 15
+    bf16x8 vx[3];
+    vx[0] = v_read(t, 0);
+    vx[1] = v_read(t, 1);
+    float mx = HAS_NEXT ? sn[0][0] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (i + 2 < NP) vx[(i + 2) % 3] = v_read(t, i + 2);
+      const int st = i / (D / 32), db = i % (D / 32);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx[i % 3], pb[st], acc[db], 0, 0, 0);
+
+      if constexpr (HAS_NEXT) {
+#pragma unroll
+        for (int e = 0; e < MPM; ++e) {
+          const int j = i * MPM + e;
+          if (j > 0) mx = fmaxf(mx, sn[j >> 4][j & 15]);
+        }
+      }
+    }
+    if constexpr (HAS_NEXT) {
+      // the max above ran over unmasked scores; a diagonal or ragged tile is
+      // masked here (rare) and its max taken again
+      if (needs_mask(t + 1)) {
+        apply_mask(t + 1, sn);
+        mx = lane_max(sn);
+      }
+      update_max(mx);
+    }
+  };
+
+  if (n_tiles > 0) {
+    // prologue: K(0), V(0), K(1) in flight; S(0)
+    issue_k(0);
+    issue_v(0);
+    if (n_tiles > 1) issue_k(1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f32x16 sa[BN / 32], sb[BN / 32];
+    s_tile(0, sa);
+    if (needs_mask(0)) apply_mask(0, sa);
+    update_max(lane_max(sa));
+    // steady state, unrolled by two so the score buffers alternate without copies
+    int t = 0;
+    for (; t + 2 < n_tiles; t += 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(t+1), V(t) landed
+      __syncthreads();                                    // ... for every wave; tile t-1 done
+      if (t + 2 < n_tiles) issue_k(t + 2);
+      issue_v(t + 1);
+      step(t, sa, sb, BoolTag<true>{});
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (t + 3 < n_tiles) issue_k(t + 3);
+      issue_v(t + 2);
+      step(t + 1, sb, sa, BoolTag<true>{});
+    }
+    if (t + 1 < n_tiles) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      issue_v(t + 1);
+      step(t, sa, sb, BoolTag<true>{});
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      step(t + 1, sb, sa, BoolTag<false>{});
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      step(t, sa, sb, BoolTag<false>{});
     }
   }
 
