@@ -14,7 +14,8 @@ namespace {
 
 using ea02::FwdParams;
 
-constexpr int kNW = 4;  // waves per workgroup (32 query rows each)
+constexpr int kNW = 8;  // waves per workgroup (32 query rows each), two per SIMD
+constexpr int kP = 4;   // LDS stages per K and per V ring
 
 int gcd_int(int a, int b) {
   while (b) {
@@ -32,13 +33,14 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 template <int D, int HW>
 hipError_t launch(const FwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, HW>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+  hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, HW, kNW, kP>), dim3(grid), dim3(kNW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdParams& p, int hw, int grid, hipStream_t stream) {
   switch (hw) {
+    case 8: return launch<D, 8>(p, grid, stream);
     case 4: return launch<D, 4>(p, grid, stream);
     case 2: return launch<D, 2>(p, grid, stream);
     default: return launch<D, 1>(p, grid, stream);

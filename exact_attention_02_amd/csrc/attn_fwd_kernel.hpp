@@ -130,10 +130,11 @@ __device__ __forceinline__ void mul_inplace(float& x, float a) {
   asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(a));
 }
 
-template <int D>
+template <int D, int NW_, int P_>
 struct Cfg {
   static constexpr int BN = 64;                  // keys per tile
-  static constexpr int NW = 4;                   // waves per workgroup
+  static constexpr int NW = NW_;                 // waves per workgroup
+  static constexpr int P = P_;                   // LDS stages (tiles of K and of V in flight)
   static constexpr int NT = NW * 64;
   static constexpr int QW = 32;                  // query rows per wave
   static constexpr int DC = D / 8;               // 16-byte chunks per row
@@ -142,10 +143,22 @@ struct Cfg {
   static constexpr int LOADS = TILE_BYTES / 1024;         // 1 KiB load instructions per tile
   static constexpr int LOADS_PER_WAVE = LOADS / NW;
   static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
-  static constexpr int LDS_BYTES = 4 * TILE_BYTES;        // K0 K1 V0 V1
+  static constexpr int LDS_BYTES = 2 * P * TILE_BYTES;    // K ring then V ring
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
-  static_assert(LOADS % NW == 0, "tile loads split evenly over waves");
+  static_assert(LOADS % NW == 0 && LOADS_PER_WAVE >= 1, "tile loads split evenly over waves");
+  static_assert(P >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
 };
+
+// s_waitcnt vmcnt(n) for a runtime n in [0, 15]: the count is an immediate.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define EA02_VM(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    EA02_VM(1) EA02_VM(2) EA02_VM(3) EA02_VM(4) EA02_VM(5) EA02_VM(6) EA02_VM(7)
+    EA02_VM(8) EA02_VM(9) EA02_VM(10) EA02_VM(11) EA02_VM(12) EA02_VM(13) EA02_VM(14) EA02_VM(15)
+#undef EA02_VM
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
 
 // 16-byte chunk swizzles.  K: the 16 (D=128) or 8 (D=64) chunks of a row are
 // permuted so that the 16 keys read together by 16 lanes at one chunk index
@@ -163,10 +176,10 @@ __device__ __forceinline__ int v_swz(int row) {
   else return 4 * ((row >> 1) & 1);
 }
 
-template <int D, int HW>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <int D, int HW, int NW, int P>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
-  using C = Cfg<D>;
+  using C = Cfg<D, NW, P>;
   constexpr int BN = C::BN;
   constexpr int BM = C::QW * C::NW / HW;  // query rows per workgroup
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
@@ -216,8 +229,8 @@ void attn_fwd_kernel(FwdParams p) {
 
   // ---- direct HBM -> LDS tile loads.  Load instruction i of a tile fills
   //      bytes [1024 i, 1024 i + 1024): lane -> (row, stored chunk j), and it
-  //      fetches global chunk j ^ swz(row).  LDS holds K0 K1 V0 V1; tile j
-  //      uses K buffer j%2 and V buffer j%2.
+  //      fetches global chunk j ^ swz(row).  LDS holds a ring of P K tiles
+  //      then a ring of P V tiles; tile j uses slot j % P of each.
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
   const int ld_row_in = lane / C::DC;
   const int ld_chunk = lane % C::DC;
@@ -227,7 +240,7 @@ void attn_fwd_kernel(FwdParams p) {
       const int li = wave * C::LOADS_PER_WAVE + i;
       const int r = li * C::ROWS_PER_LOAD + ld_row_in;
       const int off = min(tile * BN + r, N - 1) * C::ROW_BYTES + ((ld_chunk ^ k_swz<D>(r)) << 4);
-      dma_16B(k_rsrc, off, lds_base + (tile & 1) * C::TILE_BYTES + li * 1024);
+      dma_16B(k_rsrc, off, lds_base + (tile % P) * C::TILE_BYTES + li * 1024);
     }
   };
   auto issue_v = [&](int tile) {
@@ -236,7 +249,7 @@ void attn_fwd_kernel(FwdParams p) {
       const int li = wave * C::LOADS_PER_WAVE + i;
       const int r = li * C::ROWS_PER_LOAD + ld_row_in;
       const int off = min(tile * BN + r, N - 1) * C::ROW_BYTES + ((ld_chunk ^ v_swz<D>(r)) << 4);
-      dma_16B(v_rsrc, off, lds_base + (2 + (tile & 1)) * C::TILE_BYTES + li * 1024);
+      dma_16B(v_rsrc, off, lds_base + (P + tile % P) * C::TILE_BYTES + li * 1024);
     }
   };
 
@@ -254,14 +267,14 @@ void attn_fwd_kernel(FwdParams p) {
     vt_off[db] = vt_row * C::ROW_BYTES + chunk * 16 + (d & 7) * 2;
   }
   auto k_read = [&](int tile, int i) {
-    const uint8_t* kb = lds + (tile & 1) * C::TILE_BYTES;
+    const uint8_t* kb = lds + (tile % P) * C::TILE_BYTES;
     const int c = i / (D / 16), ks = i % (D / 16);
     const int key = c * 32 + col;
     return *reinterpret_cast<const u32x4*>(kb + key * C::ROW_BYTES +
                                            (((2 * ks + half) ^ k_swz<D>(key)) << 4));
   };
   auto v_read = [&](int tile, int i) {
-    const uint8_t* vb = lds + (2 + (tile & 1)) * C::TILE_BYTES;
+    const uint8_t* vb = lds + (P + tile % P) * C::TILE_BYTES;
     const int st = i / (D / 32), db = i % (D / 32);
     const uint8_t* a0 = vb + vt_off[db] + (16 * st) * C::ROW_BYTES;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
@@ -399,13 +412,30 @@ void attn_fwd_kernel(FwdParams p) {
     }
   };
 
-  if (n_tiles > 0) {
-    // prologue: K(0), V(0), K(1) in flight; S(0)
-    issue_k(0);
-    issue_v(0);
-    if (n_tiles > 1) issue_k(1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Load schedule.  Group j = {K(j) if j < n_tiles, V(j-1) if j >= 1}; the
+  // step over tile t reads K(t+1) and V(t), i.e. group t+1.  Groups are issued
+  // P-1 ahead: after the barrier that opens tile t, group t+P goes into the
+  // slots that group t used (read during tile t-1, finished by every wave).
+  auto issue_group = [&](int j) {
+    if (j < n_tiles) issue_k(j);
+    if (j >= 1 && j <= n_tiles) issue_v(j - 1);
+  };
+  auto group_loads = [&](int j) {
+    return (j < n_tiles ? C::LOADS_PER_WAVE : 0) + (j >= 1 && j <= n_tiles ? C::LOADS_PER_WAVE : 0);
+  };
+  // wait until this wave's loads of group j landed (groups j+1..last may stay
+  // in flight), then make every wave's loads visible
+  auto sync_group = [&](int j, int last) {
+    int pending = 0;
+    for (int g2 = j + 1; g2 <= last; ++g2) pending += group_loads(g2);
+    wait_vmcnt(pending);
     __syncthreads();
+  };
+
+  if (n_tiles > 0) {
+    const int pre = min(P - 1, n_tiles);
+    for (int j = 0; j <= pre; ++j) issue_group(j);
+    sync_group(0, pre);
     f32x16 sa[BN / 32], sb[BN / 32];
     s_tile(0, sa);
     if (needs_mask(0)) apply_mask(0, sa);
@@ -413,28 +443,21 @@ void attn_fwd_kernel(FwdParams p) {
     // steady state, unrolled by two so the score buffers alternate without copies
     int t = 0;
     for (; t + 2 < n_tiles; t += 2) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K(t+1), V(t) landed
-      __syncthreads();                                    // ... for every wave; tile t-1 done
-      if (t + 2 < n_tiles) issue_k(t + 2);
-      issue_v(t + 1);
+      sync_group(t + 1, min(t + P - 1, n_tiles));
+      issue_group(t + P);
       step(t, sa, sb, BoolTag<true>{});
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (t + 3 < n_tiles) issue_k(t + 3);
-      issue_v(t + 2);
+      sync_group(t + 2, min(t + P, n_tiles));
+      issue_group(t + 1 + P);
       step(t + 1, sb, sa, BoolTag<true>{});
     }
     if (t + 1 < n_tiles) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      issue_v(t + 1);
+      sync_group(t + 1, min(t + P - 1, n_tiles));
+      issue_group(t + P);
       step(t, sa, sb, BoolTag<true>{});
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      sync_group(t + 2, min(t + P, n_tiles));
       step(t + 1, sb, sa, BoolTag<false>{});
     } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      sync_group(t + 1, min(t + P - 1, n_tiles));
       step(t, sa, sb, BoolTag<false>{});
     }
   }
