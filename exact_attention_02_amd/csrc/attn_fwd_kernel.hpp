@@ -149,17 +149,6 @@ struct Cfg {
   static_assert(P >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
 };
 
-// s_waitcnt vmcnt(n) for a runtime n in [0, 15]: the count is an immediate.
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-#define EA02_VM(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
-    EA02_VM(1) EA02_VM(2) EA02_VM(3) EA02_VM(4) EA02_VM(5) EA02_VM(6) EA02_VM(7)
-    EA02_VM(8) EA02_VM(9) EA02_VM(10) EA02_VM(11) EA02_VM(12) EA02_VM(13) EA02_VM(14) EA02_VM(15)
-#undef EA02_VM
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
-}
-
 // 16-byte chunk swizzles.  K: the 16 (D=128) or 8 (D=64) chunks of a row are
 // permuted so that the 16 keys read together by 16 lanes at one chunk index
 // hit 16 different bank groups.  V: chosen so that a transpose read (4 rows x
@@ -234,22 +223,16 @@ void attn_fwd_kernel(FwdParams p) {
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
   const int ld_row_in = lane / C::DC;
   const int ld_chunk = lane % C::DC;
-  auto issue_k = [&](int tile) {
+  // one tile of K (ring 0) or V (ring 1) into ring slot `slot`; rows past the
+  // end of the sequence are clamped to the last row
+  auto issue_tile = [&](int tile, int slot, const u32x4& rsrc, int ring) {
 #pragma unroll
     for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
       const int li = wave * C::LOADS_PER_WAVE + i;
       const int r = li * C::ROWS_PER_LOAD + ld_row_in;
-      const int off = min(tile * BN + r, N - 1) * C::ROW_BYTES + ((ld_chunk ^ k_swz<D>(r)) << 4);
-      dma_16B(k_rsrc, off, lds_base + (tile % P) * C::TILE_BYTES + li * 1024);
-    }
-  };
-  auto issue_v = [&](int tile) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
-      const int li = wave * C::LOADS_PER_WAVE + i;
-      const int r = li * C::ROWS_PER_LOAD + ld_row_in;
-      const int off = min(tile * BN + r, N - 1) * C::ROW_BYTES + ((ld_chunk ^ v_swz<D>(r)) << 4);
-      dma_16B(v_rsrc, off, lds_base + (P + tile % P) * C::TILE_BYTES + li * 1024);
+      const int swz = ring == 0 ? k_swz<D>(r) : v_swz<D>(r);
+      const int off = min(tile * BN + r, N - 1) * C::ROW_BYTES + ((ld_chunk ^ swz) << 4);
+      dma_16B(rsrc, off, lds_base + (ring * P + slot) * C::TILE_BYTES + li * 1024);
     }
   };
 
@@ -268,7 +251,7 @@ void attn_fwd_kernel(FwdParams p) {
   }
   auto k_read = [&](int tile, int i) {
     const uint8_t* kb = lds + (tile % P) * C::TILE_BYTES;
-    const int c = i / (D / 16), ks = i % (D / 16);
+    const int c = i % (BN / 32), ks = i / (BN / 32);  // consecutive MFMAs alternate key blocks
     const int key = c * 32 + col;
     return *reinterpret_cast<const u32x4*>(kb + key * C::ROW_BYTES +
                                            (((2 * ks + half) ^ k_swz<D>(key)) << 4));
@@ -306,8 +289,8 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (i + 2 < NS) kx[(i + 2) % 3] = k_read(tile, i + 2);
-      s[i / (D / 16)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx[i % 3]), qf[i % (D / 16)],
-                                                                s[i / (D / 16)], 0, 0, 0);
+      s[i % (BN / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx[i % 3]), qf[i / (BN / 32)],
+                                                                 s[i % (BN / 32)], 0, 0, 0);
     }
   };
   // diagonal or ragged tile: element (c, r) holds key tile*BN + 4 half +
@@ -364,8 +347,8 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         if (i + 2 < NS) kx[(i + 2) % 3] = k_read(t + 1, i + 2);
-        sn[i / (D / 16)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(kx[i % 3]), qf[i % (D / 16)], sn[i / (D / 16)], 0, 0, 0);
+        sn[i % (BN / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(kx[i % 3]), qf[i / (BN / 32)], sn[i % (BN / 32)], 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < EPM; ++e) {
           const int j = i * EPM + e;  // element j of this lane's BN scores
@@ -412,30 +395,32 @@ void attn_fwd_kernel(FwdParams p) {
     }
   };
 
-  // Load schedule.  Group j = {K(j) if j < n_tiles, V(j-1) if j >= 1}; the
-  // step over tile t reads K(t+1) and V(t), i.e. group t+1.  Groups are issued
-  // P-1 ahead: after the barrier that opens tile t, group t+P goes into the
-  // slots that group t used (read during tile t-1, finished by every wave).
+  // Load schedule.  Group j loads K(j) into K slot j % P and V(j-1) into V
+  // slot (j-1) % P; the step over tile t reads K(t+1) and V(t), i.e. group
+  // t+1.  Groups are issued P-1 ahead: after the barrier that opens tile t,
+  // group t+P goes into the slots that group t used (read during tile t-1 and
+  // finished by every wave).  A group past either end of the sequence loads a
+  // clamped, valid tile into its (free) slots, so every group is the same
+  // number of loads and each wait below is one constant vmcnt.
   auto issue_group = [&](int j) {
-    if (j < n_tiles) issue_k(j);
-    if (j >= 1 && j <= n_tiles) issue_v(j - 1);
+    issue_tile(min(j, n_tiles - 1), j % P, k_rsrc, 0);
+    issue_tile(max(min(j - 1, n_tiles - 1), 0), (j + P - 1) % P, v_rsrc, 1);
   };
-  auto group_loads = [&](int j) {
-    return (j < n_tiles ? C::LOADS_PER_WAVE : 0) + (j >= 1 && j <= n_tiles ? C::LOADS_PER_WAVE : 0);
+  constexpr int GROUP_LOADS = 2 * C::LOADS_PER_WAVE;
+  // group j landed for every wave (groups j+1 .. j+IN_FLIGHT may stay in flight)
+  auto sync_prologue = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 1) * GROUP_LOADS) : "memory");
+    __syncthreads();
   };
-  // wait until this wave's loads of group j landed (groups j+1..last may stay
-  // in flight), then make every wave's loads visible
-  auto sync_group = [&](int j, int last) {
-    int pending = 0;
-    for (int g2 = j + 1; g2 <= last; ++g2) pending += group_loads(g2);
-    wait_vmcnt(pending);
+  auto sync_steady = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 2) * GROUP_LOADS) : "memory");
     __syncthreads();
   };
 
   if (n_tiles > 0) {
-    const int pre = min(P - 1, n_tiles);
-    for (int j = 0; j <= pre; ++j) issue_group(j);
-    sync_group(0, pre);
+#pragma unroll
+    for (int j = 0; j < P; ++j) issue_group(j);
+    sync_prologue();
     f32x16 sa[BN / 32], sb[BN / 32];
     s_tile(0, sa);
     if (needs_mask(0)) apply_mask(0, sa);
@@ -443,23 +428,26 @@ void attn_fwd_kernel(FwdParams p) {
     // steady state, unrolled by two so the score buffers alternate without copies
     int t = 0;
     for (; t + 2 < n_tiles; t += 2) {
-      sync_group(t + 1, min(t + P - 1, n_tiles));
+      sync_steady();
       issue_group(t + P);
       step(t, sa, sb, BoolTag<true>{});
-      sync_group(t + 2, min(t + P, n_tiles));
+      sync_steady();
       issue_group(t + 1 + P);
       step(t + 1, sb, sa, BoolTag<true>{});
     }
     if (t + 1 < n_tiles) {
-      sync_group(t + 1, min(t + P - 1, n_tiles));
+      sync_steady();
       issue_group(t + P);
       step(t, sa, sb, BoolTag<true>{});
-      sync_group(t + 2, min(t + P, n_tiles));
+      sync_steady();
+      issue_group(t + 1 + P);
       step(t + 1, sb, sa, BoolTag<false>{});
     } else {
-      sync_group(t + 1, min(t + P - 1, n_tiles));
+      sync_steady();
+      issue_group(t + P);
       step(t, sa, sb, BoolTag<false>{});
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may outlive the workgroup
   }
 
   // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log
