@@ -14,8 +14,12 @@ namespace {
 
 using ea02::FwdParams;
 
-constexpr int kNW = 8;  // waves per workgroup (32 query rows each), two per SIMD
-constexpr int kP = 4;   // LDS stages per K and per V ring
+// Kernel shape: KQB query blocks of 32 rows per wave, KNW waves per
+// workgroup, KP LDS stages.
+constexpr int kQB = 1;
+constexpr int kNW = kQB == 1 ? 8 : 4;
+constexpr int kBN = kQB == 1 ? 64 : 32;
+constexpr int kP = 4;
 
 int gcd_int(int a, int b) {
   while (b) {
@@ -33,14 +37,14 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 template <int D, int HW>
 hipError_t launch(const FwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, HW, kNW, kP>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+  hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, HW, kNW, kP, kQB, kBN>), dim3(grid), dim3(kNW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdParams& p, int hw, int grid, hipStream_t stream) {
   switch (hw) {
-    case 8: return launch<D, 8>(p, grid, stream);
+    case 8: if constexpr (kNW >= 8) return launch<D, 8>(p, grid, stream); else return hipErrorInvalidValue;
     case 4: return launch<D, 4>(p, grid, stream);
     case 2: return launch<D, 2>(p, grid, stream);
     default: return launch<D, 1>(p, grid, stream);
@@ -61,7 +65,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
     return ATTN_ERR_SIZE_OVERFLOW;
   const int G = static_cast<int>(H_q / H_kv);
   const int hw = gcd_int(G, kNW);
-  const int BM = 32 * kNW / hw;
+  const int BM = 32 * kQB * kNW / hw;
   const int64_t n_row_blocks = (N + BM - 1) / BM;
   const int64_t n_head_groups = G / hw;
   const int64_t n_heads_wg = B * H_kv * n_head_groups;

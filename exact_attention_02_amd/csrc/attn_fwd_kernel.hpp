@@ -130,13 +130,14 @@ __device__ __forceinline__ void mul_inplace(float& x, float a) {
   asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(a));
 }
 
-template <int D, int NW_, int P_>
+template <int D, int NW_, int P_, int QB_, int BN_>
 struct Cfg {
-  static constexpr int BN = 64;                  // keys per tile
+  static constexpr int BN = BN_;                 // keys per tile (32 or 64)
   static constexpr int NW = NW_;                 // waves per workgroup
   static constexpr int P = P_;                   // LDS stages (tiles of K and of V in flight)
+  static constexpr int QB = QB_;                 // 32-query column blocks per wave
   static constexpr int NT = NW * 64;
-  static constexpr int QW = 32;                  // query rows per wave
+  static constexpr int QW = 32 * QB;             // query rows per wave
   static constexpr int DC = D / 8;               // 16-byte chunks per row
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int TILE_BYTES = BN * ROW_BYTES;       // one K or V tile
@@ -145,6 +146,8 @@ struct Cfg {
   static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
   static constexpr int LDS_BYTES = 2 * P * TILE_BYTES;    // K ring then V ring
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
+  static_assert(QB == 1 || QB == 2, "one or two query blocks per wave");
+  static_assert(BN == 32 || BN == 64, "key tiles of 32 or 64");
   static_assert(LOADS % NW == 0 && LOADS_PER_WAVE >= 1, "tile loads split evenly over waves");
   static_assert(P >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
 };
@@ -165,10 +168,15 @@ __device__ __forceinline__ int v_swz(int row) {
   else return 4 * ((row >> 1) & 1);
 }
 
-template <int D, int HW, int NW, int P>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
+// QB = 1: eight waves of 32 query rows, two waves per SIMD (256 VGPRs each).
+// QB = 2: four waves of 64 query rows, one wave per SIMD (512 registers): each
+// K or V^T fragment read from LDS feeds two MFMAs, halving LDS traffic per
+// FLOP, and the accumulators fit in the AGPR half of the register file.
+template <int D, int HW, int NW, int P, int QB, int BN_>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void attn_fwd_kernel(FwdParams p) {
-  using C = Cfg<D, NW, P>;
+  using C = Cfg<D, NW, P, QB, BN_>;
   constexpr int BN = C::BN;
   constexpr int BM = C::QW * C::NW / HW;  // query rows per workgroup
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
@@ -191,7 +199,7 @@ void attn_fwd_kernel(FwdParams p) {
   const int rsub = wave / HW;
   const int h = g * p.G + hs * HW + hh;
   const int R0 = rb * BM;
-  const int wr0 = R0 + rsub * C::QW;
+  const int wr0 = R0 + rsub * C::QW;  // first query row of this wave
   const int N = p.N;
 
   const int kv_end = p.causal ? min(R0 + BM, N) : N;
@@ -204,22 +212,27 @@ void attn_fwd_kernel(FwdParams p) {
   const u32x4 k_rsrc = make_rsrc(p.k + kv_base, head_bytes);
   const u32x4 v_rsrc = make_rsrc(p.v + kv_base, head_bytes);
 
-  // ---- query fragments (B operand of S^T = K Q^T): lane holds query `col`,
-  //      d = 16*ks + 8*half .. +8.  Rows past the end are clamped.
-  const int my_row = wr0 + col;
-  const int q_row = min(my_row, N - 1);
-  bf16x8 qf[D / 16];
+  // ---- query fragments (B operands of S^T = K Q^T): in query block qb the
+  //      lane holds query wr0 + 32 qb + col, d = 16*ks + 8*half .. +8.  Rows
+  //      past the end are clamped.
+  int my_row[QB];
+  bf16x8 qf[QB][D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 x = *reinterpret_cast<const u32x4*>(p.q + q_base + (size_t)q_row * D + ks * 16 + half * 8);
-    x ^= p.q_sign;
-    qf[ks] = as_bf16x8(x);
+  for (int qb = 0; qb < QB; ++qb) {
+    my_row[qb] = wr0 + 32 * qb + col;
+    const int q_row = min(my_row[qb], N - 1);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(p.q + q_base + (size_t)q_row * D + ks * 16 + half * 8);
+      x ^= p.q_sign;
+      qf[qb][ks] = as_bf16x8(x);
+    }
   }
 
   // ---- direct HBM -> LDS tile loads.  Load instruction i of a tile fills
   //      bytes [1024 i, 1024 i + 1024): lane -> (row, stored chunk j), and it
   //      fetches global chunk j ^ swz(row).  LDS holds a ring of P K tiles
-  //      then a ring of P V tiles; tile j uses slot j % P of each.
+  //      then a ring of P V tiles.
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
   const int ld_row_in = lane / C::DC;
   const int ld_chunk = lane % C::DC;
@@ -251,7 +264,7 @@ void attn_fwd_kernel(FwdParams p) {
   }
   auto k_read = [&](int tile, int i) {
     const uint8_t* kb = lds + (tile % P) * C::TILE_BYTES;
-    const int c = i % (BN / 32), ks = i / (BN / 32);  // consecutive MFMAs alternate key blocks
+    const int c = i % (BN / 32), ks = i / (BN / 32);  // consecutive reads alternate key blocks
     const int key = c * 32 + col;
     return *reinterpret_cast<const u32x4*>(kb + key * C::ROW_BYTES +
                                            (((2 * ks + half) ^ k_swz<D>(key)) << 4));
@@ -264,33 +277,43 @@ void attn_fwd_kernel(FwdParams p) {
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * C::ROW_BYTES));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  constexpr int NS = (BN / 32) * (D / 16);  // S^T MFMAs per tile
-  constexpr int NP = (BN / 16) * (D / 32);  // O^T MFMAs per tile
-  constexpr int NV = BN / 2;                // scores per lane per tile (16 per 32-key block)
-  constexpr int EPM = NV / NS;              // exponentials per S^T MFMA (2 at D=128, 4 at D=64)
-  constexpr int MPM = NV / NP;              // max operations per O^T MFMA
-  static_assert(EPM * NS == NV && MPM * NP == NV, "score work splits evenly over the MFMAs");
+  constexpr int NS = (BN / 32) * (D / 16);  // K fragment reads per tile (each feeds QB MFMAs)
+  constexpr int NP = (BN / 16) * (D / 32);  // V^T fragment reads per tile (each feeds QB MFMAs)
+  constexpr int NV = BN / 2;                // scores per lane per query block per tile
+  constexpr int EPR = QB * NV / NS;         // exponentials per K fragment read
+  constexpr int MPR = QB * NV / NP;         // max operations per V^T fragment read
+  static_assert(EPR * NS == QB * NV && MPR * NP == QB * NV, "score work splits evenly");
+  constexpr int PF = QB == 1 ? 2 : 3;       // LDS operand prefetch distance
 
-  // ---- running state (one query per lane)
-  float m_used = -INFINITY;  // max used in the exponent (log2-scaled units)
-  float l_run = 0.f;         // this lane's partial sum of P over its keys
-  f32x16 acc[D / 32];
+  // ---- running state: per query block, one query per lane
+  float m_used[QB], l_run[QB];
+  f32x16 acc[D / 32][QB];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  for (int qb = 0; qb < QB; ++qb) {
+    m_used[qb] = -INFINITY;  // max used in the exponent (log2-scaled units)
+    l_run[qb] = 0.f;         // this lane's partial sum of P over its keys
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc[i][qb] = f32x16{};
+  }
   const float sl2 = p.scale_log2;
 
+  using Scores = f32x16[BN / 32][QB];
   // S^T = K Q^T of one tile with no other work interleaved (prologue only)
-  auto s_tile = [&](int tile, f32x16* s) {
+  auto s_tile = [&](int tile, Scores& s) {
 #pragma unroll
-    for (int c = 0; c < BN / 32; ++c) s[c] = f32x16{};
-    u32x4 kx[3];
-    kx[0] = k_read(tile, 0);
-    kx[1] = k_read(tile, 1);
+    for (int c = 0; c < BN / 32; ++c)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[c][qb] = f32x16{};
+    u32x4 kx[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kx[i] = k_read(tile, i);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      if (i + 2 < NS) kx[(i + 2) % 3] = k_read(tile, i + 2);
-      s[i % (BN / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx[i % 3]), qf[i / (BN / 32)],
-                                                                 s[i % (BN / 32)], 0, 0, 0);
+      if (i + PF < NS) kx[(i + PF) % (PF + 1)] = k_read(tile, i + PF);
+      const int c = i % (BN / 32), ks = i / (BN / 32);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s[c][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx[i % (PF + 1)]), qf[qb][ks], s[c][qb], 0, 0, 0);
     }
   };
   // diagonal or ragged tile: element (c, r) holds key tile*BN + 4 half +
@@ -299,88 +322,107 @@ void attn_fwd_kernel(FwdParams p) {
     const int key0 = tile * BN;
     return (p.causal && key0 + BN - 1 > wr0) || key0 + BN > N;
   };
-  auto apply_mask = [&](int tile, f32x16* s) {
-    const int lim = (p.causal ? min(my_row + 1, N) : N) - tile * BN - 4 * half;
+  auto apply_mask = [&](int tile, Scores& s) {
 #pragma unroll
-    for (int c = 0; c < BN / 32; ++c)
+    for (int qb = 0; qb < QB; ++qb) {
+      const int lim = (p.causal ? min(my_row[qb] + 1, N) : N) - tile * BN - 4 * half;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        s[c][r] = (c * 32 + 8 * (r >> 2) + (r & 3) < lim) ? s[c][r] : -INFINITY;
+      for (int c = 0; c < BN / 32; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[c][qb][r] = (c * 32 + 8 * (r >> 2) + (r & 3) < lim) ? s[c][qb][r] : -INFINITY;
+    }
   };
   // raise the exponent's max when the tile max exceeds it by more than the
   // slack (wave-uniform branch; rare after the first tile)
-  auto update_max = [&](float mx_lane) {
-    const float mt = half_swap_max(mx_lane) * sl2;  // sl2 > 0: a masked row stays -inf
-    if (__builtin_amdgcn_ballot_w64(mt > m_used + kRescaleSlack)) {
-      const float m_new = fmaxf(m_used, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used - m_new);
-      l_run *= alpha;
+  auto update_max = [&](const float* mx_lane) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-      m_used = m_new;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mt = half_swap_max(mx_lane[qb]) * sl2;  // sl2 > 0: a masked row stays -inf
+      if (__builtin_amdgcn_ballot_w64(mt > m_used[qb] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_used[qb], mt);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used[qb] - m_new);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db][qb] *= alpha;
+        m_used[qb] = m_new;
+      }
     }
   };
-  auto lane_max = [&](const f32x16* s) {
-    float mx = s[0][0];
+  auto lane_max = [&](const Scores& s, float* mx) {
 #pragma unroll
-    for (int c = 0; c < BN / 32; ++c)
+    for (int qb = 0; qb < QB; ++qb) {
+      float m = s[0][qb][0];
 #pragma unroll
-      for (int r = (c == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[c][r]);
-    return mx;
+      for (int c = 0; c < BN / 32; ++c)
+#pragma unroll
+        for (int r = (c == 0 ? 1 : 0); r < 16; ++r) m = fmaxf(m, s[c][qb][r]);
+      mx[qb] = m;
+    }
   };
 
   // One pipelined step over tile t (its scores already in sc, masked, max
   // applied): P(t) = 2^(S(t) sl2 - m) interleaved with S(t+1) = K(t+1) Q^T
   // into sn (when HAS_NEXT), then O += V(t) P(t) interleaved with the lane max
   // of S(t+1).
-  auto step = [&](int t, f32x16* sc, f32x16* sn, auto has_next_tag) {
+  auto step = [&](int t, Scores& sc, Scores& sn, auto has_next_tag) {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
-    const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
-    bf16x8 pb[BN / 16];
-    f32x8 pf;
+    float m_sub[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_sub[qb] = (m_used[qb] == -INFINITY) ? 0.f : m_used[qb];
+    bf16x8 pb[QB][BN / 16];
+    f32x8 pf[QB];
+    // exponential number j of this tile: query block j / NV, element j % NV
+    auto p_elem = [&](int j) {
+      const int qb = j / NV, e = j % NV;
+      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 4][qb][e & 15], sl2, -m_sub[qb]));
+      pf[qb][e & 7] = pe;
+      l_run[qb] += pe;
+      if ((e & 7) == 7) pb[qb][e >> 3] = __builtin_convertvector(pf[qb], bf16x8);
+    };
     if constexpr (HAS_NEXT) {
 #pragma unroll
-      for (int c = 0; c < BN / 32; ++c) sn[c] = f32x16{};
-      u32x4 kx[3];
-      kx[0] = k_read(t + 1, 0);
-      kx[1] = k_read(t + 1, 1);
+      for (int c = 0; c < BN / 32; ++c)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sn[c][qb] = f32x16{};
+      u32x4 kx[PF + 1];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) kx[i] = k_read(t + 1, i);
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        if (i + 2 < NS) kx[(i + 2) % 3] = k_read(t + 1, i + 2);
-        sn[i % (BN / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(kx[i % 3]), qf[i / (BN / 32)], sn[i % (BN / 32)], 0, 0, 0);
+        if (i + PF < NS) kx[(i + PF) % (PF + 1)] = k_read(t + 1, i + PF);
+        const int c = i % (BN / 32), ks = i / (BN / 32);
 #pragma unroll
-        for (int e = 0; e < EPM; ++e) {
-          const int j = i * EPM + e;  // element j of this lane's BN scores
-          pf[j & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j >> 4][j & 15], sl2, -m_sub));
-          l_run += pf[j & 7];
-          if ((j & 7) == 7) pb[j >> 3] = __builtin_convertvector(pf, bf16x8);
-        }
+        for (int qb = 0; qb < QB; ++qb)
+          sn[c][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx[i % (PF + 1)]), qf[qb][ks],
+                                                              sn[c][qb], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < EPR; ++e) p_elem(i * EPR + e);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        pf[j & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j >> 4][j & 15], sl2, -m_sub));
-        l_run += pf[j & 7];
-        if ((j & 7) == 7) pb[j >> 3] = __builtin_convertvector(pf, bf16x8);
-      }
+      for (int j = 0; j < QB * NV; ++j) p_elem(j);
     }
     // O^T += V^T P^T; k-step st covers keys 16 st .. 16 st + 15
-    bf16x8 vx[3];
-    vx[0] = v_read(t, 0);
-    vx[1] = v_read(t, 1);
-    float mx = HAS_NEXT ? sn[0][0] : 0.f;
+    bf16x8 vx[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) vx[i] = v_read(t, i);
+    float mx[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = HAS_NEXT ? sn[0][qb][0] : 0.f;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      if (i + 2 < NP) vx[(i + 2) % 3] = v_read(t, i + 2);
+      if (i + PF < NP) vx[(i + PF) % (PF + 1)] = v_read(t, i + PF);
       const int st = i / (D / 32), db = i % (D / 32);
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx[i % 3], pb[st], acc[db], 0, 0, 0);
-
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx[i % (PF + 1)], pb[qb][st], acc[db][qb], 0, 0, 0);
       if constexpr (HAS_NEXT) {
 #pragma unroll
-        for (int e = 0; e < MPM; ++e) {
-          const int j = i * MPM + e;
-          if (j > 0) mx = fmaxf(mx, sn[j >> 4][j & 15]);
+        for (int e = 0; e < MPR; ++e) {
+          const int j = i * MPR + e;
+          const int qb = j / NV, el = j % NV;
+          if (el > 0) mx[qb] = fmaxf(mx[qb], sn[el >> 4][qb][el & 15]);
         }
       }
     }
@@ -389,7 +431,7 @@ void attn_fwd_kernel(FwdParams p) {
       // masked here (rare) and its max taken again
       if (needs_mask(t + 1)) {
         apply_mask(t + 1, sn);
-        mx = lane_max(sn);
+        lane_max(sn, mx);
       }
       update_max(mx);
     }
@@ -407,7 +449,6 @@ void attn_fwd_kernel(FwdParams p) {
     issue_tile(max(min(j - 1, n_tiles - 1), 0), (j + P - 1) % P, v_rsrc, 1);
   };
   constexpr int GROUP_LOADS = 2 * C::LOADS_PER_WAVE;
-  // group j landed for every wave (groups j+1 .. j+IN_FLIGHT may stay in flight)
   auto sync_prologue = [&]() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 1) * GROUP_LOADS) : "memory");
     __syncthreads();
@@ -421,10 +462,14 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int j = 0; j < P; ++j) issue_group(j);
     sync_prologue();
-    f32x16 sa[BN / 32], sb[BN / 32];
+    Scores sa, sb;
     s_tile(0, sa);
     if (needs_mask(0)) apply_mask(0, sa);
-    update_max(lane_max(sa));
+    {
+      float mx[QB];
+      lane_max(sa, mx);
+      update_max(mx);
+    }
     // steady state, unrolled by two so the score buffers alternate without copies
     int t = 0;
     for (; t + 2 < n_tiles; t += 2) {
@@ -451,21 +496,25 @@ void attn_fwd_kernel(FwdParams p) {
   }
 
   // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log
-  const float l_tot = half_swap_sum(l_run);
-  const float inv = 1.f / l_tot;
-  if (my_row < N) {
-    uint16_t* orow = p.o + q_base + (size_t)my_row * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = half_swap_sum(l_run[qb]);
+    const float inv = 1.f / l_tot;
+    if (my_row[qb] < N) {
+      uint16_t* orow = p.o + q_base + (size_t)my_row[qb] * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * half;
-        f32x4 f = {acc[db][4 * g4 + 0] * inv, acc[db][4 * g4 + 1] * inv,
-                   acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv};
-        const bf16x4 bv = __builtin_convertvector(f, bf16x4);
-        *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, bv);
-      }
-    if (half == 0) p.lse[((size_t)b * p.H_q + h) * (size_t)N + my_row] = (m_used + __log2f(l_tot)) * kLn2;
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * half;
+          f32x4 f = {acc[db][qb][4 * g4 + 0] * inv, acc[db][qb][4 * g4 + 1] * inv,
+                     acc[db][qb][4 * g4 + 2] * inv, acc[db][qb][4 * g4 + 3] * inv};
+          const bf16x4 bv = __builtin_convertvector(f, bf16x4);
+          *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, bv);
+        }
+      if (half == 0)
+        p.lse[((size_t)b * p.H_q + h) * (size_t)N + my_row[qb]] = (m_used[qb] + __log2f(l_tot)) * kLn2;
+    }
   }
 }
 
