@@ -1,7 +1,7 @@
 """Checks that pin the CPU oracle to facts other than itself.
 
 Each check takes an oracle namespace `ora` (with attention_forward,
-attention_rows and kv_head) and raises AssertionError on failure.  They are
+attention_rows, kv_head and merge_partials) and raises AssertionError on failure.  They are
 run against the real oracle (all must pass) and against mutants of it with a
 planted mistake (at least one must fail), so each pin is shown to bite.
 
@@ -14,7 +14,12 @@ Pins used:
     every key by a common vector, large scores without overflow;
   * head map: both printed formulas agree, and GQA equals MHA on repeated K/V;
   * library special cases: scipy logsumexp of the scores, and PyTorch's
-    scaled_dot_product_attention in float64 on the CPU.
+    scaled_dot_product_attention in float64 on the CPU (with its lower-right
+    causal bias for N_q < N_kv);
+  * fewer query rows than keys: brute force, the suffix of square causal
+    attention, decode (one row sees every key);
+  * merge of partial results: disjoint key splits merged through their LSEs
+    equal attention over all keys.
 """
 from __future__ import annotations
 
@@ -44,9 +49,13 @@ def _close(a, b, tol=TOL, what=""):
 
 
 def _brute(q, k, v, is_causal, sm_scale):
-    """Scalar-loop attention with exactly rounded sums; tiny inputs only."""
+    """Scalar-loop attention with exactly rounded sums; tiny inputs only.
+
+    With fewer query rows than keys, causal row i sees keys 0..i + N_kv - N_q
+    (the last query row sees every key)."""
     B, H_q, N, D = q.shape
-    H_kv = k.shape[1]
+    H_kv, N_kv = k.shape[1], k.shape[2]
+    off = N_kv - N
     G = H_q // H_kv
     O = np.zeros((B, H_q, N, D))
     L = np.zeros((B, H_q, N))
@@ -54,7 +63,7 @@ def _brute(q, k, v, is_causal, sm_scale):
         for h in range(H_q):
             g = h // G
             for i in range(N):
-                keys = range(i + 1) if is_causal else range(N)
+                keys = range(i + off + 1) if is_causal else range(N_kv)
                 s = [sm_scale * math.fsum(q[b, h, i, d] * k[b, g, j, d] for d in range(D))
                      for j in keys]
                 mx = max(s)
@@ -78,6 +87,22 @@ def pin_brute_force_tiny(ora):
         Ob, Lb = _brute(q, k, v, causal, sc)
         _close(O, Ob, what="brute O")
         _close(L, Lb, what="brute LSE")
+
+
+def pin_brute_force_rect(ora):
+    """Fewer query rows than keys (prefill against a cache, decode)."""
+    rng = np.random.default_rng(16)
+    for (B, H_q, H_kv, N_q, N_kv, D, causal) in [
+        (1, 2, 1, 3, 8, 4, True), (2, 4, 2, 1, 9, 3, True), (1, 2, 2, 4, 7, 5, False),
+        (1, 3, 1, 1, 5, 2, False), (1, 2, 1, 6, 6, 3, True),
+    ]:
+        q = rng.standard_normal((B, H_q, N_q, D))
+        k = rng.standard_normal((B, H_kv, N_kv, D))
+        v = rng.standard_normal((B, H_kv, N_kv, D))
+        O, L = ora.attention_forward(q, k, v, is_causal=causal, sm_scale=0.6)
+        Ob, Lb = _brute(q, k, v, causal, 0.6)
+        _close(O, Ob, what="brute rect O")
+        _close(L, Lb, what="brute rect LSE")
 
 
 # ---------------------------------------------------------------- closed forms
@@ -226,6 +251,55 @@ def pin_large_scores(ora):
     _close(O[0, 0, 5], v[0, 0, 3], tol=1e-9, what="dominant key")
 
 
+def pin_causal_suffix(ora):
+    """N_q < N_kv causal rows are the last N_q rows of square causal attention
+    whose queries end with them (the rect case reduces to the square one)."""
+    q, k, v = _qkv(1, 2, 2, 10, 4, 161)
+    sc = 0.8
+    O, L = ora.attention_forward(q, k, v, is_causal=True, sm_scale=sc)
+    for n_q in (1, 3, 9):
+        Os, Ls = ora.attention_forward(q[:, :, 10 - n_q:], k, v, is_causal=True, sm_scale=sc)
+        _close(Os, O[:, :, 10 - n_q:], what="suffix O")
+        _close(Ls, L[:, :, 10 - n_q:], what="suffix LSE")
+
+
+def pin_decode_sees_all_keys(ora):
+    """A single query row with the causal flag attends to every key."""
+    q, k, v = _qkv(2, 4, 1, 1, 4, 171)
+    k = _rand((2, 1, 13, 4), 172)
+    v = _rand((2, 1, 13, 4), 173)
+    Oc, Lc = ora.attention_forward(q, k, v, is_causal=True, sm_scale=0.5)
+    On, Ln = ora.attention_forward(q, k, v, is_causal=False, sm_scale=0.5)
+    _close(Oc, On, what="decode O")
+    _close(Lc, Ln, what="decode LSE")
+
+
+def pin_merge_partials(ora):
+    """Attention over disjoint key subsets, merged through the LSEs, equals
+    attention over their union; an empty subset (lse = -inf, O = 0) adds
+    nothing; LSE values in the thousands do not overflow the merge."""
+    q, k, v = _qkv(1, 2, 1, 5, 4, 181)
+    k = _rand((1, 1, 23, 4), 182)
+    v = _rand((1, 1, 23, 4), 183)
+    for sc in (0.7, 300.0):
+        O, L = ora.attention_forward(q, k, v, is_causal=False, sm_scale=sc)
+        cuts = [0, 6, 6, 17, 23]                       # one empty split
+        os_, ls_ = [], []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            if a == b:
+                os_.append(np.zeros_like(O))
+                ls_.append(np.full_like(L, -np.inf))
+            else:
+                Op, Lp = ora.attention_forward(q, k[:, :, a:b], v[:, :, a:b], is_causal=False,
+                                               sm_scale=sc)
+                os_.append(Op)
+                ls_.append(Lp)
+        with np.errstate(over="raise"):
+            Om, Lm = ora.merge_partials(np.stack(os_), np.stack(ls_))
+        _close(Om, O, tol=1e-11, what="merged O")
+        _close(Lm, L, tol=1e-11, what="merged LSE")
+
+
 # ---------------------------------------------------------------- head map
 def pin_head_map(ora):
     """Both printed GQA formulas agree on every divisible pair up to 128 heads."""
@@ -280,9 +354,32 @@ def pin_torch_sdpa(ora):
         _close(O, ref, what="sdpa")
 
 
+def pin_torch_sdpa_lower_right(ora):
+    """N_q != N_kv against PyTorch: plain non-causal, and causal through its
+    bottom-right (lower-right) causal bias."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention.bias import causal_lower_right
+    rng = np.random.default_rng(191)
+    for (N_q, N_kv, causal) in [(7, 30, False), (30, 7, False), (7, 30, True), (1, 19, True)]:
+        q = rng.standard_normal((1, 2, N_q, 8))
+        k = rng.standard_normal((1, 2, N_kv, 8))
+        v = rng.standard_normal((1, 2, N_kv, 8))
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        if causal:
+            ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=causal_lower_right(N_q, N_kv),
+                                                 scale=0.3)
+        else:
+            ref = F.scaled_dot_product_attention(tq, tk, tv, scale=0.3)
+        O, _ = ora.attention_forward(q, k, v, is_causal=causal, sm_scale=0.3)
+        _close(O, ref.numpy(), what="sdpa lower-right")
+
+
 PINS = [
     pin_brute_force_tiny, pin_single_key, pin_two_keys, pin_zero_scale, pin_identical_keys,
     pin_causal_row0, pin_rows_sum_to_one, pin_convex_hull, pin_causal_prefix,
     pin_permutation, pin_key_shift, pin_large_scores, pin_head_map,
     pin_gqa_equals_repeated_mha, pin_scipy_logsumexp, pin_torch_sdpa,
+    pin_brute_force_rect, pin_causal_suffix, pin_decode_sees_all_keys, pin_merge_partials,
+    pin_torch_sdpa_lower_right,
 ]

@@ -103,10 +103,17 @@ MUTATIONS = {
     "lse_without_max": ("lse[s:s + ROW_BLOCK] = m + np.log(l)",
                         "lse[s:s + ROW_BLOCK] = np.log(l)"),
     "scale_dropped": ("S = sm_scale * (", "S = ("),
-    "causal_key_range_short": ("nk = int(r.max()) + 1 if is_causal else N",
-                               "nk = int(r.max()) if is_causal else N"),
+    "causal_key_range_short": ("nk = int(r.max()) + off + 1 if is_causal else N_kv",
+                               "nk = int(r.max()) + off if is_causal else N_kv"),
+    "causal_offset_ignored": ("off = N_kv - N_q if is_causal else 0", "off = 0"),
+    "causal_offset_wrong_sign": ("off = N_kv - N_q if is_causal else 0",
+                                 "off = N_q - N_kv if is_causal else 0"),
     "v_replaced_by_k": ("Vg = v[b, g, :nk, :]", "Vg = k[b, g, :nk, :]"),
     "keys_reversed": ("Kg = k[b, g, :nk, :]", "Kg = k[b, g, :nk, :][::-1]"),
+    "merge_without_max": ("w = np.exp(lse_parts - m[None])", "w = np.exp(lse_parts)"),
+    "merge_lse_without_max": ("lse = m + np.log(tot)", "lse = np.log(tot)"),
+    "merge_unnormalised": ("(w[..., None] * o_parts).sum(axis=0) / tot[..., None]",
+                           "(w[..., None] * o_parts).sum(axis=0)"),
 }
 
 
@@ -119,7 +126,7 @@ def _mutant(old, new):
     class M:
         pass
     m = M()
-    for name in ("attention_forward", "attention_rows", "kv_head"):
+    for name in ("attention_forward", "attention_rows", "kv_head", "merge_partials"):
         setattr(m, name, ns[name])
     return m
 
