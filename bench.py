@@ -97,7 +97,8 @@ def cpu_baseline(w, q64, k64, v64, budget_s=15.0):
     cores = max(1, min(cores, 16))
     rng = np.random.default_rng(12345)
     blk = 512
-    n_blocks = (w.N + blk - 1) // blk
+    n_blocks = (w.Nq + blk - 1) // blk
+    off = w.N - w.Nq if w.causal else 0
     flops = 0.0
     done = 0
     t0 = time.perf_counter()
@@ -112,9 +113,9 @@ def cpu_baseline(w, q64, k64, v64, budget_s=15.0):
             b = int(rng.integers(w.B))
             h = int(rng.integers(w.H_q))
             r0 = int(rng.integers(n_blocks)) * blk
-            rows = np.arange(r0, min(r0 + blk, w.N))
+            rows = np.arange(r0, min(r0 + blk, w.Nq))
             f = ex.submit(_oracle_unit_shared, (b, h, rows, w.causal, w.sm_scale))
-            vis = (rows + 1).sum() if w.causal else rows.size * w.N
+            vis = (rows + off + 1).sum() if w.causal else rows.size * w.N
             pending.add((f, 4.0 * w.D * float(vis)))
             submitted += 1
 
@@ -145,26 +146,40 @@ def cpu_baseline(w, q64, k64, v64, budget_s=15.0):
 
 
 # ---------------------------------------------------------------- GPU timing
+def make_step(ea, torch, w, qd, kd, vd, out, lse):
+    """One call over the whole workload: attn_fwd for square workloads, else
+    attn_fwd_splitkv with the library's split count and a preallocated workspace."""
+    if w.N_q is None:
+        return (lambda: ea.attn_fwd(qd, kd, vd, out, lse, is_causal=w.causal,
+                                    sm_scale=w.sm_scale)), 1
+    ns = ea.attn_splitkv_num_splits(w.B, w.H_q, w.H_kv, w.Nq, w.N, w.D, w.causal)
+    nbytes = ea.attn_splitkv_workspace_size(w.B, w.H_q, w.Nq, w.D, ns)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=qd.device) if nbytes else None
+    return (lambda: ea.attn_fwd_splitkv(qd, kd, vd, out, lse, is_causal=w.causal,
+                                        sm_scale=w.sm_scale, n_splits=ns, workspace=ws)), ns
+
+
 def time_workload(ea, torch, w, steps, warmup):
     dev = torch.device("cuda", 0)
     q, k, v = workloads.workload_inputs(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty(w.q_shape(), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((w.B, w.H_q, w.N), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H_q, w.Nq), dtype=torch.float32, device=dev)
+    step, n_splits = make_step(ea, torch, w, qd, kd, vd, out, lse)
     for _ in range(warmup):
-        ea.attn_fwd(qd, kd, vd, out, lse, is_causal=w.causal, sm_scale=w.sm_scale)
+        step()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record()
-        ea.attn_fwd(qd, kd, vd, out, lse, is_causal=w.causal, sm_scale=w.sm_scale)
+        step()
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    res = {"wall_ms_per_step": wall * 1e3 / steps, "event_ms": ev_ms}
+    res = {"wall_ms_per_step": wall * 1e3 / steps, "event_ms": ev_ms, "n_splits": n_splits}
     return res, (q, k, v, out, lse)
 
 
@@ -179,8 +194,9 @@ def sampled_parity(w, q, k, v, out, lse):
     max_o = max_l = 0.0
     ok = bool(torch_isfinite_all(o) and torch_isfinite_all(l))
     for h in sorted({0, w.H_q - 1, int(rng.integers(w.H_q))}):
-        rows = np.unique(np.concatenate([[0, 1, 63, 64, w.N // 2, w.N - 1],
-                                         rng.choice(w.N, 10, replace=False)]))
+        n = w.Nq
+        rows = np.unique(np.concatenate([[r for r in (0, 1, 63, 64, n // 2, n - 1) if r < n],
+                                         rng.choice(n, min(10, n), replace=False)])).astype(np.int64)
         Or, Lr = oracle.attention_rows(q64, k64, v64, 0, h, rows, is_causal=w.causal,
                                        sm_scale=w.sm_scale)
         og = o[0, h, rows].double().numpy()
@@ -251,8 +267,10 @@ def main():
             r, _ = time_workload(ea, torch, ww, 10, 3)
             e = r["event_ms"]
             tf = ww.flops() / (float(np.median(e)) * 1e-3) / 1e12
+            gbs = ww.algorithmic_bytes() / (float(np.median(e)) * 1e-3) / 1e9
             log(f"[sweep] {name:24s} median {float(np.median(e)):9.4f} ms  min {min(e):9.4f} ms  "
-                f"{tf:8.1f} TFLOP/s  {100 * tf / PEAK_BF16_TFLOPS:5.1f}% of peak")
+                f"{tf:8.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:5.1f}%)  {gbs:7.0f} GB/s "
+                f"({100 * gbs / PEAK_HBM_GBS:5.1f}%)  splits {r['n_splits']}")
 
     cpu = parity = None
     if not args.no_cpu_baseline:
@@ -265,6 +283,18 @@ def main():
         log(f"[bench] cpu_baseline {cpu}")
 
     traffic = read_traffic(w.name)
+    nbytes = w.algorithmic_bytes()
+    if flops / nbytes >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        # below the ridge (decode): bytes moved, not FLOPs, bound the kernel
+        gbs = nbytes / (avg_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roofline.update({"traffic": traffic, "kernel": "attn_fwd_kernel", "avg_launch_ms": round(avg_ms, 4),
+                     "n_splits": res["n_splits"],
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes})
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -279,14 +309,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "N": w.N,
-                   "D": w.D, "causal": w.causal, "seed": w.seed},
+                   "N_q": w.Nq, "D": w.D, "causal": w.causal, "seed": w.seed},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic,
-                     "kernel": "attn_fwd_kernel", "avg_launch_ms": round(avg_ms, 4),
-                     "algorithmic_flops_per_launch": flops,
-                     "algorithmic_bytes_per_launch": w.algorithmic_bytes()},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
     }

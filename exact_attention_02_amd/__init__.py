@@ -6,9 +6,11 @@ If the library is not built, every call raises; there is no fallback path.
 
     out, lse = fwd(q, k, v, is_causal=True)          # allocates out and lse
     attn_fwd(q, k, v, out, lse, is_causal=True)      # caller-provided buffers
+    out, lse = fwd_splitkv(q1, k, v, is_causal=True) # N_q != N_kv, key splits, decode
 
 q: [B, H_q, N, D] bf16, k and v: [B, H_kv, N, D] bf16, contiguous, on the
-current CUDA (HIP) device; out: like q; lse: [B, H_q, N] float32.
+current CUDA (HIP) device; out: like q; lse: [B, H_q, N] float32.  The split
+entry points take q with N_q rows and k, v with N_kv rows.
 The same names and semantics as the C functions declared in include/attn.h.
 """
 from __future__ import annotations
@@ -19,10 +21,12 @@ import os
 
 from .build import LIB_PATH
 
-__all__ = ["attn_fwd", "fwd", "attn_status_string", "attn_abi_version", "load_library",
-           "AttnError", "EXPORTED_SYMBOLS"]
+__all__ = ["attn_fwd", "fwd", "attn_fwd_splitkv", "fwd_splitkv", "attn_splitkv_num_splits",
+           "attn_splitkv_workspace_size", "attn_status_string", "attn_abi_version",
+           "load_library", "AttnError", "EXPORTED_SYMBOLS"]
 
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_status_string", "attn_abi_version")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splitkv", "attn_splitkv_num_splits",
+                    "attn_splitkv_workspace_size", "attn_status_string", "attn_abi_version")
 
 _lib = None
 
@@ -45,6 +49,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_fwd_splitkv.restype = ctypes.c_int
+    lib.attn_fwd_splitkv.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p]
+    lib.attn_splitkv_num_splits.restype = ctypes.c_int64
+    lib.attn_splitkv_num_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int]
+    lib.attn_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.attn_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 5
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_abi_version.restype = ctypes.c_int
@@ -76,6 +88,13 @@ def _check_tensor(t, name, shape, dtype):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
 def attn_fwd(q, k, v, out, lse, is_causal: bool = False, sm_scale: float | None = None,
              stream=None) -> None:
     """Enqueue the forward on `stream` (default: torch's current stream) into out/lse."""
@@ -94,9 +113,7 @@ def attn_fwd(q, k, v, out, lse, is_causal: bool = False, sm_scale: float | None 
             raise ValueError(f"{name} is on {t.device}, q on {q.device}")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    handle = _stream_handle(stream, q.device)
     lib = load_library()
     with torch.cuda.device(q.device):
         st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -112,4 +129,74 @@ def fwd(q, k, v, is_causal: bool = False, sm_scale: float | None = None, stream=
     out = torch.empty((B, H_q, N, D), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, H_q, N), dtype=torch.float32, device=q.device)
     attn_fwd(q, k, v, out, lse, is_causal=is_causal, sm_scale=sm_scale, stream=stream)
+    return out, lse
+
+
+def attn_splitkv_num_splits(B: int, H_q: int, H_kv: int, N_q: int, N_kv: int, D: int,
+                            is_causal: bool = False) -> int:
+    """Split count the library picks for n_splits=0 on the current device (-1: bad sizes)."""
+    return int(load_library().attn_splitkv_num_splits(B, H_q, H_kv, N_q, N_kv, D,
+                                                      int(bool(is_causal))))
+
+
+def attn_splitkv_workspace_size(B: int, H_q: int, N_q: int, D: int, n_splits: int) -> int:
+    """Workspace bytes attn_fwd_splitkv needs for n_splits key ranges (0 when n_splits <= 1)."""
+    return int(load_library().attn_splitkv_workspace_size(B, H_q, N_q, D, n_splits))
+
+
+def attn_fwd_splitkv(q, k, v, out, lse, is_causal: bool = False, sm_scale: float | None = None,
+                     n_splits: int = 0, workspace=None, stream=None) -> None:
+    """Enqueue the N_q x N_kv forward with n_splits key ranges (0: library's choice).
+
+    workspace: a contiguous device tensor of at least attn_splitkv_workspace_size(...)
+    bytes (any dtype), or None when the split count used is 1."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, D]")
+    B, H_q, N_q, D = q.shape
+    H_kv, N_kv = k.shape[1], k.shape[2]
+    _check_tensor(q, "q", (B, H_q, N_q, D), torch.bfloat16)
+    _check_tensor(k, "k", (B, H_kv, N_kv, D), torch.bfloat16)
+    _check_tensor(v, "v", (B, H_kv, N_kv, D), torch.bfloat16)
+    _check_tensor(out, "out", (B, H_q, N_q, D), torch.bfloat16)
+    _check_tensor(lse, "lse", (B, H_q, N_q), torch.float32)
+    for name, t in (("k", k), ("v", v), ("out", out), ("lse", lse)):
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != q.device:
+            raise ValueError("workspace must be a tensor on q's device")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr(), B, H_q, H_kv, N_q, N_kv, D, float(sm_scale),
+                                  int(bool(is_causal)), int(n_splits), ws_ptr, ws_bytes, handle)
+    if st != 0:
+        raise AttnError(st, attn_status_string(st))
+
+
+def fwd_splitkv(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
+                n_splits: int = 0, stream=None):
+    """Allocate out, lse and the workspace, run attn_fwd_splitkv, return (out, lse)."""
+    import torch
+    B, H_q, N_q, D = q.shape
+    H_kv, N_kv = k.shape[1], k.shape[2]
+    out = torch.empty((B, H_q, N_q, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        ns = n_splits if n_splits > 0 else attn_splitkv_num_splits(B, H_q, H_kv, N_q, N_kv, D,
+                                                                   is_causal)
+    ws = None
+    if ns > 1:
+        nbytes = attn_splitkv_workspace_size(B, H_q, N_q, D, ns)
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
+    attn_fwd_splitkv(q, k, v, out, lse, is_causal=is_causal, sm_scale=sm_scale,
+                     n_splits=max(ns, 1), workspace=ws, stream=stream)
     return out, lse

@@ -1,10 +1,12 @@
 // C ABI of the fused attention forward (declared in include/attn.h):
-// argument validation, tile-configuration choice and kernel launch.
+// argument validation, kernel-shape and split choice, and kernel launches.
 // The library allocates nothing, keeps no state and never synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cfloat>
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 
 #include "../../include/attn.h"
@@ -13,42 +15,204 @@
 namespace {
 
 using ea02::FwdParams;
+using ea02::MergeParams;
 
-// Kernel shape: KQB query blocks of 32 rows per wave, KNW waves per
-// workgroup, KP LDS stages.
-constexpr int kQB = 1;
-constexpr int kNW = kQB == 1 ? 8 : 4;
-constexpr int kBN = kQB == 1 ? 64 : 32;
-constexpr int kP = 4;
-
-int gcd_int(int a, int b) {
-  while (b) {
-    int t = a % b;
-    a = b;
-    b = t;
-  }
-  return a;
-}
+// Kernel shapes.  Wide: eight waves of 32 (row, head) pairs share each K/V
+// tile (256 pairs per workgroup, 64-key tiles, four LDS stages, 128 KiB LDS).
+// Narrow: one wave of 32 pairs (32-key tiles, four stages, 64 KiB LDS, two
+// workgroups per CU) for kv heads with at most kNarrowPairs pairs, e.g. a
+// decode step, where the wide shape would leave most waves without a query.
+constexpr int kWideNW = 8, kWideP = 4, kWideBN = 64;
+constexpr int kNarrowNW = 1, kNarrowP = 4, kNarrowBN = 32;
+constexpr int kNarrowPairs = 64;
+constexpr int kMaxSplits = 256;
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
 }
 
-template <int D, int HW>
-hipError_t launch(const FwdParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, HW, kNW, kP, kQB, kBN>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+struct Shape {
+  bool narrow;
+  int pairs_per_wg;
+  int bn;
+  int wg_per_cu;
+};
+
+Shape pick_shape(int64_t n_pairs) {
+  if (n_pairs <= kNarrowPairs) return {true, 32 * kNarrowNW, kNarrowBN, 2};
+  return {false, 32 * kWideNW, kWideBN, 1};
+}
+
+template <int D, bool SPLIT>
+hipError_t launch_fwd(bool narrow, const FwdParams& p, int grid, hipStream_t stream) {
+  if (narrow)
+    hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kNarrowNW, kNarrowP, 1, kNarrowBN, SPLIT>), dim3(grid),
+                       dim3(kNarrowNW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kWideNW, kWideP, 1, kWideBN, SPLIT>), dim3(grid),
+                       dim3(kWideNW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const FwdParams& p, int hw, int grid, hipStream_t stream) {
-  switch (hw) {
-    case 8: if constexpr (kNW >= 8) return launch<D, 8>(p, grid, stream); else return hipErrorInvalidValue;
-    case 4: return launch<D, 4>(p, grid, stream);
-    case 2: return launch<D, 2>(p, grid, stream);
-    default: return launch<D, 1>(p, grid, stream);
+hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
+  constexpr int rows_per_block = 256 / (D / 4);
+  const int64_t blocks = (m.rows + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL((ea02::attn_merge_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, m);
+  return hipGetLastError();
+}
+
+// Arguments shared by both entry points, after validation.
+struct Problem {
+  const void *q, *k, *v;
+  void* out;
+  float* lse;
+  int64_t B, H_q, H_kv, N_q, N_kv, D;
+  float sm_scale;
+  int is_causal;
+};
+
+// Checks common to both entry points, in the documented order, up to and
+// including the empty-work test (*empty set when there is nothing to do).
+int check_sizes(const Problem& a, int64_t n_splits, bool* empty) {
+  *empty = false;
+  if (a.B < 0 || a.H_q < 0 || a.H_kv < 0 || a.N_q < 0 || a.N_kv < 0 || a.D < 0 || n_splits < 0)
+    return ATTN_ERR_NEGATIVE_SIZE;
+  if (a.H_kv < 1 || a.H_q % a.H_kv != 0) return ATTN_ERR_HEAD_RATIO;
+  if (a.D != 64 && a.D != 128) return ATTN_ERR_HEAD_DIM;
+  if (a.is_causal != 0 && a.is_causal != 1) return ATTN_ERR_CAUSAL_FLAG;
+  if (!std::isfinite(a.sm_scale)) return ATTN_ERR_SCALE;
+  if (n_splits > kMaxSplits) return ATTN_ERR_SPLITS;
+  if (a.is_causal && a.N_q > a.N_kv) return ATTN_ERR_CAUSAL_SHAPE;
+  // K/V rows are addressed with 32-bit byte offsets within one kv head
+  const int64_t lim24 = int64_t(1) << 24;
+  if (a.N_q > lim24 || a.N_kv > lim24 || a.N_kv * a.D * 2 > (int64_t(1) << 31) || a.B > lim24 ||
+      a.H_q > (int64_t(1) << 16) || a.B * a.H_q * a.N_q > INT32_MAX)
+    return ATTN_ERR_SIZE_OVERFLOW;
+  const int64_t n_pairs = a.N_q * (a.H_q / a.H_kv);
+  if (n_pairs > (int64_t(1) << 30)) return ATTN_ERR_SIZE_OVERFLOW;
+  const Shape sh = pick_shape(n_pairs);
+  const int64_t grid = ((n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg) * a.B * a.H_kv *
+                       (n_splits > 1 ? n_splits : 1);
+  if (grid > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
+  if (a.B == 0 || a.H_q == 0 || a.N_q == 0) {
+    *empty = true;
+    return ATTN_OK;
   }
+  if (a.N_kv == 0) return ATTN_ERR_NO_KEYS;
+  return ATTN_OK;
+}
+
+int check_buffers(const Problem& a) {
+  if (!a.q || !a.k || !a.v || !a.out || !a.lse) return ATTN_ERR_NULL_POINTER;
+  auto mis16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+  if (mis16(a.q) || mis16(a.k) || mis16(a.v) || mis16(a.out) || (reinterpret_cast<uintptr_t>(a.lse) & 3u))
+    return ATTN_ERR_ALIGNMENT;
+  return ATTN_OK;
+}
+
+int check_alias(const Problem& a, const void* ws, size_t ws_used) {
+  const size_t nq = size_t(a.B * a.H_q * a.N_q * a.D) * 2, nkv = size_t(a.B * a.H_kv * a.N_kv * a.D) * 2;
+  const size_t nl = size_t(a.B * a.H_q * a.N_q) * 4;
+  const void* ins[3] = {a.q, a.k, a.v};
+  const size_t in_n[3] = {nq, nkv, nkv};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(a.out, nq, ins[i], in_n[i]) || overlaps(a.lse, nl, ins[i], in_n[i]) ||
+        overlaps(ws, ws_used, ins[i], in_n[i]))
+      return ATTN_ERR_ALIAS;
+  if (overlaps(a.out, nq, a.lse, nl) || overlaps(ws, ws_used, a.out, nq) || overlaps(ws, ws_used, a.lse, nl))
+    return ATTN_ERR_ALIAS;
+  return ATTN_OK;
+}
+
+size_t workspace_bytes(int64_t B, int64_t H_q, int64_t N_q, int64_t D, int64_t n_splits) {
+  if (n_splits <= 1) return 0;
+  return size_t(n_splits) * size_t(B * H_q * N_q) * size_t(D + 1) * 4;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+
+// Number of key splits the library picks: none while the unsplit grid already
+// fills every CU slot; otherwise enough splits for about two workgroups per
+// slot, each split keeping at least 8 key tiles.
+int64_t choose_splits(const Problem& a) {
+  const int64_t n_pairs = a.N_q * (a.H_q / a.H_kv);
+  const Shape sh = pick_shape(n_pairs);
+  const int64_t wgs = ((n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg) * a.B * a.H_kv;
+  const int64_t slots = int64_t(device_cus()) * sh.wg_per_cu;
+  if (wgs <= 0 || wgs >= slots) return 1;
+  const int64_t tiles = (a.N_kv + sh.bn - 1) / sh.bn;
+  int64_t n = (2 * slots + wgs - 1) / wgs;
+  n = std::min<int64_t>(n, tiles / 8);
+  n = std::min<int64_t>(n, kMaxSplits);
+  return n < 1 ? 1 : n;
+}
+
+// Launch after every check passed: one pass when n_splits <= 1, else the split
+// pass into the workspace followed by the merge.
+int run(const Problem& a, int64_t n_splits, void* ws, void* stream) {
+  const int G = static_cast<int>(a.H_q / a.H_kv);
+  const int64_t n_pairs = a.N_q * G;
+  const Shape sh = pick_shape(n_pairs);
+  const int64_t n_pair_blocks = (n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg;
+  const bool split = n_splits > 1;
+  const int64_t grid = n_pair_blocks * a.B * a.H_kv * (split ? n_splits : 1);
+  const int64_t rows = a.B * a.H_q * a.N_q;
+
+  FwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<uint16_t*>(a.out);
+  p.lse = a.lse;
+  p.o_part = split ? static_cast<float*>(ws) : nullptr;
+  p.lse_part = split ? static_cast<float*>(ws) + size_t(n_splits) * size_t(rows) * size_t(a.D) : nullptr;
+  p.B = static_cast<int>(a.B);
+  p.H_q = static_cast<int>(a.H_q);
+  p.H_kv = static_cast<int>(a.H_kv);
+  p.N_q = static_cast<int>(a.N_q);
+  p.N_kv = static_cast<int>(a.N_kv);
+  p.G = G;
+  p.n_pairs = static_cast<int>(n_pairs);
+  p.causal_off = a.is_causal ? static_cast<int>(a.N_kv - a.N_q) : 0;
+  p.n_pair_blocks = static_cast<int>(n_pair_blocks);
+  p.n_heads_wg = static_cast<int>(a.B * a.H_kv);
+  p.n_splits = split ? static_cast<int>(n_splits) : 1;
+  // A zero scale becomes the smallest normal float: finite scores times it
+  // round to 0 in the exponent (uniform weights, as for a zero scale), while
+  // masked scores (-inf) stay -inf instead of turning into NaN.
+  p.scale_log2 = std::fmax(std::fabs(a.sm_scale) * ea02::kLog2e, FLT_MIN);
+  p.q_sign = (a.sm_scale < 0.f) ? 0x80008000u : 0u;
+  p.causal = a.is_causal;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int g32 = static_cast<int>(grid);
+  hipError_t err;
+  if (!split)
+    err = (a.D == 128) ? launch_fwd<128, false>(sh.narrow, p, g32, s) : launch_fwd<64, false>(sh.narrow, p, g32, s);
+  else
+    err = (a.D == 128) ? launch_fwd<128, true>(sh.narrow, p, g32, s) : launch_fwd<64, true>(sh.narrow, p, g32, s);
+  if (err != hipSuccess) return ATTN_ERR_LAUNCH;
+  if (split) {
+    MergeParams m;
+    m.o_part = p.o_part;
+    m.lse_part = p.lse_part;
+    m.o = p.o;
+    m.lse = p.lse;
+    m.rows = rows;
+    m.n_splits = p.n_splits;
+    err = (a.D == 128) ? launch_merge<128>(m, s) : launch_merge<64>(m, s);
+    if (err != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
 }
 
 }  // namespace
@@ -56,58 +220,44 @@ hipError_t launch_d(const FwdParams& p, int hw, int grid, hipStream_t stream) {
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                         int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t D,
                         float sm_scale, int is_causal, void* stream) {
-  if (B < 0 || H_q < 0 || H_kv < 0 || N < 0 || D < 0) return ATTN_ERR_NEGATIVE_SIZE;
-  if (H_kv < 1 || H_q % H_kv != 0) return ATTN_ERR_HEAD_RATIO;
-  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
-  if (is_causal != 0 && is_causal != 1) return ATTN_ERR_CAUSAL_FLAG;
-  if (!std::isfinite(sm_scale)) return ATTN_ERR_SCALE;
-  if (N > (int64_t(1) << 24) || B > (int64_t(1) << 24) || H_q > (int64_t(1) << 16))
-    return ATTN_ERR_SIZE_OVERFLOW;
-  const int G = static_cast<int>(H_q / H_kv);
-  const int hw = gcd_int(G, kNW);
-  const int BM = 32 * kQB * kNW / hw;
-  const int64_t n_row_blocks = (N + BM - 1) / BM;
-  const int64_t n_head_groups = G / hw;
-  const int64_t n_heads_wg = B * H_kv * n_head_groups;
-  const int64_t grid = n_heads_wg * n_row_blocks;
-  if (grid > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
-  if (B == 0 || H_q == 0 || N == 0) return ATTN_OK;
-  if (!q || !k || !v || !out || !lse) return ATTN_ERR_NULL_POINTER;
-  auto mis16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
-  if (mis16(q) || mis16(k) || mis16(v) || mis16(out) || (reinterpret_cast<uintptr_t>(lse) & 3u))
-    return ATTN_ERR_ALIGNMENT;
-  const size_t nq = size_t(B * H_q * N * D) * 2, nkv = size_t(B * H_kv * N * D) * 2;
-  const size_t nl = size_t(B * H_q * N) * 4;
-  if (overlaps(out, nq, q, nq) || overlaps(out, nq, k, nkv) || overlaps(out, nq, v, nkv) ||
-      overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) || overlaps(lse, nl, v, nkv) ||
-      overlaps(out, nq, lse, nl))
-    return ATTN_ERR_ALIAS;
+  const Problem a{q, k, v, out, lse, B, H_q, H_kv, N, N, D, sm_scale, is_causal};
+  bool empty = false;
+  int st = check_sizes(a, 1, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if ((st = check_buffers(a)) != ATTN_OK) return st;
+  if ((st = check_alias(a, nullptr, 0)) != ATTN_OK) return st;
+  return run(a, 1, nullptr, stream);
+}
 
-  FwdParams p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.o = static_cast<uint16_t*>(out);
-  p.lse = lse;
-  p.B = static_cast<int>(B);
-  p.H_q = static_cast<int>(H_q);
-  p.H_kv = static_cast<int>(H_kv);
-  p.N = static_cast<int>(N);
-  p.G = G;
-  p.n_row_blocks = static_cast<int>(n_row_blocks);
-  p.n_head_groups = static_cast<int>(n_head_groups);
-  p.n_heads_wg = static_cast<int>(n_heads_wg);
-  // A zero scale becomes the smallest normal float: finite scores times it
-  // round to 0 in the exponent (uniform weights, as for a zero scale), while
-  // masked scores (-inf) stay -inf instead of turning into NaN.
-  p.scale_log2 = std::fmax(std::fabs(sm_scale) * ea02::kLog2e, FLT_MIN);
-  p.q_sign = (sm_scale < 0.f) ? 0x80008000u : 0u;
-  p.causal = is_causal;
+extern "C" int64_t attn_splitkv_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv,
+                                           int64_t D, int is_causal) {
+  const Problem a{nullptr, nullptr, nullptr, nullptr, nullptr, B, H_q, H_kv, N_q, N_kv, D, 1.f, is_causal};
+  bool empty = false;
+  if (check_sizes(a, 0, &empty) != ATTN_OK) return -1;
+  if (empty) return 1;
+  return choose_splits(a);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t err = (D == 128) ? launch_d<128>(p, hw, static_cast<int>(grid), s)
-                                    : launch_d<64>(p, hw, static_cast<int>(grid), s);
-  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+extern "C" size_t attn_splitkv_workspace_size(int64_t B, int64_t H_q, int64_t N_q, int64_t D, int64_t n_splits) {
+  if (B < 0 || H_q < 0 || N_q < 0 || D < 0 || n_splits < 0 || n_splits > kMaxSplits) return 0;
+  return workspace_bytes(B, H_q, N_q, D, n_splits);
+}
+
+extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                                int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t D,
+                                float sm_scale, int is_causal, int64_t n_splits, void* workspace,
+                                size_t workspace_size, void* stream) {
+  const Problem a{q, k, v, out, lse, B, H_q, H_kv, N_q, N_kv, D, sm_scale, is_causal};
+  bool empty = false;
+  int st = check_sizes(a, n_splits, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if ((st = check_buffers(a)) != ATTN_OK) return st;
+  const int64_t ns = n_splits == 0 ? choose_splits(a) : n_splits;
+  const size_t need = workspace_bytes(B, H_q, N_q, D, ns);
+  if (need > 0 && (!workspace || workspace_size < need || (reinterpret_cast<uintptr_t>(workspace) & 15u)))
+    return ATTN_ERR_WORKSPACE;
+  if ((st = check_alias(a, workspace, need)) != ATTN_OK) return st;
+  return run(a, ns, workspace, stream);
 }
 
 extern "C" const char* attn_status_string(int status) {
@@ -118,13 +268,18 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
     case ATTN_ERR_CAUSAL_FLAG: return "is_causal must be 0 or 1";
     case ATTN_ERR_SCALE: return "sm_scale must be finite";
-    case ATTN_ERR_SIZE_OVERFLOW: return "sizes exceed the supported range (N <= 2^24, grid < 2^31)";
+    case ATTN_ERR_SIZE_OVERFLOW:
+      return "sizes exceed the supported range (N <= 2^24, N_kv*D*2 <= 2^31, B*H_q*N_q < 2^31, N_q*H_q/H_kv <= 2^30)";
     case ATTN_ERR_NULL_POINTER: return "a buffer pointer is NULL";
     case ATTN_ERR_ALIGNMENT: return "q, k, v, out must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_ALIAS: return "out or lse overlaps an input or each other";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_CAUSAL_SHAPE: return "is_causal needs N_q <= N_kv";
+    case ATTN_ERR_NO_KEYS: return "N_kv is 0 while there are query rows";
+    case ATTN_ERR_SPLITS: return "n_splits must be in [0, 256]";
+    case ATTN_ERR_WORKSPACE: return "workspace is NULL, too small or not 16-byte aligned";
     default: return "unknown status";
   }
 }
 
-extern "C" int attn_abi_version(void) { return 1; }
+extern "C" int attn_abi_version(void) { return 2; }

@@ -24,20 +24,29 @@
 //    index.  K fragments are 128-bit LDS reads; V^T fragments come from the
 //    LDS transpose read ds_read_b64_tr_b16 on the untransposed V tile, two per
 //    MFMA, in the key order the S^T accumulator layout implies.
-//  * Two LDS buffers: the loads of tile t+1 are issued right after the barrier
-//    that opens tile t and land while tile t is computed; one barrier per tile.
+//  * A ring of P LDS stages for K and for V: after the barrier that opens tile
+//    t the loads of tile t+P are issued into the stage tile t-1 used, so P-1
+//    tiles are in flight while one is computed; one barrier per tile.
 //  * Lazy rescaling: the max used in the exponent is raised only when some
 //    row's true max exceeds it by more than 2^8 (a wave-uniform branch), so
 //    P <= 256 and the accumulator is rescaled on a few tiles only.  The final
 //    O = acc / l and LSE use the same max, so the result is exact up to
 //    rounding.
-//  * GQA/MQA: the waves of a workgroup take different query heads of one kv
-//    group over the same rows, so each K/V tile in LDS serves all of them.
+//  * GQA/MQA: a workgroup serves one kv head.  Its MFMA columns enumerate
+//    (query row, query head) pairs of that kv group, row-major with the G =
+//    H_q/H_kv heads fastest, so every K/V tile in LDS serves all G heads and a
+//    decode step (one query row) still fills G columns.
 //  * Causal: the tile loop ends at the workgroup's last row; only tiles that
-//    cross a wave's diagonal (or the ragged end of the sequence) run the
-//    masked variant; tiles wholly above a wave's rows are skipped by it.
-//  * Rows past the end of the sequence are clamped to the last row on load
-//    (their keys are masked, their outputs not stored), so loads need no
+//    cross a wave's diagonal (or the ragged end of the keys) run the masked
+//    variant.  With fewer query rows than keys the mask is bottom-right
+//    aligned: row i sits at key position i + N_kv - N_q.
+//  * Split of the key axis (SPLIT): blockIdx also selects one of n_splits
+//    contiguous ranges of the workgroup's key tiles, and the workgroup writes
+//    an fp32 partial result (O normalised by its own l, and log2 l + m) that
+//    the merge kernel combines through the log-sum-exps (page "Attention
+//    Kernel 实现与正确性验证", section 2.4, split-T with a safe-softmax merge).
+//  * Pairs and keys past the ends are clamped to the last valid one on load
+//    (their scores are masked, their outputs not stored), so loads need no
 //    bounds branches.
 #pragma once
 
@@ -60,16 +69,20 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct FwdParams {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* o;
-  float* lse;
-  int B, H_q, H_kv, N;
+  const uint16_t* q;  // [B, H_q, N_q, D] bf16
+  const uint16_t* k;  // [B, H_kv, N_kv, D] bf16
+  const uint16_t* v;  // [B, H_kv, N_kv, D] bf16
+  uint16_t* o;        // [B, H_q, N_q, D] bf16 (single pass)
+  float* lse;         // [B, H_q, N_q] natural log (single pass)
+  float* o_part;      // [n_splits, B, H_q, N_q, D] fp32 (split pass)
+  float* lse_part;    // [n_splits, B, H_q, N_q] log2 units (split pass)
+  int B, H_q, H_kv, N_q, N_kv;
   int G;              // H_q / H_kv
-  int n_row_blocks;   // ceil(N / rows per workgroup)
-  int n_head_groups;  // G / heads per workgroup
-  int n_heads_wg;     // B * H_kv * n_head_groups: workgroups per row block
+  int n_pairs;        // N_q * G: (row, head) pairs per kv head
+  int causal_off;     // N_kv - N_q when causal, else 0
+  int n_pair_blocks;  // ceil(n_pairs / pairs per workgroup)
+  int n_heads_wg;     // B * H_kv
+  int n_splits;       // key-axis splits (1 for the single pass)
   float scale_log2;   // max(|sm_scale| * log2(e), FLT_MIN): strictly positive, so
                       // a masked score (-inf) never meets a zero factor
   uint32_t q_sign;    // 0x80008000 when sm_scale < 0 (Q is negated on load), else 0
@@ -150,6 +163,7 @@ struct Cfg {
   static_assert(BN == 32 || BN == 64, "key tiles of 32 or 64");
   static_assert(LOADS % NW == 0 && LOADS_PER_WAVE >= 1, "tile loads split evenly over waves");
   static_assert(P >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
+  static_assert((P - 1) * 2 * LOADS_PER_WAVE <= 63, "loads in flight fit the 6-bit vmcnt");
 };
 
 // 16-byte chunk swizzles.  K: the 16 (D=128) or 8 (D=64) chunks of a row are
@@ -168,17 +182,18 @@ __device__ __forceinline__ int v_swz(int row) {
   else return 4 * ((row >> 1) & 1);
 }
 
-// QB = 1: eight waves of 32 query rows, two waves per SIMD (256 VGPRs each).
-// QB = 2: four waves of 64 query rows, one wave per SIMD (512 registers): each
-// K or V^T fragment read from LDS feeds two MFMAs, halving LDS traffic per
-// FLOP, and the accumulators fit in the AGPR half of the register file.
-template <int D, int HW, int NW, int P, int QB, int BN_>
+// QB = 1: waves of 32 (row, head) pairs, two waves per SIMD (256 VGPRs each).
+// QB = 2: 64 pairs per wave, one wave per SIMD (512 registers): each K or V^T
+// fragment read from LDS feeds two MFMAs, halving LDS traffic per FLOP.
+// SPLIT: write the fp32 partial result of one key range instead of the final
+// bf16 output.
+template <int D, int NW, int P, int QB, int BN_, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void attn_fwd_kernel(FwdParams p) {
   using C = Cfg<D, NW, P, QB, BN_>;
   constexpr int BN = C::BN;
-  constexpr int BM = C::QW * C::NW / HW;  // query rows per workgroup
+  constexpr int PPW = C::QW * C::NW;  // (row, head) pairs per workgroup
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -187,43 +202,60 @@ void attn_fwd_kernel(FwdParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // ---- work decomposition: heaviest row blocks first (causal), heads fastest
+  // ---- work decomposition: heaviest pair blocks first (causal), then the
+  //      key splits, kv heads fastest
   const int bid = blockIdx.x;
-  const int rb = p.n_row_blocks - 1 - bid / p.n_heads_wg;
-  int rest = bid % p.n_heads_wg;
-  const int hs = rest % p.n_head_groups;
-  rest /= p.n_head_groups;
-  const int g = rest % p.H_kv;
-  const int b = rest / p.H_kv;
-  const int hh = wave % HW;
-  const int rsub = wave / HW;
-  const int h = g * p.G + hs * HW + hh;
-  const int R0 = rb * BM;
-  const int wr0 = R0 + rsub * C::QW;  // first query row of this wave
-  const int N = p.N;
+  const int head_wg = bid % p.n_heads_wg;
+  const int rest = bid / p.n_heads_wg;
+  const int split = SPLIT ? rest % p.n_splits : 0;
+  const int pb = p.n_pair_blocks - 1 - (SPLIT ? rest / p.n_splits : rest);
+  const int g = head_wg % p.H_kv;
+  const int b = head_wg / p.H_kv;
+  const int G = p.G;
+  const int last_pair = p.n_pairs - 1;
+  const int P0 = pb * PPW;            // first pair of the workgroup
+  const int wp0 = P0 + wave * C::QW;  // first pair of this wave
+  const int wave_row0 = min(wp0, last_pair) / G;
+  const int wg_row_end = min(P0 + PPW - 1, last_pair) / G + 1;
+  const int N_kv = p.N_kv;
+  const int off = p.causal_off;
 
-  const int kv_end = p.causal ? min(R0 + BM, N) : N;
-  const int n_tiles = (kv_end + BN - 1) / BN;
+  // key tiles of this workgroup: [0, kv_end) of the kv head, of which the
+  // split takes a contiguous range of n_tiles tiles starting at key kbase
+  const int kv_end = p.causal ? min(wg_row_end + off, N_kv) : N_kv;
+  int n_tiles = (kv_end + BN - 1) / BN;
+  int kbase = 0;
+  if constexpr (SPLIT) {
+    const int per = (n_tiles + p.n_splits - 1) / p.n_splits;
+    const int t0 = min(split * per, n_tiles);
+    n_tiles = min(per, n_tiles - t0);
+    kbase = t0 * BN;
+  }
 
-  const size_t kv_base = ((size_t)b * p.H_kv + g) * (size_t)N * D;
-  const size_t q_base = ((size_t)b * p.H_q + h) * (size_t)N * D;
+  const size_t kv_base = ((size_t)b * p.H_kv + g) * (size_t)N_kv * D;
   // K and V of this kv head as buffer resources (base in SGPRs, 32-bit offsets)
-  const uint32_t head_bytes = (uint32_t)N * C::ROW_BYTES;
+  const uint32_t head_bytes = (uint32_t)N_kv * C::ROW_BYTES;
   const u32x4 k_rsrc = make_rsrc(p.k + kv_base, head_bytes);
   const u32x4 v_rsrc = make_rsrc(p.v + kv_base, head_bytes);
 
   // ---- query fragments (B operands of S^T = K Q^T): in query block qb the
-  //      lane holds query wr0 + 32 qb + col, d = 16*ks + 8*half .. +8.  Rows
-  //      past the end are clamped.
+  //      lane holds pair wp0 + 32 qb + col = (row, head g*G + j), d = 16*ks +
+  //      8*half .. +8.  Pairs past the end are clamped to the last one.
   int my_row[QB];
+  bool my_valid[QB];
+  size_t my_bhr[QB];  // (b * H_q + h) * N_q + row
   bf16x8 qf[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    my_row[qb] = wr0 + 32 * qb + col;
-    const int q_row = min(my_row[qb], N - 1);
+    const int pair = wp0 + 32 * qb + col;
+    my_valid[qb] = pair <= last_pair;
+    const int pc = min(pair, last_pair);
+    my_row[qb] = pc / G;
+    const int h = g * G + (pc - my_row[qb] * G);
+    my_bhr[qb] = ((size_t)b * p.H_q + h) * (size_t)p.N_q + my_row[qb];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(p.q + q_base + (size_t)q_row * D + ks * 16 + half * 8);
+      u32x4 x = *reinterpret_cast<const u32x4*>(p.q + my_bhr[qb] * D + ks * 16 + half * 8);
       x ^= p.q_sign;
       qf[qb][ks] = as_bf16x8(x);
     }
@@ -236,16 +268,16 @@ void attn_fwd_kernel(FwdParams p) {
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
   const int ld_row_in = lane / C::DC;
   const int ld_chunk = lane % C::DC;
-  // one tile of K (ring 0) or V (ring 1) into ring slot `slot`; rows past the
-  // end of the sequence are clamped to the last row
+  // one tile of K (ring 0) or V (ring 1) into ring slot `slot`; tile numbers
+  // count from the split's first key; keys past the end are clamped to the last
   auto issue_tile = [&](int tile, int slot, const u32x4& rsrc, int ring) {
 #pragma unroll
     for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
       const int li = wave * C::LOADS_PER_WAVE + i;
       const int r = li * C::ROWS_PER_LOAD + ld_row_in;
       const int swz = ring == 0 ? k_swz<D>(r) : v_swz<D>(r);
-      const int off = min(tile * BN + r, N - 1) * C::ROW_BYTES + ((ld_chunk ^ swz) << 4);
-      dma_16B(rsrc, off, lds_base + (ring * P + slot) * C::TILE_BYTES + li * 1024);
+      const int byte = min(kbase + tile * BN + r, N_kv - 1) * C::ROW_BYTES + ((ld_chunk ^ swz) << 4);
+      dma_16B(rsrc, byte, lds_base + (ring * P + slot) * C::TILE_BYTES + li * 1024);
     }
   };
 
@@ -316,16 +348,17 @@ void attn_fwd_kernel(FwdParams p) {
         s[c][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx[i % (PF + 1)]), qf[qb][ks], s[c][qb], 0, 0, 0);
     }
   };
-  // diagonal or ragged tile: element (c, r) holds key tile*BN + 4 half +
-  // [c*32 + 8(r/4) + r%4]; it is visible when the bracket is below lim
+  // diagonal or ragged tile: element (c, r) holds key kbase + tile*BN +
+  // 4 half + [c*32 + 8(r/4) + r%4]; it is visible when the bracket is below
+  // lim.  Rows grow with the pair index, so the wave's first row decides.
   auto needs_mask = [&](int tile) {
-    const int key0 = tile * BN;
-    return (p.causal && key0 + BN - 1 > wr0) || key0 + BN > N;
+    const int key0 = kbase + tile * BN;
+    return (p.causal && key0 + BN - 1 > wave_row0 + off) || key0 + BN > N_kv;
   };
   auto apply_mask = [&](int tile, Scores& s) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const int lim = (p.causal ? min(my_row[qb] + 1, N) : N) - tile * BN - 4 * half;
+      const int lim = (p.causal ? min(my_row[qb] + off + 1, N_kv) : N_kv) - kbase - tile * BN - 4 * half;
 #pragma unroll
       for (int c = 0; c < BN / 32; ++c)
 #pragma unroll
@@ -495,13 +528,17 @@ void attn_fwd_kernel(FwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may outlive the workgroup
   }
 
-  // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log
+  // ---- epilogue.  Single pass: O = acc / l (bf16, round to nearest even),
+  //      LSE in natural log.  Split pass: fp32 O = acc / l and log2-unit
+  //      m + log2 l of this key range; a range with no visible key (l = 0)
+  //      gives O = 0 and -inf, the neutral element of the merge.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = half_swap_sum(l_run[qb]);
-    const float inv = 1.f / l_tot;
-    if (my_row[qb] < N) {
-      uint16_t* orow = p.o + q_base + (size_t)my_row[qb] * D;
+    if (!my_valid[qb]) continue;
+    if constexpr (!SPLIT) {
+      const float inv = 1.f / l_tot;
+      uint16_t* orow = p.o + my_bhr[qb] * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -512,10 +549,64 @@ void attn_fwd_kernel(FwdParams p) {
           const bf16x4 bv = __builtin_convertvector(f, bf16x4);
           *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, bv);
         }
-      if (half == 0)
-        p.lse[((size_t)b * p.H_q + h) * (size_t)N + my_row[qb]] = (m_used[qb] + __log2f(l_tot)) * kLn2;
+      if (half == 0) p.lse[my_bhr[qb]] = (m_used[qb] + __log2f(l_tot)) * kLn2;
+    } else {
+      const bool seen = l_tot > 0.f;
+      const float inv = seen ? 1.f / l_tot : 0.f;
+      const size_t slot = (size_t)split * ((size_t)p.B * p.H_q * p.N_q) + my_bhr[qb];
+      float* orow = p.o_part + slot * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * half;
+          f32x4 f = {acc[db][qb][4 * g4 + 0] * inv, acc[db][qb][4 * g4 + 1] * inv,
+                     acc[db][qb][4 * g4 + 2] * inv, acc[db][qb][4 * g4 + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + d0) = f;
+        }
+      if (half == 0) p.lse_part[slot] = seen ? m_used[qb] + __log2f(l_tot) : -INFINITY;
     }
   }
+}
+
+// Merge of the split pass (page "Attention Kernel 实现与正确性验证", section
+// 2.4: the split-T partial results combined by a safe softmax over their
+// log-sum-exps).  Per (b, h, row), with L_s the log2-unit partial LSEs:
+//   M = max_s L_s,  w_s = 2^(L_s - M),  O = sum_s w_s O_s / sum_s w_s,
+//   LSE = (M + log2 sum_s w_s) ln 2.
+// One thread handles 4 consecutive d of one row: D/4 threads per row.
+struct MergeParams {
+  const float* o_part;    // [n_splits, rows, D]
+  const float* lse_part;  // [n_splits, rows]
+  uint16_t* o;            // [rows, D] bf16
+  float* lse;             // [rows]
+  int64_t rows;           // B * H_q * N_q
+  int n_splits;
+};
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void attn_merge_kernel(MergeParams p) {
+  constexpr int TPR = D / 4;  // threads per row
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int d0 = 4 * (threadIdx.x % TPR);
+  if (row >= p.rows) return;
+  const size_t stride = (size_t)p.rows;
+  float M = -INFINITY;
+  for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, p.lse_part[s * stride + row]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < p.n_splits; ++s) {
+      const float w = __builtin_amdgcn_exp2f(p.lse_part[s * stride + row] - M);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p.o_part + (s * stride + row) * D + d0);
+      wsum += w;
+      acc += w * x;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const bf16x4 bv = __builtin_convertvector(acc * inv, bf16x4);
+  *reinterpret_cast<u32x2*>(p.o + (size_t)row * D + d0) = __builtin_bit_cast(u32x2, bv);
+  if (d0 == 0) p.lse[row] = wsum > 0.f ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 }  // namespace ea02

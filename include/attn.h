@@ -14,17 +14,22 @@
  *
  * Link with libea02_attn.so.  All functions are thread-safe; the library
  * keeps no state between calls and never allocates device memory.
+ * Kernel shapes (not part of the contract): kv heads with more than 64
+ * (query row, query head) pairs run on eight-wave workgroups with 64-key
+ * tiles, smaller ones (decode) on one-wave workgroups with 32-key tiles.
  */
 #ifndef EA02_ATTN_H
 #define EA02_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-/* Status codes.  0 is success; every other value names the first failed check. */
+/* Status codes.  0 is success; every other value names the first failed check
+ * (the order of the checks is given with each function). */
 enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NEGATIVE_SIZE = 1,  /* B, H_q, H_kv, N or D below zero              */
@@ -32,11 +37,17 @@ enum attn_status {
   ATTN_ERR_HEAD_DIM = 3,       /* D is neither 64 nor 128                      */
   ATTN_ERR_CAUSAL_FLAG = 4,    /* is_causal is neither 0 nor 1                 */
   ATTN_ERR_SCALE = 5,          /* sm_scale is NaN or infinite                  */
-  ATTN_ERR_SIZE_OVERFLOW = 6,  /* N > 2^24 or the launch grid exceeds 2^31-1   */
+  ATTN_ERR_SIZE_OVERFLOW = 6,  /* N > 2^24, N*D*2 > 2^31 (one kv head's K rows
+                                  take 32-bit byte offsets), B*H_q*N >= 2^31,
+                                  or the launch grid exceeds 2^31-1           */
   ATTN_ERR_NULL_POINTER = 7,   /* a buffer pointer is NULL for non-empty work  */
   ATTN_ERR_ALIGNMENT = 8,      /* q,k,v,out not 16-byte or lse not 4-byte aligned */
   ATTN_ERR_ALIAS = 9,          /* out or lse overlaps an input or each other   */
-  ATTN_ERR_LAUNCH = 10         /* the HIP runtime rejected the kernel launch   */
+  ATTN_ERR_LAUNCH = 10,        /* the HIP runtime rejected the kernel launch   */
+  ATTN_ERR_CAUSAL_SHAPE = 11,  /* is_causal with more query rows than keys     */
+  ATTN_ERR_NO_KEYS = 12,       /* N_kv = 0 while there are query rows          */
+  ATTN_ERR_SPLITS = 13,        /* n_splits above 256                           */
+  ATTN_ERR_WORKSPACE = 14      /* split workspace NULL, too small or misaligned */
 };
 
 /*
@@ -67,8 +78,8 @@ enum attn_status {
  * Synchronisation: the call only enqueues work; results are visible to later
  * work on the same stream.  It never synchronises.
  *
- * Errors: the arguments are checked in the order of enum attn_status; on a
- * failed check nothing is enqueued and nothing is written.  Empty work
+ * Errors: the arguments are checked in the order of enum attn_status up to
+ * ATTN_ERR_LAUNCH; on a failed check nothing is enqueued and nothing is written.  Empty work
  * (B, H_q or N equal to 0) returns ATTN_OK without touching any pointer.
  * No exception crosses the ABI and the library never aborts.
  */
@@ -76,10 +87,76 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int64_t B, int64_t H_q, int64_t H_kv, int64_t N, int64_t D,
              float sm_scale, int is_causal, void* stream);
 
+/*
+ * attn_fwd_splitkv -- the same forward for N_q query rows against N_kv keys,
+ * optionally with the key axis split into n_splits ranges that are computed
+ * in parallel and merged (decode: N_q = 1).
+ *
+ * Method: page "Attention Kernel 实现与正确性验证", section 2.4 (FlashMLA
+ * decode v2, split-T): a partial kernel per (batch, head block, key split)
+ * followed by a safe-softmax merge.  For key splits K_1..K_S of the visible
+ * keys, with O_s and LSE_s the attention output and log-sum-exp over K_s
+ * alone,
+ *   LSE = log sum_s exp(LSE_s),   out = sum_s exp(LSE_s - LSE) * O_s,
+ * which is exactly attention over all visible keys.  The partials are fp32.
+ *
+ * Semantics as attn_fwd, with i in [0, N_q), j in [0, N_kv), and under
+ * is_causal the mask aligned to the bottom-right corner: query row i sees keys
+ * j <= i + (N_kv - N_q), so the last query row sees every key (for N_q = N_kv
+ * this is attn_fwd's square mask; for N_q = 1 a causal and a non-causal call
+ * agree).  This alignment is a reading: the pages only treat N_q = N_kv.
+ *
+ * Arguments (as attn_fwd, except)
+ *   q, out   [B, H_q, N_q, D];  k, v  [B, H_kv, N_kv, D];  lse  [B, H_q, N_q]
+ *   n_splits 0 = the library's choice (attn_splitkv_num_splits), 1 = one pass
+ *            with no workspace and no merge, 2..256 = that many key ranges
+ *            (a range may be empty when it exceeds a workgroup's key tiles)
+ *   workspace, workspace_size  device scratch of at least
+ *            attn_splitkv_workspace_size(B, H_q, N_q, D, n_splits') bytes,
+ *            16-byte aligned, where n_splits' is the split count actually used;
+ *            unused (may be NULL) when that count is 1.  Its contents are
+ *            undefined on entry and after the call; calls that overlap on the
+ *            same workspace race.
+ *
+ * Ownership: the caller allocates out, lse and the workspace; the library
+ * allocates nothing.  Synchronisation as attn_fwd: two kernels are enqueued
+ * on `stream` when n_splits' > 1, one otherwise.
+ *
+ * Errors, checked in this order; nothing is enqueued on failure:
+ *   NEGATIVE_SIZE (any size or n_splits < 0), HEAD_RATIO, HEAD_DIM,
+ *   CAUSAL_FLAG, SCALE, SPLITS (n_splits > 256), CAUSAL_SHAPE (is_causal and
+ *   N_q > N_kv), SIZE_OVERFLOW (N_q or N_kv > 2^24, N_kv * D * 2 > 2^31,
+ *   B * H_q * N_q >= 2^31, N_q * H_q / H_kv > 2^30, grid >= 2^31), then empty work (B, H_q or N_q = 0) returns ATTN_OK, then
+ *   NO_KEYS (N_kv = 0), NULL_POINTER, ALIGNMENT, WORKSPACE, ALIAS (out, lse
+ *   or the used workspace overlapping an input or each other), LAUNCH.
+ */
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t D,
+                     float sm_scale, int is_causal, int64_t n_splits, void* workspace,
+                     size_t workspace_size, void* stream);
+
+/*
+ * attn_splitkv_num_splits -- the split count attn_fwd_splitkv uses for
+ * n_splits = 0 on the current device: 1 when the unsplit launch already has
+ * about one workgroup per CU slot, otherwise enough splits for about two, with
+ * at least eight key tiles per split and at most 256.  Returns -1 when the
+ * sizes fail attn_fwd_splitkv's size checks (NEGATIVE_SIZE .. SIZE_OVERFLOW).
+ * Queries the current device's CU count; enqueues nothing.
+ */
+int64_t attn_splitkv_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv,
+                                int64_t D, int is_causal);
+
+/*
+ * attn_splitkv_workspace_size -- bytes of workspace for n_splits key ranges:
+ * 0 when n_splits <= 1, else n_splits * B * H_q * N_q * (D + 1) * 4 (fp32
+ * partial outputs, then fp32 partial log-sum-exps).  0 for invalid sizes.
+ */
+size_t attn_splitkv_workspace_size(int64_t B, int64_t H_q, int64_t N_q, int64_t D, int64_t n_splits);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);
 
-/* Library ABI version, currently 1. */
+/* Library ABI version, currently 2 (1 had attn_fwd only). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

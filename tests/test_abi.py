@@ -38,7 +38,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
 
 
 def test_status_strings_distinct(lib):
@@ -70,6 +70,8 @@ def call(lib, q=Q, k=K, v=V, o=O, l=L, B=1, H_q=4, H_kv=2, N=16, D=64, scale=0.1
     (dict(scale=float("nan")), "ATTN_ERR_SCALE"),
     (dict(scale=float("inf")), "ATTN_ERR_SCALE"),
     (dict(N=(1 << 24) + 1), "ATTN_ERR_SIZE_OVERFLOW"),
+    (dict(N=(1 << 23) + 1, D=128), "ATTN_ERR_SIZE_OVERFLOW"),
+    (dict(B=1 << 15, H_q=1 << 12, H_kv=1 << 12, N=1 << 4), "ATTN_ERR_SIZE_OVERFLOW"),
     (dict(q=0), "ATTN_ERR_NULL_POINTER"),
     (dict(l=0), "ATTN_ERR_NULL_POINTER"),
     (dict(k=K + 8), "ATTN_ERR_ALIGNMENT"),
@@ -93,6 +95,84 @@ def test_checks_run_in_declared_order(lib):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(H_q=0, H_kv=1)])
 def test_empty_work_is_success_without_pointers(lib, kw):
     assert call(lib, q=0, k=0, v=0, o=0, l=0, **kw) == STATUS["ATTN_OK"]
+
+
+# ------------------------------------------------------------ split-KV entry
+W = 0x100000000 + 5 * 64 * MiB   # fake workspace address
+
+
+def call_split(lib, q=Q, k=K, v=V, o=O, l=L, B=1, H_q=4, H_kv=2, N_q=16, N_kv=40, D=64,
+               scale=0.125, causal=0, n_splits=4, ws=W, ws_bytes=64 * MiB):
+    return lib.attn_fwd_splitkv(q, k, v, o, l, B, H_q, H_kv, N_q, N_kv, D, ctypes.c_float(scale),
+                                causal, n_splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N_q=-1), "ATTN_ERR_NEGATIVE_SIZE"),
+    (dict(N_kv=-1), "ATTN_ERR_NEGATIVE_SIZE"),
+    (dict(n_splits=-1), "ATTN_ERR_NEGATIVE_SIZE"),
+    (dict(H_q=6, H_kv=4), "ATTN_ERR_HEAD_RATIO"),
+    (dict(D=32), "ATTN_ERR_HEAD_DIM"),
+    (dict(causal=3), "ATTN_ERR_CAUSAL_FLAG"),
+    (dict(scale=float("-inf")), "ATTN_ERR_SCALE"),
+    (dict(n_splits=257), "ATTN_ERR_SPLITS"),
+    (dict(causal=1, N_q=41, N_kv=40), "ATTN_ERR_CAUSAL_SHAPE"),
+    (dict(N_kv=(1 << 24) + 1), "ATTN_ERR_SIZE_OVERFLOW"),
+    (dict(N_q=(1 << 24), H_q=128, H_kv=1), "ATTN_ERR_SIZE_OVERFLOW"),
+    (dict(N_kv=0), "ATTN_ERR_NO_KEYS"),
+    (dict(v=0), "ATTN_ERR_NULL_POINTER"),
+    (dict(q=Q + 4), "ATTN_ERR_ALIGNMENT"),
+    (dict(ws=0), "ATTN_ERR_WORKSPACE"),
+    (dict(ws=W + 8), "ATTN_ERR_WORKSPACE"),
+    (dict(ws_bytes=100), "ATTN_ERR_WORKSPACE"),
+    (dict(ws=Q + 64 * MiB - 256), "ATTN_ERR_ALIAS"),
+    (dict(ws=O - 1024, ws_bytes=64 * MiB), "ATTN_ERR_ALIAS"),
+    (dict(l=V + 32), "ATTN_ERR_ALIAS"),
+])
+def test_splitkv_invalid_arguments_rejected(lib, kw, code):
+    assert call_split(lib, **kw) == STATUS[code]
+
+
+def test_splitkv_check_order(lib):
+    assert call_split(lib, n_splits=300, D=80) == STATUS["ATTN_ERR_HEAD_DIM"]
+    assert call_split(lib, n_splits=300, causal=1, N_q=50) == STATUS["ATTN_ERR_SPLITS"]
+    assert call_split(lib, q=0, N_kv=0) == STATUS["ATTN_ERR_NO_KEYS"]
+    assert call_split(lib, q=0, ws=0) == STATUS["ATTN_ERR_NULL_POINTER"]
+    assert call_split(lib, ws=0, l=Q) == STATUS["ATTN_ERR_WORKSPACE"]
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N_q=0), dict(N_q=0, N_kv=0), dict(B=0, N_kv=0)])
+def test_splitkv_empty_work_is_success_without_pointers(lib, kw):
+    assert call_split(lib, q=0, k=0, v=0, o=0, l=0, ws=0, **kw) == STATUS["ATTN_OK"]
+
+
+def test_splitkv_single_pass_needs_no_workspace(lib):
+    # with one split there is no workspace: its absence is no error, and the
+    # call only fails later, at a check of real arguments
+    assert call_split(lib, n_splits=1, ws=0, ws_bytes=0, o=Q) == STATUS["ATTN_ERR_ALIAS"]
+
+
+def test_workspace_size_formula():
+    for (B, H_q, N_q, D, ns) in [(1, 32, 1, 128, 16), (2, 8, 100, 64, 3), (1, 1, 1, 64, 256)]:
+        assert ea.attn_splitkv_workspace_size(B, H_q, N_q, D, ns) == ns * B * H_q * N_q * (D + 1) * 4
+    assert ea.attn_splitkv_workspace_size(1, 32, 1, 128, 1) == 0
+    assert ea.attn_splitkv_workspace_size(1, 32, 1, 128, 0) == 0
+    assert ea.attn_splitkv_workspace_size(1, 32, 1, 128, 257) == 0
+    assert ea.attn_splitkv_workspace_size(-1, 32, 1, 128, 4) == 0
+
+
+def test_num_splits_choice():
+    # the unsplit launch already fills the device: one pass
+    assert ea.attn_splitkv_num_splits(1, 32, 8, 32768, 32768, 128, True) == 1
+    # decode over a long cache: several splits, each with enough key tiles
+    n = ea.attn_splitkv_num_splits(1, 32, 32, 1, 65536, 128, False)
+    assert 2 <= n <= 256
+    assert 65536 // 32 // n >= 8
+    # too few keys to split
+    assert ea.attn_splitkv_num_splits(1, 32, 32, 1, 100, 128, False) == 1
+    assert ea.attn_splitkv_num_splits(1, 32, 32, 0, 100, 128, False) == 1
+    assert ea.attn_splitkv_num_splits(1, 32, 32, 1, 100, 96, False) == -1
+    assert ea.attn_splitkv_num_splits(1, 4, 4, 20, 10, 64, True) == -1
 
 
 def test_binding_rejects_cpu_tensors():

@@ -1,0 +1,257 @@
+"""GPU parity of the split-KV forward (N_q != N_kv, key splits, decode) against
+the float64 CPU oracle.
+
+Cases run attn_fwd_splitkv through the C ABI on seeded bf16 inputs and compare
+element by element with the oracle's attention (bottom-right causal alignment
+for N_q < N_kv) under the same tolerances as the single-pass forward:
+|O - O_ref| <= 2e-2 + 2e-2 |O_ref|, |LSE - LSE_ref| <= 1e-3, nothing non-finite.
+The split count is varied explicitly (1, 2, 3, 7, more splits than key tiles,
+the library's own choice) so that empty splits and the merge of partial
+results are exercised; decode covers the softmax-decode shape B=1, H=32,
+D=128 of the page "Attention Kernel 实现与正确性验证", section 3.5.1.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+O_ATOL = 2e-2
+O_RTOL = 2e-2
+LSE_ATOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def ea():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_02_amd as m
+    m.load_library()
+    return m
+
+
+def _dev():
+    return torch.device("cuda", 0)
+
+
+def _run_split(ea, q, k, v, causal, scale, n_splits, poison=True):
+    dev = _dev()
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    B, H_q, N_q, D = q.shape
+    H_kv, N_kv = k.shape[1], k.shape[2]
+    out = torch.empty((B, H_q, N_q, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H_q, N_q), dtype=torch.float32, device=dev)
+    ns = n_splits if n_splits > 0 else ea.attn_splitkv_num_splits(B, H_q, H_kv, N_q, N_kv, D,
+                                                                  causal)
+    ws = None
+    nbytes = ea.attn_splitkv_workspace_size(B, H_q, N_q, D, ns)
+    if nbytes:
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+        if poison:
+            ws.fill_(0xFF)          # NaN in every fp32 slot: unwritten partials would show
+    if poison:
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    ea.attn_fwd_splitkv(qd, kd, vd, out, lse, is_causal=causal, sm_scale=scale,
+                        n_splits=n_splits, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def _check(o_gpu, l_gpu, O_ref, L_ref, what=""):
+    o = o_gpu.to(torch.float64).numpy()
+    l = l_gpu.to(torch.float64).numpy()
+    assert np.all(np.isfinite(o)), f"{what}: non-finite O"
+    assert np.all(np.isfinite(l)), f"{what}: non-finite LSE"
+    err_o = np.abs(o - O_ref)
+    bad = err_o > O_ATOL + O_RTOL * np.abs(O_ref)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} O elements out of tolerance; "
+                           f"max abs err {err_o.max():.3e}")
+    err_l = np.abs(l - L_ref)
+    assert err_l.max(initial=0.0) <= LSE_ATOL, f"{what}: max LSE err {err_l.max():.3e}"
+
+
+def _case(ea, B, H_q, H_kv, N_q, N_kv, D, causal, seed, n_splits, scale=None):
+    q, k, v = workloads.make_inputs(B, H_q, H_kv, N_q, D, seed, N_kv=N_kv)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    o, l = _run_split(ea, q, k, v, causal, scale, n_splits)
+    O_ref, L_ref = oracle.attention_forward(workloads.to_float64(q), workloads.to_float64(k),
+                                            workloads.to_float64(v), is_causal=causal,
+                                            sm_scale=scale)
+    _check(o, l, O_ref, L_ref,
+           what=f"B{B} Hq{H_q} Hkv{H_kv} Nq{N_q} Nkv{N_kv} D{D} c{int(causal)} s{n_splits}")
+
+
+# ------------------------------------------------------------ split counts
+@pytest.mark.parametrize("n_splits", [1, 2, 3, 7, 40, 0])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_counts_square(ea, n_splits, causal, D):
+    """N_q = N_kv = 300 over 5 key tiles of 64: 40 splits leave most ranges empty."""
+    _case(ea, 1, 8, 2, 300, 300, D, causal, seed=8100 + D, n_splits=n_splits)
+
+
+@pytest.mark.parametrize("n_splits", [1, 2, 5, 0])
+def test_split_causal_long_rows(ea, n_splits):
+    """Causal with splits over a workgroup's range: later splits lie past the
+    diagonal of the workgroup's first rows, whose partials are empty."""
+    _case(ea, 1, 4, 1, 700, 700, 128, True, seed=8200, n_splits=n_splits)
+
+
+def test_single_split_equals_attn_fwd(ea):
+    """n_splits = 1 is the single pass: bit-identical to attn_fwd."""
+    dev = _dev()
+    for (H_q, H_kv, N, D) in [(8, 2, 333, 128), (4, 4, 40, 64), (32, 8, 1, 128)]:
+        q, k, v = workloads.make_inputs(1, H_q, H_kv, N, D, seed=8300 + N)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        for causal in (False, True):
+            o1, l1 = ea.fwd(qd, kd, vd, is_causal=causal)
+            o2, l2 = ea.fwd_splitkv(qd, kd, vd, is_causal=causal, n_splits=1)
+            torch.cuda.synchronize()
+            assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+            assert torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------ N_q != N_kv
+@pytest.mark.parametrize("N_q,N_kv", [(1, 1), (1, 63), (1, 64), (1, 65), (5, 33), (17, 300),
+                                      (100, 1000), (257, 513), (64, 4096)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n_splits", [1, 3, 0])
+def test_rectangular(ea, N_q, N_kv, causal, n_splits):
+    _case(ea, 1, 8, 2, N_q, N_kv, 128, causal, seed=8400 + N_q + N_kv, n_splits=n_splits)
+
+
+@pytest.mark.parametrize("N_q,N_kv", [(300, 100), (64, 1)])
+@pytest.mark.parametrize("n_splits", [1, 4])
+def test_more_queries_than_keys_non_causal(ea, N_q, N_kv, n_splits):
+    _case(ea, 2, 4, 2, N_q, N_kv, 64, False, seed=8500 + N_q, n_splits=n_splits)
+
+
+@pytest.mark.parametrize("H_q,H_kv,N_q", [(12, 4, 7), (6, 1, 9), (32, 1, 1), (32, 1, 2),
+                                          (8, 1, 8), (8, 1, 5), (64, 8, 3), (3, 3, 40)])
+def test_pair_packing(ea, H_q, H_kv, N_q):
+    """(row, head) pairs per kv head around the one-wave limit of 64 and groups
+    that do not divide 32."""
+    for causal, ns in ((False, 0), (True, 0), (True, 3)):
+        _case(ea, 2, H_q, H_kv, N_q, 257, 128, causal, seed=8600 + H_q + N_q, n_splits=ns)
+
+
+# ------------------------------------------------------------ decode
+@pytest.mark.parametrize("name", ["decode_mha_n4096", "decode_mha_n16384", "decode_mha_n65536",
+                                  "decode_gqa4_n65536"])
+def test_decode_workloads_full(ea, name):
+    """Every head of the decode workloads, with the library's split choice."""
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.workload_inputs(w)
+    o, l = _run_split(ea, q, k, v, w.causal, w.sm_scale, 0)
+    O_ref, L_ref = oracle.attention_forward(workloads.to_float64(q), workloads.to_float64(k),
+                                            workloads.to_float64(v), is_causal=w.causal,
+                                            sm_scale=w.sm_scale)
+    _check(o, l, O_ref, L_ref, what=name)
+
+
+@pytest.mark.parametrize("n_splits", [1, 2, 16, 256])
+def test_decode_split_counts(ea, n_splits):
+    _case(ea, 2, 16, 4, 1, 5000, 128, True, seed=8700, n_splits=n_splits)
+
+
+def test_chunk_prefill_sampled(ea):
+    """A 512-row chunk against an 8192-key cache at the full shape; sampled rows."""
+    w = workloads.WORKLOADS["chunk_gqa4_q512_n8192"]
+    q, k, v = workloads.workload_inputs(w)
+    q64, k64, v64 = (workloads.to_float64(t) for t in (q, k, v))
+    rng = np.random.default_rng(w.seed)
+    for n_splits in (0, 4):
+        o, l = _run_split(ea, q, k, v, w.causal, w.sm_scale, n_splits)
+        for h in (0, 13, 31):
+            rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 510, 511],
+                                             rng.choice(w.Nq, 8, replace=False)]))
+            O_ref, L_ref = oracle.attention_rows(q64, k64, v64, 0, h, rows, is_causal=True,
+                                                 sm_scale=w.sm_scale)
+            _check(o[0, h, rows], l[0, h, rows], O_ref, L_ref, what=f"chunk h{h} s{n_splits}")
+
+
+# ------------------------------------------------------------ values
+@pytest.mark.parametrize("scale", [0.0, -0.09, 2.0])
+def test_split_scale_values(ea, scale):
+    _case(ea, 1, 4, 1, 3, 900, 128, True, seed=8800, n_splits=6, scale=scale)
+
+
+def test_split_growing_scores(ea):
+    """Keys with growing norm: the running max rises inside every split, and the
+    splits' maxima differ widely, so the merge weights span many octaves."""
+    q, k, v = workloads.make_inputs(1, 4, 2, 2, 128, seed=8900, N_kv=3000)
+    k = (k.float() * torch.linspace(0.1, 4.0, 3000).view(1, 1, -1, 1)).to(torch.bfloat16)
+    O_ref, L_ref = oracle.attention_forward(workloads.to_float64(q), workloads.to_float64(k),
+                                            workloads.to_float64(v), is_causal=True,
+                                            sm_scale=0.125)
+    for ns in (1, 5, 0):
+        o, l = _run_split(ea, q, k, v, True, 0.125, ns)
+        _check(o, l, O_ref, L_ref, what=f"ramp s{ns}")
+
+
+# ------------------------------------------------------------ hygiene
+def test_split_deterministic_and_no_overrun(ea):
+    dev = _dev()
+    q, k, v = workloads.make_inputs(1, 8, 2, 3, 128, seed=9000, N_kv=2000)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    ns = 5
+    need = ea.attn_splitkv_workspace_size(1, 8, 3, 128, ns)
+    res = []
+    for _ in range(2):
+        ob = torch.full((q.numel() + 4096,), 7.0, dtype=torch.bfloat16, device=dev)
+        lb = torch.full((24 + 1024,), 7.0, dtype=torch.float32, device=dev)
+        wb = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device=dev)
+        out = ob[:q.numel()].view(q.shape)
+        lse = lb[:24].view(1, 8, 3)
+        ea.attn_fwd_splitkv(qd, kd, vd, out, lse, is_causal=True, n_splits=ns, workspace=wb[:need])
+        torch.cuda.synchronize()
+        assert torch.all(ob[q.numel():] == 7.0) and torch.all(lb[24:] == 7.0), "overrun"
+        assert torch.all(wb[need:] == 0x5A), "workspace overrun"
+        res.append((out.clone(), lse.clone()))
+    assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
+    assert torch.equal(res[0][1], res[1][1])
+
+
+def test_workspace_reused_for_smaller_problem(ea):
+    """One workspace serves a large call then a smaller one; the second result
+    does not depend on what the first left behind."""
+    dev = _dev()
+    big = workloads.make_inputs(1, 8, 2, 4, 128, seed=9100, N_kv=4000)
+    small = workloads.make_inputs(1, 4, 1, 2, 128, seed=9101, N_kv=700)
+    need = ea.attn_splitkv_workspace_size(1, 8, 4, 128, 8)
+    ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+    results = []
+    for (q, k, v) in (big, small):
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        ea.attn_fwd_splitkv(qd, kd, vd, out, lse, is_causal=True, n_splits=8, workspace=ws)
+        torch.cuda.synchronize()
+        results.append((q, k, v, out.cpu(), lse.cpu()))
+    for (q, k, v, o, l) in results:
+        O_ref, L_ref = oracle.attention_forward(workloads.to_float64(q), workloads.to_float64(k),
+                                                workloads.to_float64(v), is_causal=True,
+                                                sm_scale=1 / math.sqrt(128))
+        _check(o, l, O_ref, L_ref, what="ws reuse")
+
+
+def test_split_errors_raise(ea):
+    dev = _dev()
+    q = torch.zeros((1, 4, 8, 128), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((1, 4, 4, 128), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ea.AttnError) as e:
+        ea.fwd_splitkv(q, k, k, is_causal=True)
+    assert e.value.status == 11
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 4, 8), dtype=torch.float32, device=dev)
+    with pytest.raises(ea.AttnError) as e:
+        ea.attn_fwd_splitkv(q, k, k, out, lse, n_splits=4, workspace=None)
+    assert e.value.status == 14

@@ -23,6 +23,8 @@ import torch
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
+    """N is the key count; N_q (default N) the query rows.  N_q < N is a
+    prefill chunk against a KV cache, N_q = 1 a decode step."""
     name: str
     B: int
     H_q: int
@@ -31,27 +33,35 @@ class Workload:
     D: int
     causal: bool
     seed: int
+    N_q: int | None = None
+
+    @property
+    def Nq(self) -> int:
+        return self.N if self.N_q is None else self.N_q
 
     @property
     def sm_scale(self) -> float:
         return 1.0 / math.sqrt(self.D)
 
     def q_shape(self):
-        return (self.B, self.H_q, self.N, self.D)
+        return (self.B, self.H_q, self.Nq, self.D)
 
     def kv_shape(self):
         return (self.B, self.H_kv, self.N, self.D)
 
     def flops(self) -> float:
-        """Attention FLOPs: two contractions of 2*N*N*D each per (b, h_q), halved when causal."""
-        f = 4.0 * self.B * self.H_q * self.N * self.N * self.D
-        return f / 2 if self.causal else f
+        """Attention FLOPs: two contractions of 2*D per visible (query, key) pair
+        per head.  Causal counts N_q*N - N_q^2/2 pairs (N^2/2 when square)."""
+        pairs = float(self.Nq) * self.N
+        if self.causal:
+            pairs -= float(self.Nq) * self.Nq / 2
+        return 4.0 * self.B * self.H_q * pairs * self.D
 
     def algorithmic_bytes(self) -> int:
         """Q, K, V read once (bf16) plus O (bf16) and LSE (fp32) written once."""
-        qo = self.B * self.H_q * self.N * self.D * 2
+        qo = self.B * self.H_q * self.Nq * self.D * 2
         kv = self.B * self.H_kv * self.N * self.D * 2
-        lse = self.B * self.H_q * self.N * 4
+        lse = self.B * self.H_q * self.Nq * 4
         return 2 * qo + 2 * kv + lse
 
 
@@ -65,6 +75,15 @@ _W = [
     Workload("gqa4_n8192_causal", 1, 32, 8, 8192, 128, True, 508),
     Workload("gqa4_n16384_causal", 1, 32, 8, 16384, 128, True, 516),
     Workload("gqa4_n32768_causal", 1, 32, 8, 32768, 128, True, 532),
+    # one decode step (one query row) against a KV cache: the softmax-decode
+    # shape B=1, H=32, D=128 of the page "Attention Kernel 实现与正确性验证",
+    # section 3.5.1, at its three context lengths, plus a GQA-4 variant
+    Workload("decode_mha_n4096", 1, 32, 32, 4096, 128, True, 601, N_q=1),
+    Workload("decode_mha_n16384", 1, 32, 32, 16384, 128, True, 602, N_q=1),
+    Workload("decode_mha_n65536", 1, 32, 32, 65536, 128, True, 603, N_q=1),
+    Workload("decode_gqa4_n65536", 1, 32, 8, 65536, 128, True, 604, N_q=1),
+    # a 512-row prefill chunk appended to an 8192-key cache (bottom-right causal)
+    Workload("chunk_gqa4_q512_n8192", 1, 32, 8, 8192, 128, True, 605, N_q=512),
 ]
 WORKLOADS = {w.name: w for w in _W}
 
@@ -73,15 +92,16 @@ HEADLINE = "gqa4_n32768_causal"
 
 
 def make_inputs(B: int, H_q: int, H_kv: int, N: int, D: int, seed: int,
-                dist: str = "normal"):
-    """Draw bf16 Q [B,H_q,N,D], K and V [B,H_kv,N,D] on the CPU.
+                dist: str = "normal", N_kv: int | None = None):
+    """Draw bf16 Q [B,H_q,N,D], K and V [B,H_kv,N_kv,D] (N_kv defaults to N) on the CPU.
 
     dist="normal": i.i.d. N(0,1) float32 rounded to bf16 (the workloads' recipe).
     dist="uniform": i.i.d. U(-1,1), used by a few edge-case tests.
     """
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
-    shapes = [(B, H_q, N, D), (B, H_kv, N, D), (B, H_kv, N, D)]
+    nk = N if N_kv is None else N_kv
+    shapes = [(B, H_q, N, D), (B, H_kv, nk, D), (B, H_kv, nk, D)]
     out = []
     for s in shapes:
         if dist == "normal":
@@ -95,7 +115,7 @@ def make_inputs(B: int, H_q: int, H_kv: int, N: int, D: int, seed: int,
 
 
 def workload_inputs(w: Workload):
-    return make_inputs(w.B, w.H_q, w.H_kv, w.N, w.D, w.seed)
+    return make_inputs(w.B, w.H_q, w.H_kv, w.Nq, w.D, w.seed, N_kv=w.N)
 
 
 def to_float64(t: torch.Tensor) -> np.ndarray:
