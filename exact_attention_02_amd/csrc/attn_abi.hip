@@ -18,12 +18,14 @@ using ea02::FwdParams;
 using ea02::MergeParams;
 
 // Kernel shapes.  Wide: eight waves of 32 (row, head) pairs share each K/V
-// tile (256 pairs per workgroup, 64-key tiles, four LDS stages, 128 KiB LDS).
-// Narrow: one wave of 32 pairs (32-key tiles, four stages, 64 KiB LDS, two
-// workgroups per CU) for kv heads with at most kNarrowPairs pairs, e.g. a
-// decode step, where the wide shape would leave most waves without a query.
+// tile (256 pairs per workgroup, 64-key tiles, four LDS stages, 128 KiB LDS,
+// one workgroup per CU).  Narrow: one wave of 32 pairs (32-key tiles, two
+// stages, 32 KiB LDS at D=128) for kv heads with at most kNarrowPairs pairs,
+// e.g. a decode step, where the wide shape would leave most waves without a
+// query; five (D=128) or eight (D=64, register-bound) fit on a CU, which keeps
+// enough loads in flight for such HBM-bound work.
 constexpr int kWideNW = 8, kWideP = 4, kWideBN = 64;
-constexpr int kNarrowNW = 1, kNarrowP = 4, kNarrowBN = 32;
+constexpr int kNarrowNW = 1, kNarrowP = 2, kNarrowBN = 32;
 constexpr int kNarrowPairs = 64;
 constexpr int kMaxSplits = 256;
 
@@ -40,8 +42,8 @@ struct Shape {
   int wg_per_cu;
 };
 
-Shape pick_shape(int64_t n_pairs) {
-  if (n_pairs <= kNarrowPairs) return {true, 32 * kNarrowNW, kNarrowBN, 2};
+Shape pick_shape(int64_t n_pairs, int64_t D) {
+  if (n_pairs <= kNarrowPairs) return {true, 32 * kNarrowNW, kNarrowBN, D == 128 ? 5 : 8};
   return {false, 32 * kWideNW, kWideBN, 1};
 }
 
@@ -56,11 +58,19 @@ hipError_t launch_fwd(bool narrow, const FwdParams& p, int grid, hipStream_t str
   return hipGetLastError();
 }
 
+// One block per output row; the block's split lanes grow with the split count
+// so that each thread merges at most about kMergeBatch splits (blocks of 64,
+// 256 or 1024 threads).
 template <int D>
 hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
-  constexpr int rows_per_block = 256 / (D / 4);
-  const int64_t blocks = (m.rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL((ea02::attn_merge_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, m);
+  constexpr int tpr = D / 4;
+  const dim3 grid(static_cast<unsigned>(m.rows));
+  if (m.n_splits <= ea02::kMergeBatch * (64 / tpr))
+    hipLaunchKernelGGL((ea02::attn_merge_kernel<D, 64>), grid, dim3(64), 0, stream, m);
+  else if (m.n_splits <= ea02::kMergeBatch * (256 / tpr))
+    hipLaunchKernelGGL((ea02::attn_merge_kernel<D, 256>), grid, dim3(256), 0, stream, m);
+  else
+    hipLaunchKernelGGL((ea02::attn_merge_kernel<D, 1024>), grid, dim3(1024), 0, stream, m);
   return hipGetLastError();
 }
 
@@ -93,7 +103,7 @@ int check_sizes(const Problem& a, int64_t n_splits, bool* empty) {
     return ATTN_ERR_SIZE_OVERFLOW;
   const int64_t n_pairs = a.N_q * (a.H_q / a.H_kv);
   if (n_pairs > (int64_t(1) << 30)) return ATTN_ERR_SIZE_OVERFLOW;
-  const Shape sh = pick_shape(n_pairs);
+  const Shape sh = pick_shape(n_pairs, a.D);
   const int64_t grid = ((n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg) * a.B * a.H_kv *
                        (n_splits > 1 ? n_splits : 1);
   if (grid > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
@@ -141,16 +151,16 @@ int device_cus() {
 }
 
 // Number of key splits the library picks: none while the unsplit grid already
-// fills every CU slot; otherwise enough splits for about two workgroups per
-// slot, each split keeping at least 8 key tiles.
+// fills every workgroup slot of the device; otherwise enough splits for about
+// two workgroups per CU, each split keeping at least 8 key tiles.
 int64_t choose_splits(const Problem& a) {
   const int64_t n_pairs = a.N_q * (a.H_q / a.H_kv);
-  const Shape sh = pick_shape(n_pairs);
+  const Shape sh = pick_shape(n_pairs, a.D);
   const int64_t wgs = ((n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg) * a.B * a.H_kv;
-  const int64_t slots = int64_t(device_cus()) * sh.wg_per_cu;
-  if (wgs <= 0 || wgs >= slots) return 1;
+  const int64_t cus = device_cus();
+  if (wgs <= 0 || wgs >= cus * sh.wg_per_cu) return 1;
   const int64_t tiles = (a.N_kv + sh.bn - 1) / sh.bn;
-  int64_t n = (2 * slots + wgs - 1) / wgs;
+  int64_t n = (2 * cus + wgs - 1) / wgs;
   n = std::min<int64_t>(n, tiles / 8);
   n = std::min<int64_t>(n, kMaxSplits);
   return n < 1 ? 1 : n;
@@ -161,7 +171,7 @@ int64_t choose_splits(const Problem& a) {
 int run(const Problem& a, int64_t n_splits, void* ws, void* stream) {
   const int G = static_cast<int>(a.H_q / a.H_kv);
   const int64_t n_pairs = a.N_q * G;
-  const Shape sh = pick_shape(n_pairs);
+  const Shape sh = pick_shape(n_pairs, a.D);
   const int64_t n_pair_blocks = (n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg;
   const bool split = n_splits > 1;
   const int64_t grid = n_pair_blocks * a.B * a.H_kv * (split ? n_splits : 1);

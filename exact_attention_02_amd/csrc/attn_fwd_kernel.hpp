@@ -574,7 +574,12 @@ void attn_fwd_kernel(FwdParams p) {
 // log-sum-exps).  Per (b, h, row), with L_s the log2-unit partial LSEs:
 //   M = max_s L_s,  w_s = 2^(L_s - M),  O = sum_s w_s O_s / sum_s w_s,
 //   LSE = (M + log2 sum_s w_s) ln 2.
-// One thread handles 4 consecutive d of one row: D/4 threads per row.
+// A thread owns 4 consecutive d of one row and every SL-th split ("split
+// lane"); it takes its own max over its splits first, then sums its weighted
+// partial outputs with loads issued four splits at a time, and the SL split
+// lanes of the row are combined through LDS by the same rule.  SL is chosen
+// per launch so that a thread sees at most a few splits: few rows (a decode
+// step) still spread over many threads.
 struct MergeParams {
   const float* o_part;    // [n_splits, rows, D]
   const float* lse_part;  // [n_splits, rows]
@@ -584,29 +589,76 @@ struct MergeParams {
   int n_splits;
 };
 
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void attn_merge_kernel(MergeParams p) {
-  constexpr int TPR = D / 4;  // threads per row
-  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  const int d0 = 4 * (threadIdx.x % TPR);
-  if (row >= p.rows) return;
+constexpr int kMergeBatch = 4;  // splits whose loads a thread issues together
+
+template <int D, int NT>
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT))) void attn_merge_kernel(MergeParams p) {
+  constexpr int TPR = D / 4;  // threads per row and split lane
+  constexpr int SL = NT / TPR;
+  const int t = threadIdx.x;
+  const int c = t % TPR;
+  const int j = t / TPR;
+  const int64_t row = blockIdx.x;
   const size_t stride = (size_t)p.rows;
-  float M = -INFINITY;
-  for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, p.lse_part[s * stride + row]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int n = p.n_splits;
+  const float* lse_r = p.lse_part + row;
+  const float* o_r = p.o_part + (size_t)row * D + 4 * c;
+
+  float m = -INFINITY;
+  for (int s0 = j; s0 < n; s0 += kMergeBatch * SL) {
+    float l[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int s = s0 + u * SL;
+      l[u] = s < n ? lse_r[s * stride] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) m = fmaxf(m, l[u]);
+  }
   float wsum = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < p.n_splits; ++s) {
-      const float w = __builtin_amdgcn_exp2f(p.lse_part[s * stride + row] - M);
-      const f32x4 x = *reinterpret_cast<const f32x4*>(p.o_part + (s * stride + row) * D + d0);
-      wsum += w;
-      acc += w * x;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (m != -INFINITY) {
+    for (int s0 = j; s0 < n; s0 += kMergeBatch * SL) {
+      float l[kMergeBatch];
+      f32x4 x[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int s = min(s0 + u * SL, n - 1);
+        l[u] = s0 + u * SL < n ? lse_r[s * stride] : -INFINITY;
+        x[u] = *reinterpret_cast<const f32x4*>(o_r + s * stride * D);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const float w = __builtin_amdgcn_exp2f(l[u] - m);  // 2^-inf = 0
+        wsum += w;
+        acc += w * x[u];
+      }
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  const bf16x4 bv = __builtin_convertvector(acc * inv, bf16x4);
-  *reinterpret_cast<u32x2*>(p.o + (size_t)row * D + d0) = __builtin_bit_cast(u32x2, bv);
-  if (d0 == 0) p.lse[row] = wsum > 0.f ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
+  __shared__ float st_m[SL][TPR], st_w[SL][TPR];
+  __shared__ f32x4 st_o[SL][TPR];
+  st_m[j][c] = m;
+  st_w[j][c] = wsum;
+  st_o[j][c] = acc;
+  __syncthreads();
+  if (j != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < SL; ++k) M = fmaxf(M, st_m[k][c]);
+  float tot = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
+      const float f = __builtin_amdgcn_exp2f(st_m[k][c] - M);  // a lane with no split has m = -inf
+      tot += f * st_w[k][c];
+      o += f * st_o[k][c];
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const bf16x4 bv = __builtin_convertvector(o * inv, bf16x4);
+  *reinterpret_cast<u32x2*>(p.o + (size_t)row * D + 4 * c) = __builtin_bit_cast(u32x2, bv);
+  if (c == 0) p.lse[row] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace ea02

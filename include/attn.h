@@ -137,9 +137,9 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, flo
 
 /*
  * attn_splitkv_num_splits -- the split count attn_fwd_splitkv uses for
- * n_splits = 0 on the current device: 1 when the unsplit launch already has
- * about one workgroup per CU slot, otherwise enough splits for about two, with
- * at least eight key tiles per split and at most 256.  Returns -1 when the
+ * n_splits = 0 on the current device: 1 when the unsplit launch already fills
+ * every workgroup slot, otherwise enough splits for about two workgroups per
+ * CU, with at least eight key tiles per split and at most 256.  Returns -1 when the
  * sizes fail attn_fwd_splitkv's size checks (NEGATIVE_SIZE .. SIZE_OVERFLOW).
  * Queries the current device's CU count; enqueues nothing.
  */
