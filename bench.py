@@ -292,7 +292,8 @@ def main():
         gbs = nbytes / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roofline.update({"traffic": traffic, "kernel": "attn_fwd_kernel", "avg_launch_ms": round(avg_ms, 4),
+    kernel = "attn_fwd_kernel" if res["n_splits"] == 1 else "attn_fwd_kernel split pass + attn_merge_kernel"
+    roofline.update({"traffic": traffic, "kernel": kernel, "avg_launch_ms": round(avg_ms, 4),
                      "n_splits": res["n_splits"],
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes})
     line = {
