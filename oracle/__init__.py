@@ -1,3 +1,4 @@
 """CPU float64 oracle (test infrastructure only; never on the product path)."""
 from .naive_attention import (attention_forward, attention_rows, kv_head, merge_partials,  # noqa: F401
                               ROW_BLOCK)
+from .naive_backward import attention_backward, backward_keys, backward_rows  # noqa: F401

@@ -1,0 +1,168 @@
+"""Checks that pin the backward oracle (dQ, dK, dV) to facts other than itself.
+
+Each check takes a namespace `ora` with attention_backward, backward_rows,
+backward_keys (the backward oracle, possibly a mutant) and attention_forward
+(the pinned forward oracle), and raises AssertionError on failure.
+
+Pins used:
+  * finite differences: central differences of sum(dO * O) through the forward
+    oracle, element by element, on tiny inputs (square, rectangular, causal,
+    GQA);
+  * library: PyTorch autograd through scaled_dot_product_attention in float64
+    on the CPU (K/V repeated per group, gradients summed back; the lower-right
+    causal bias for N_q < N_kv), for all three oracle entry points;
+  * closed forms: one key (dQ = dK = 0, dV = summed dO), zero scale (dQ = dK = 0,
+    dV = dO averaged over each row's visible keys), identical keys (dQ = 0);
+  * invariant: the key gradients of a kv head sum to zero (softmax rows are
+    invariant to a common shift of all keys);
+  * head map: GQA gradients equal MHA gradients on repeated K/V, summed back.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TOL = 1e-10
+
+
+def _close(a, b, tol=TOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert err <= tol * (1 + np.max(np.abs(b), initial=0.0)), f"{what}: max err {err}"
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _inputs(B, H_q, H_kv, N_q, N_kv, D, seed):
+    return (_rand((B, H_q, N_q, D), seed), _rand((B, H_kv, N_kv, D), seed + 1),
+            _rand((B, H_kv, N_kv, D), seed + 2), _rand((B, H_q, N_q, D), seed + 3))
+
+
+def pin_bwd_finite_differences(ora):
+    eps = 1e-5
+    for (B, H_q, H_kv, N_q, N_kv, D, causal, seed) in [
+        (1, 2, 1, 3, 5, 3, True, 11), (1, 2, 2, 4, 4, 2, False, 12), (1, 3, 1, 4, 4, 2, True, 13),
+        (1, 2, 1, 1, 6, 3, True, 14), (1, 1, 1, 5, 3, 2, False, 15),
+    ]:
+        q, k, v, dO = _inputs(B, H_q, H_kv, N_q, N_kv, D, seed)
+        sc = 0.8
+
+        def loss(q_, k_, v_):
+            O, _ = ora.attention_forward(q_, k_, v_, is_causal=causal, sm_scale=sc)
+            return float(np.sum(dO * O))
+
+        dQ, dK, dV = ora.attention_backward(q, k, v, dO, is_causal=causal, sm_scale=sc)
+        for name, x, g in (("q", q, dQ), ("k", k, dK), ("v", v, dV)):
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            _close(g, fd, tol=1e-7, what=f"FD d{name} {causal} {N_q}x{N_kv}")
+
+
+def _torch_grads(q, k, v, dO, causal, sc):
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention.bias import causal_lower_right
+    H_q, H_kv = q.shape[1], k.shape[1]
+    G = H_q // H_kv
+    tq = torch.from_numpy(q).requires_grad_(True)
+    tk = torch.from_numpy(k).requires_grad_(True)
+    tv = torch.from_numpy(v).requires_grad_(True)
+    kr = tk.repeat_interleave(G, dim=1)
+    vr = tv.repeat_interleave(G, dim=1)
+    N_q, N_kv = q.shape[2], k.shape[2]
+    if causal and N_q != N_kv:
+        o = F.scaled_dot_product_attention(tq, kr, vr, attn_mask=causal_lower_right(N_q, N_kv),
+                                           scale=sc)
+    else:
+        o = F.scaled_dot_product_attention(tq, kr, vr, is_causal=causal, scale=sc)
+    o.backward(torch.from_numpy(dO))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def pin_bwd_torch_autograd(ora):
+    for (B, H_q, H_kv, N_q, N_kv, D, causal, seed) in [
+        (2, 4, 2, 17, 17, 8, True, 21), (1, 4, 4, 9, 23, 16, False, 22),
+        (1, 6, 2, 7, 30, 8, True, 23), (1, 3, 1, 1, 19, 8, True, 24),
+    ]:
+        q, k, v, dO = _inputs(B, H_q, H_kv, N_q, N_kv, D, seed)
+        sc = 1.0 / math.sqrt(D)
+        tq, tk, tv = _torch_grads(q, k, v, dO, causal, sc)
+        dQ, dK, dV = ora.attention_backward(q, k, v, dO, is_causal=causal, sm_scale=sc)
+        _close(dQ, tq, what="torch dQ")
+        _close(dK, tk, what="torch dK")
+        _close(dV, tv, what="torch dV")
+        rows = np.array([0, N_q - 1, N_q // 2])
+        for h in (0, H_q - 1):
+            _close(ora.backward_rows(q, k, v, dO, B - 1, h, rows, is_causal=causal, sm_scale=sc),
+                   tq[B - 1, h, rows], what="torch dQ rows")
+        keys = np.array([0, N_kv - 1, N_kv // 3])
+        for g in range(H_kv):
+            bk, bv = ora.backward_keys(q, k, v, dO, 0, g, keys, is_causal=causal, sm_scale=sc)
+            _close(bk, tk[0, g, keys], what="torch dK keys")
+            _close(bv, tv[0, g, keys], what="torch dV keys")
+
+
+def pin_bwd_single_key(ora):
+    q, k, v, dO = _inputs(2, 4, 2, 3, 1, 8, 31)
+    dQ, dK, dV = ora.attention_backward(q, k, v, dO, is_causal=False, sm_scale=0.7)
+    _close(dQ, np.zeros_like(dQ), what="1-key dQ")
+    _close(dK, np.zeros_like(dK), what="1-key dK")
+    for b in range(2):
+        for g in range(2):
+            _close(dV[b, g, 0], dO[b, 2 * g:2 * g + 2].sum(axis=(0, 1)), what="1-key dV")
+
+
+def pin_bwd_zero_scale(ora):
+    q, k, v, dO = _inputs(1, 2, 1, 6, 6, 4, 41)
+    for causal in (False, True):
+        dQ, dK, dV = ora.attention_backward(q, k, v, dO, is_causal=causal, sm_scale=0.0)
+        _close(dQ, np.zeros_like(dQ), what="scale0 dQ")
+        _close(dK, np.zeros_like(dK), what="scale0 dK")
+        for j in range(6):
+            exp = sum(dO[0, h, i] / ((i + 1) if causal else 6)
+                      for h in range(2) for i in range(6) if (not causal or j <= i))
+            _close(dV[0, 0, j], exp, what="scale0 dV")
+
+
+def pin_bwd_identical_keys(ora):
+    q, k, v, dO = _inputs(1, 2, 1, 7, 7, 5, 51)
+    k[:] = k[:, :, :1]
+    for causal in (False, True):
+        dQ, _, _ = ora.attention_backward(q, k, v, dO, is_causal=causal, sm_scale=0.6)
+        _close(dQ, np.zeros_like(dQ), what="identical keys dQ")
+
+
+def pin_bwd_key_grads_sum_to_zero(ora):
+    q, k, v, dO = _inputs(2, 4, 2, 9, 12, 6, 61)
+    for causal in (False, True):
+        _, dK, _ = ora.attention_backward(q, k, v, dO, is_causal=causal, sm_scale=0.9)
+        _close(dK.sum(axis=2), np.zeros((2, 2, 6)), what="sum_j dK_j")
+
+
+def pin_bwd_gqa_equals_repeated(ora):
+    q, k, v, dO = _inputs(1, 6, 2, 8, 8, 4, 71)
+    for causal in (False, True):
+        dQ, dK, dV = ora.attention_backward(q, k, v, dO, is_causal=causal, sm_scale=0.5)
+        kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+        dQr, dKr, dVr = ora.attention_backward(q, kr, vr, dO, is_causal=causal, sm_scale=0.5)
+        _close(dQ, dQr, tol=1e-13, what="gqa dQ")
+        _close(dK, dKr.reshape(1, 2, 3, 8, 4).sum(axis=2), tol=1e-13, what="gqa dK")
+        _close(dV, dVr.reshape(1, 2, 3, 8, 4).sum(axis=2), tol=1e-13, what="gqa dV")
+
+
+PINS_BWD = [
+    pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_single_key, pin_bwd_zero_scale,
+    pin_bwd_identical_keys, pin_bwd_key_grads_sum_to_zero, pin_bwd_gqa_equals_repeated,
+]
