@@ -25,7 +25,12 @@ element b, query head h and kv head g:
 
 The gradient through the softmax, dS = P * (dP - rowsum(P * dP)), is the
 Jacobian of the row softmax applied to dP; Dl is taken as rowsum(dO * O), which
-equals rowsum(P * dP) because O = P V.
+equals rowsum(P * dP) because O = P V.  The forward hands q, k, v, the
+log-sum-exp and o to the backward (page "Flash Attention 与 Kernel 优化",
+"输出与保存状态": all five are kept in the autograd context), so o is an input
+of the backward: with `out` given, Dl = rowsum(dO * out) uses it (a GPU
+backward receives the bf16-rounded forward output); without it, O is
+computed here, which gives the exact gradient.
 
 Implementation shape: per (b, h) the full score matrix is materialised (so
 inputs are limited to a few thousand rows and keys), in float64, with no
@@ -52,8 +57,10 @@ def _probs(q, k, b, h, g, rows, *, is_causal, sm_scale, off, keys=None):
     return P if keys is None else P[:, keys]
 
 
-def attention_backward(q, k, v, dout, *, is_causal: bool, sm_scale: float):
-    """(dQ [B,H_q,N_q,D], dK [B,H_kv,N_kv,D], dV [B,H_kv,N_kv,D]) in float64."""
+def attention_backward(q, k, v, dout, *, is_causal: bool, sm_scale: float, out=None):
+    """(dQ [B,H_q,N_q,D], dK [B,H_kv,N_kv,D], dV [B,H_kv,N_kv,D]) in float64.
+
+    out: optional forward output [B,H_q,N_q,D] used for Dl (see above)."""
     B, H_q, H_kv, N_q, N_kv, D = _check(q, k, v)
     if dout.shape != q.shape:
         raise ValueError("dout must have the shape of q")
@@ -69,7 +76,7 @@ def attention_backward(q, k, v, dout, *, is_causal: bool, sm_scale: float):
             g = kv_head(h, H_q, H_kv)
             P = _probs(q, k, b, h, g, rows, is_causal=is_causal, sm_scale=sm_scale, off=off)
             dO = dout[b, h]
-            O = P @ v[b, g]
+            O = P @ v[b, g] if out is None else out[b, h]
             dV[b, g] += P.T @ dO
             dP = dO @ v[b, g].T
             Dl = (dO * O).sum(axis=1)
@@ -79,28 +86,31 @@ def attention_backward(q, k, v, dout, *, is_causal: bool, sm_scale: float):
     return dQ, dK, dV
 
 
-def backward_rows(q, k, v, dout, b: int, h: int, rows, *, is_causal: bool, sm_scale: float):
-    """dQ[b, h, rows] ([len(rows), D], float64)."""
+def backward_rows(q, k, v, dout, b: int, h: int, rows, *, is_causal: bool, sm_scale: float,
+                  out=None):
+    """dQ[b, h, rows] ([len(rows), D], float64); out as in attention_backward."""
     B, H_q, H_kv, N_q, N_kv, D = _check(q, k, v)
     off = N_kv - N_q if is_causal else 0
     g = kv_head(h, H_q, H_kv)
     rows = np.asarray(rows, dtype=np.int64)
-    out = np.empty((rows.size, D))
+    res = np.empty((rows.size, D))
     for s in range(0, rows.size, ROW_BLOCK):
         r = rows[s:s + ROW_BLOCK]
         P = _probs(q, k, b, h, g, r, is_causal=is_causal, sm_scale=sm_scale, off=off)
         dO = dout[b, h, r]
-        O = P @ v[b, g]
+        O = P @ v[b, g] if out is None else out[b, h, r]
         dP = dO @ v[b, g].T
         Dl = (dO * O).sum(axis=1)
         dS = P * (dP - Dl[:, None])
-        out[s:s + ROW_BLOCK] = sm_scale * (dS @ k[b, g])
-    return out
+        res[s:s + ROW_BLOCK] = sm_scale * (dS @ k[b, g])
+    return res
 
 
-def backward_keys(q, k, v, dout, b: int, g: int, keys, *, is_causal: bool, sm_scale: float):
+def backward_keys(q, k, v, dout, b: int, g: int, keys, *, is_causal: bool, sm_scale: float,
+                  out=None):
     """(dK[b, g, keys], dV[b, g, keys]) ([len(keys), D] each, float64), summed
-    over the query heads of kv head g and all their rows."""
+    over the query heads of kv head g and all their rows; out as in
+    attention_backward."""
     B, H_q, H_kv, N_q, N_kv, D = _check(q, k, v)
     off = N_kv - N_q if is_causal else 0
     keys = np.asarray(keys, dtype=np.int64)
@@ -112,7 +122,7 @@ def backward_keys(q, k, v, dout, b: int, g: int, keys, *, is_causal: bool, sm_sc
             r = np.arange(s, min(s + ROW_BLOCK, N_q))
             P = _probs(q, k, b, h, g, r, is_causal=is_causal, sm_scale=sm_scale, off=off)
             dO = dout[b, h, r]
-            O = P @ v[b, g]
+            O = P @ v[b, g] if out is None else out[b, h, r]
             Dl = (dO * O).sum(axis=1)
             Pk = P[:, keys]
             dPk = dO @ v[b, g, keys].T

@@ -15,7 +15,9 @@ Pins used:
     dV = dO averaged over each row's visible keys), identical keys (dQ = 0);
   * invariant: the key gradients of a kv head sum to zero (softmax rows are
     invariant to a common shift of all keys);
-  * head map: GQA gradients equal MHA gradients on repeated K/V, summed back.
+  * head map: GQA gradients equal MHA gradients on repeated K/V, summed back;
+  * the forward output as an input: the exact output changes nothing, and a
+    perturbed one moves dQ by the closed-form amount and leaves dV unchanged.
 """
 from __future__ import annotations
 
@@ -162,7 +164,35 @@ def pin_bwd_gqa_equals_repeated(ora):
         _close(dV, dVr.reshape(1, 2, 3, 8, 4).sum(axis=2), tol=1e-13, what="gqa dV")
 
 
+def pin_bwd_supplied_exact_output(ora):
+    """Handing the backward the exact forward output changes nothing; a
+    perturbed output moves dQ by exactly -scale * (dO . delta) * (P K) per row."""
+    q, k, v, dO = _inputs(1, 4, 2, 11, 14, 6, 81)
+    for causal in (False, True):
+        O, _ = ora.attention_forward(q, k, v, is_causal=causal, sm_scale=0.7)
+        ref = ora.attention_backward(q, k, v, dO, is_causal=causal, sm_scale=0.7)
+        got = ora.attention_backward(q, k, v, dO, is_causal=causal, sm_scale=0.7, out=O)
+        for a, b_ in zip(got, ref):
+            _close(a, b_, tol=1e-13, what="supplied O")
+        dl = _rand(O.shape, 82, 1e-3)
+        dQ2, dK2, dV2 = ora.attention_backward(q, k, v, dO, is_causal=causal, sm_scale=0.7,
+                                               out=O + dl)
+        _close(dV2, ref[2], tol=1e-13, what="dV independent of O")
+        # dS changes by -P * delta_i with delta_i = dO_i . dl_i, so dQ_i by -0.7 delta_i (P K)_i;
+        # (P K)_i is attention with K as the values
+        shift = np.einsum("bhnd,bhnd->bhn", dO, dl)
+        PK, _ = ora.attention_forward(q, k, k, is_causal=causal, sm_scale=0.7)
+        _close(dQ2, ref[0] - 0.7 * shift[..., None] * PK, tol=1e-12, what="dQ shift")
+        rows = np.array([0, 10])
+        _close(ora.backward_rows(q, k, v, dO, 0, 1, rows, is_causal=causal, sm_scale=0.7, out=O + dl),
+               dQ2[0, 1, rows], what="rows with out")
+        keys = np.array([0, 13])
+        bk, _ = ora.backward_keys(q, k, v, dO, 0, 1, keys, is_causal=causal, sm_scale=0.7, out=O + dl)
+        _close(bk, dK2[0, 1, keys], what="keys with out")
+
+
 PINS_BWD = [
     pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_single_key, pin_bwd_zero_scale,
     pin_bwd_identical_keys, pin_bwd_key_grads_sum_to_zero, pin_bwd_gqa_equals_repeated,
+    pin_bwd_supplied_exact_output,
 ]

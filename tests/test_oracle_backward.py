@@ -56,6 +56,7 @@ MUTATIONS = {
     "keys_dv_scaled": ("dV += Pk.T @ dO", "dV += sm_scale * (Pk.T @ dO)"),
     "dv_scaled": ("dV[b, g] += P.T @ dO", "dV[b, g] += sm_scale * (P.T @ dO)"),
     "head_map_modulo": ("g = kv_head(h, H_q, H_kv)", "g = h % H_kv"),
+    "supplied_output_ignored": ("O = P @ v[b, g] if out is None else out[b, h]", "O = P @ v[b, g]"),
 }
 
 
