@@ -7,6 +7,7 @@ If the library is not built, every call raises; there is no fallback path.
     out, lse = fwd(q, k, v, is_causal=True)          # allocates out and lse
     attn_fwd(q, k, v, out, lse, is_causal=True)      # caller-provided buffers
     out, lse = fwd_splitkv(q1, k, v, is_causal=True) # N_q != N_kv, key splits, decode
+    dq, dk, dv = bwd(q, k, v, out, dout, lse, is_causal=True)   # backward
 
 q: [B, H_q, N, D] bf16, k and v: [B, H_kv, N, D] bf16, contiguous, on the
 current CUDA (HIP) device; out: like q; lse: [B, H_q, N] float32.  The split
@@ -22,11 +23,13 @@ import os
 from .build import LIB_PATH
 
 __all__ = ["attn_fwd", "fwd", "attn_fwd_splitkv", "fwd_splitkv", "attn_splitkv_num_splits",
-           "attn_splitkv_workspace_size", "attn_status_string", "attn_abi_version",
+           "attn_splitkv_workspace_size", "attn_bwd", "bwd", "attn_bwd_workspace_size",
+           "attn_status_string", "attn_abi_version",
            "load_library", "AttnError", "EXPORTED_SYMBOLS"]
 
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splitkv", "attn_splitkv_num_splits",
-                    "attn_splitkv_workspace_size", "attn_status_string", "attn_abi_version")
+                    "attn_splitkv_workspace_size", "attn_bwd", "attn_bwd_workspace_size",
+                    "attn_status_string", "attn_abi_version")
 
 _lib = None
 
@@ -57,6 +60,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_splitkv_num_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int]
     lib.attn_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.attn_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 5
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int64] * 3
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_abi_version.restype = ctypes.c_int
@@ -200,3 +208,63 @@ def fwd_splitkv(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
     attn_fwd_splitkv(q, k, v, out, lse, is_causal=is_causal, sm_scale=sm_scale,
                      n_splits=max(ns, 1), workspace=ws, stream=stream)
     return out, lse
+
+
+def attn_bwd_workspace_size(B: int, H_q: int, N_q: int) -> int:
+    """Workspace bytes attn_bwd needs (per query row: log2-unit LSE and rowsum(dO*O))."""
+    return int(load_library().attn_bwd_workspace_size(B, H_q, N_q))
+
+
+def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, is_causal: bool = False,
+             sm_scale: float | None = None, workspace=None, stream=None) -> None:
+    """Enqueue the backward into dq, dk, dv (workspace: attn_bwd_workspace_size bytes)."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, D]")
+    B, H_q, N_q, D = q.shape
+    H_kv, N_kv = k.shape[1], k.shape[2]
+    for name, t, shape, dt in (("q", q, (B, H_q, N_q, D), torch.bfloat16),
+                               ("k", k, (B, H_kv, N_kv, D), torch.bfloat16),
+                               ("v", v, (B, H_kv, N_kv, D), torch.bfloat16),
+                               ("out", out, (B, H_q, N_q, D), torch.bfloat16),
+                               ("dout", dout, (B, H_q, N_q, D), torch.bfloat16),
+                               ("lse", lse, (B, H_q, N_q), torch.float32),
+                               ("dq", dq, (B, H_q, N_q, D), torch.bfloat16),
+                               ("dk", dk, (B, H_kv, N_kv, D), torch.bfloat16),
+                               ("dv", dv, (B, H_kv, N_kv, D), torch.bfloat16)):
+        _check_tensor(t, name, shape, dt)
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != q.device:
+            raise ValueError("workspace must be a tensor on q's device")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                          B, H_q, H_kv, N_q, N_kv, D, float(sm_scale), int(bool(is_causal)),
+                          ws_ptr, ws_bytes, handle)
+    if st != 0:
+        raise AttnError(st, attn_status_string(st))
+
+
+def bwd(q, k, v, out, dout, lse, is_causal: bool = False, sm_scale: float | None = None,
+        stream=None):
+    """Allocate dq, dk, dv and the workspace, run attn_bwd, return (dq, dk, dv)."""
+    import torch
+    B, H_q, N_q, D = q.shape
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    nbytes = attn_bwd_workspace_size(B, H_q, N_q)
+    ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
+    attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, is_causal=is_causal, sm_scale=sm_scale,
+             workspace=ws, stream=stream)
+    return dq, dk, dv

@@ -1,0 +1,488 @@
+// Attention backward for gfx950 (CDNA4): device code.
+//
+// Method (page "Attention Kernel 实现与正确性验证", section 1.1, third trick:
+// the backward recomputes the attention from Q, K and the saved row
+// statistics instead of storing S; page "Flash Attention 与 Kernel 优化",
+// "Autograd 包装与反向传播": rebuild s = q k^T scale, apply the causal mask,
+// rebuild p, then dv, dp, ds, dq, dk).  With the forward's log-sum-exp L:
+//   P  = exp(scale Q K^T - L)          (masked entries 0)
+//   dV = P^T dO,   dP = dO V^T,   Dl = rowsum(dO * O),   dS = P * (dP - Dl)
+//   dQ = scale dS K,   dK = scale dS^T Q          (dK, dV summed over the
+//                                                  query heads of a kv head)
+//
+// Three kernels, no atomics (the result is deterministic):
+//  * attn_bwd_prep_kernel: Dl = rowsum(dO * O) and L2 = L log2(e) per row.
+//  * attn_bwd_dkdv_kernel: a workgroup owns 32 keys per wave of one kv head;
+//    K and V of those keys stay in registers while the query rows of every
+//    head of the group stream through LDS (head-major, so each tile is
+//    contiguous rows of one head).  Products are taken with the rows of the
+//    MFMA accumulator being query rows and its columns keys (a lane owns one
+//    key): S = Q K^T and dP = dO V^T read Q and dO from LDS as A operands;
+//    dV^T = dO^T P and dK^T = Q^T dS read dO^T and Q^T with the LDS transpose
+//    read, while P and dS, rounded to bf16, are the B operands exactly as the
+//    accumulator holds them (the query order this implies is the order the
+//    transpose read returns).
+//  * attn_bwd_dq_kernel: the forward's layout (a lane owns one (row, head)
+//    pair of a kv group, K/V tiles stream through LDS): S^T = K Q^T,
+//    dP^T = V dO^T, dS^T = P^T (dP^T - Dl), dQ^T += K^T dS^T with K^T from the
+//    transpose read.
+// Tiles read both row-wise (16-byte chunks) and with the transpose read use
+// a swizzle that is conflict-free for both patterns (bwd_swz below).
+#pragma once
+
+#include "attn_fwd_kernel.hpp"
+
+namespace ea02 {
+
+struct BwdParams {
+  const uint16_t* q;     // [B, H_q, N_q, D] bf16
+  const uint16_t* k;     // [B, H_kv, N_kv, D]
+  const uint16_t* v;     // [B, H_kv, N_kv, D]
+  const uint16_t* o;     // [B, H_q, N_q, D]  (forward output)
+  const uint16_t* dout;  // [B, H_q, N_q, D]
+  const float* lse;      // [B, H_q, N_q] natural log (forward)
+  uint16_t* dq;          // [B, H_q, N_q, D]
+  uint16_t* dk;          // [B, H_kv, N_kv, D]
+  uint16_t* dv;          // [B, H_kv, N_kv, D]
+  float* lse2;           // [B, H_q, N_q] workspace: L log2(e)
+  float* delta;          // [B, H_q, N_q] workspace: rowsum(dO * O)
+  int B, H_q, H_kv, N_q, N_kv;
+  int G;                 // H_q / H_kv
+  int n_pairs;           // N_q * G
+  int causal_off;        // N_kv - N_q when causal, else 0
+  int causal;
+  int n_heads_wg;        // B * H_kv
+  int n_key_blocks;      // dK/dV kernel: ceil(N_kv / keys per workgroup)
+  int n_pair_blocks;     // dQ kernel: ceil(n_pairs / pairs per workgroup)
+  float scale_log2;      // max(|sm_scale| log2(e), FLT_MIN)
+  float grad_scale;      // sm_scale (signed): factor of dQ and dK
+  uint32_t k_sign;       // 0x80008000 when sm_scale < 0: K negated in S (dK/dV kernel)
+  uint32_t q_sign;       // 0x80008000 when sm_scale < 0: Q negated in S^T (dQ kernel)
+  int64_t rows;          // B * H_q * N_q
+};
+
+// 16-byte chunk swizzle for tiles read both row-wise (16 lanes, 16 rows, one
+// chunk: the XOR must be a bijection on 16 (D=128) or, per row parity, 8 (D=64)
+// consecutive rows) and with ds_read_b64_tr_b16 (a half wave reads 4 rows x 4
+// chunks: the XOR must move those 4 rows into 4 different aligned 4-chunk
+// groups (D=128) or row pairs of one parity into different halves (D=64)).
+template <int D>
+__device__ __forceinline__ int bwd_swz(int row) {
+  if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
+  else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
+
+// 4 bytes per lane from the buffer at byte offset voff into LDS at lds_addr +
+// 4 * lane (inline asm: not tracked by the compiler, see dma_16B).
+__device__ __forceinline__ void dma_4B(u32x4 rsrc, int voff, uint32_t lds_addr) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
+}
+
+// ---------------------------------------------------------------- prep
+// One row per D/8 threads (16 bytes each): Dl = sum_d dO * O, L2 = L log2 e.
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void attn_bwd_prep_kernel(BwdParams p) {
+  constexpr int TPR = D / 8;
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < p.rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * D + 8 * c);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(p.dout + row * D + 8 * c);
+    const bf16x8 ab = as_bf16x8(a), gb = as_bf16x8(g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)ab[e] * (float)gb[e];
+  }
+#pragma unroll
+  for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
+  if (row < p.rows && c == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D, int NW, int P, int BP>
+struct BwdKvCfg {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int DC = D / 8;                       // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BP * ROW_BYTES;      // Q or dO rows of one tile
+  static constexpr int LOADS = TILE_BYTES / 1024;
+  static constexpr int LPW = LOADS / NW;                 // 1 KiB loads per wave per tile and tensor
+  static constexpr int RPL = 1024 / ROW_BYTES;           // rows per 1 KiB load
+  static constexpr int STAT_BYTES = 2 * 4 * 64;          // per wave: L2 and Dl of up to 64 rows
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + NW * STAT_BYTES;
+  static constexpr int LDS_BYTES = P * STAGE_BYTES;
+  static constexpr int GROUP_LOADS = 2 * LPW + 2;
+  static_assert(BP == 32 || BP == 64, "tiles of 32 or 64 rows");
+  static_assert(LOADS % NW == 0 && LPW >= 1, "tile loads split evenly over waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
+  static_assert((P - 1) * GROUP_LOADS <= 63, "loads in flight fit the 6-bit vmcnt");
+};
+
+template <int D, int NW, int P, int BP>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(BwdParams p) {
+  using C = BwdKvCfg<D, NW, P, BP>;
+  constexpr int BK = 32 * NW;   // keys per workgroup
+  constexpr int NBLK = BP / 32; // 32-row blocks per tile
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // heaviest key blocks first (causal: block 0 sees every row), kv heads fastest
+  const int bid = blockIdx.x;
+  const int head_wg = bid % p.n_heads_wg;
+  const int kb = bid / p.n_heads_wg;
+  const int g = head_wg % p.H_kv;
+  const int b = head_wg / p.H_kv;
+  const int G = p.G;
+  const int N_q = p.N_q, N_kv = p.N_kv;
+  const int off = p.causal_off;
+  const int k0 = kb * BK;
+  const int kw = k0 + 32 * wave;     // first key of this wave
+  const int my_key = kw + col;
+
+  // rows before r_start see no key of this block; per head, row tiles of BP
+  const int r_start = p.causal ? max(0, k0 - off) : 0;
+  const int n_rt = (N_q - r_start + BP - 1) / BP;
+  const int n_tiles = G * n_rt;
+
+  // K and V of this lane's key: B operands of S = Q K^T and dP = dO V^T
+  const size_t kv_base = ((size_t)b * p.H_kv + g) * (size_t)N_kv * D;
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const size_t kr = kv_base + (size_t)min(my_key, N_kv - 1) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(p.k + kr + ks * 16 + half * 8);
+      x ^= p.k_sign;
+      kf[ks] = as_bf16x8(x);
+      vf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.v + kr + ks * 16 + half * 8));
+    }
+  }
+
+  // Q, dO, L2 and Dl of the kv group's G heads: [G, N_q, ...] contiguous
+  const size_t qg_rows = ((size_t)b * p.H_q + (size_t)g * G) * (size_t)N_q;
+  const u32x4 q_rsrc = make_rsrc(p.q + qg_rows * D, (uint32_t)((size_t)G * N_q * C::ROW_BYTES));
+  const u32x4 do_rsrc = make_rsrc(p.dout + qg_rows * D, (uint32_t)((size_t)G * N_q * C::ROW_BYTES));
+  const u32x4 l_rsrc = make_rsrc(p.lse2 + qg_rows, (uint32_t)((size_t)G * N_q * 4));
+  const u32x4 d_rsrc = make_rsrc(p.delta + qg_rows, (uint32_t)((size_t)G * N_q * 4));
+
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
+  const int ld_row_in = lane / C::DC;
+  const int ld_chunk = lane % C::DC;
+  auto tile_rows = [&](int t, int& hs, int& row0) {
+    hs = t / n_rt;
+    row0 = r_start + (t - hs * n_rt) * BP;
+  };
+  // one tile (Q, dO, and this wave's private copy of L2 and Dl) into stage slot
+  auto issue = [&](int t, int slot) {
+    int hs, row0;
+    tile_rows(t, hs, row0);
+    const uint32_t st = lds_base + slot * C::STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      const int li = wave * C::LPW + i;
+      const int r = li * C::RPL + ld_row_in;
+      const int row = min(row0 + r, N_q - 1);
+      const int byte = (hs * N_q + row) * C::ROW_BYTES + ((ld_chunk ^ bwd_swz<D>(r)) << 4);
+      dma_16B(q_rsrc, byte, st + li * 1024);
+      dma_16B(do_rsrc, byte, st + C::TILE_BYTES + li * 1024);
+    }
+    const int srow = min(row0 + min(lane, BP - 1), N_q - 1);
+    const uint32_t sb = st + 2 * C::TILE_BYTES + wave * C::STAT_BYTES;
+    dma_4B(l_rsrc, (hs * N_q + srow) * 4, sb);
+    dma_4B(d_rsrc, (hs * N_q + srow) * 4, sb + 256);
+  };
+
+  // transpose-read offsets (tile-relative): rows 16 st + 4 half + L/4 (+8 for
+  // the second read), d = db*32 + 16 (G16 & 1) + 4 (L & 3); the swizzle of
+  // those rows does not depend on st
+  const int L16 = lane & 15;
+  int tr_off[2][D / 32];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int row = 4 * half + (L16 >> 2) + 8 * hi;
+      const int d = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
+      tr_off[hi][db] = row * C::ROW_BYTES + (((d >> 3) ^ bwd_swz<D>(row)) << 4) + (d & 7) * 2;
+    }
+  auto tr_read = [&](const uint8_t* base, int st, int db) {
+    const uint8_t* a = base + (16 * st) * C::ROW_BYTES;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[0][db]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[1][db]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto row_read = [&](const uint8_t* base, int row, int chunk) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(base + row * C::ROW_BYTES +
+                                                      ((chunk ^ bwd_swz<D>(row)) << 4)));
+  };
+
+  f32x16 dkT[D / 32], dvT[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dkT[db] = f32x16{};
+    dvT[db] = f32x16{};
+  }
+  const float sl2 = p.scale_log2;
+
+  auto compute = [&](int t, int slot) {
+    int hs, row0;
+    tile_rows(t, hs, row0);
+    const uint8_t* qt = lds + slot * C::STAGE_BYTES;
+    const uint8_t* dot = qt + C::TILE_BYTES;
+    const float* stl = reinterpret_cast<const float*>(qt + 2 * C::TILE_BYTES + wave * C::STAT_BYTES);
+    const float* std_ = stl + 64;
+    // masked tile: rows that cannot see some key of this wave, or rows past N_q
+    const bool masked = (p.causal && row0 + off < kw + 31) || row0 + BP > N_q;
+#pragma unroll
+    for (int c = 0; c < NBLK; ++c) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read(qt, c * 32 + col, 2 * ks + half), kf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read(dot, c * 32 + col, 2 * ks + half), vf[ks], dp, 0, 0, 0);
+      }
+      // element r holds query row row0 + c*32 + 8(r/4) + 4 half + r%4
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l4[j] = *reinterpret_cast<const f32x4*>(stl + c * 32 + 8 * j + 4 * half);
+        d4[j] = *reinterpret_cast<const f32x4*>(std_ + c * 32 + 8 * j + 4 * half);
+      }
+      f32x8 pf, sf;
+      bf16x8 pb[2], dsb[2];
+      const int lo_vis = my_key - off - row0 - c * 32 - 4 * half;  // visible: index >= lo_vis
+      const int hi_vis = N_q - row0 - c * 32 - 4 * half;           // and index < hi_vis
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[r >> 2][r & 3]));
+        if (masked) {
+          const int idx = 8 * (r >> 2) + (r & 3);
+          if ((p.causal && idx < lo_vis) || idx >= hi_vis) pe = 0.f;
+        }
+        pf[r & 7] = pe;
+        sf[r & 7] = pe * (dp[r] - d4[r >> 2][r & 3]);
+        if ((r & 7) == 7) {
+          pb[r >> 3] = __builtin_convertvector(pf, bf16x8);
+          dsb[r >> 3] = __builtin_convertvector(sf, bf16x8);
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(dot + c * 32 * C::ROW_BYTES, st, db), pb[st], dvT[db], 0, 0, 0);
+          dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qt + c * 32 * C::ROW_BYTES, st, db), dsb[st], dkT[db], 0, 0, 0);
+        }
+    }
+  };
+
+  // Load ring: tile t goes to slot t % P, issued P-1 tiles ahead; past the
+  // last tile a clamped tile is re-loaded so every wait is one constant vmcnt.
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int j = 0; j < P - 1; ++j) issue(min(j, n_tiles - 1), j);
+    for (int t = 0; t < n_tiles; ++t) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 2) * C::GROUP_LOADS) : "memory");
+      __syncthreads();
+      issue(min(t + P - 1, n_tiles - 1), (t + P - 1) % P);
+      compute(t, t % P);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may outlive the workgroup
+  }
+
+  // dK^T, dV^T: the lane holds key my_key, d = db*32 + 8(r/4) + 4 half + r%4
+  if (my_key < N_kv) {
+    uint16_t* dkr = p.dk + kv_base + (size_t)my_key * D;
+    uint16_t* dvr = p.dv + kv_base + (size_t)my_key * D;
+    const float gs = p.grad_scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * half;
+        f32x4 fk = {dkT[db][4 * g4] * gs, dkT[db][4 * g4 + 1] * gs, dkT[db][4 * g4 + 2] * gs, dkT[db][4 * g4 + 3] * gs};
+        f32x4 fv = {dvT[db][4 * g4], dvT[db][4 * g4 + 1], dvT[db][4 * g4 + 2], dvT[db][4 * g4 + 3]};
+        *reinterpret_cast<u32x2*>(dkr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(fk, bf16x4));
+        *reinterpret_cast<u32x2*>(dvr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(fv, bf16x4));
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+template <int D, int NW, int P, int BN>
+struct BwdQCfg {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int DC = D / 8;
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;
+  static constexpr int LOADS = TILE_BYTES / 1024;
+  static constexpr int LPW = LOADS / NW;
+  static constexpr int RPL = 1024 / ROW_BYTES;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;   // K then V
+  static constexpr int LDS_BYTES = P * STAGE_BYTES;
+  static constexpr int GROUP_LOADS = 2 * LPW;
+  static_assert(BN == 32 || BN == 64, "key tiles of 32 or 64");
+  static_assert(LOADS % NW == 0 && LPW >= 1, "tile loads split evenly over waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
+  static_assert((P - 1) * GROUP_LOADS <= 63, "loads in flight fit the 6-bit vmcnt");
+};
+
+template <int D, int NW, int P, int BN>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dq_kernel(BwdParams p) {
+  using C = BwdQCfg<D, NW, P, BN>;
+  constexpr int PPW = 32 * NW;  // (row, head) pairs per workgroup
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  const int bid = blockIdx.x;
+  const int head_wg = bid % p.n_heads_wg;
+  const int pb = p.n_pair_blocks - 1 - bid / p.n_heads_wg;  // heaviest first
+  const int g = head_wg % p.H_kv;
+  const int b = head_wg / p.H_kv;
+  const int G = p.G;
+  const int N_kv = p.N_kv;
+  const int off = p.causal_off;
+  const int last_pair = p.n_pairs - 1;
+  const int P0 = pb * PPW;
+  const int wp0 = P0 + wave * 32;
+  const int wave_row0 = min(wp0, last_pair) / G;
+  const int wg_row_end = min(P0 + PPW - 1, last_pair) / G + 1;
+  const int kv_end = p.causal ? min(wg_row_end + off, N_kv) : N_kv;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+
+  // this lane's pair: Q and dO fragments (B operands), L2 and Dl
+  const int pair = wp0 + col;
+  const bool valid = pair <= last_pair;
+  const int pc = min(pair, last_pair);
+  const int my_row = pc / G;
+  const int h = g * G + (pc - my_row * G);
+  const size_t bhr = ((size_t)b * p.H_q + h) * (size_t)p.N_q + my_row;
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 x = *reinterpret_cast<const u32x4*>(p.q + bhr * D + ks * 16 + half * 8);
+    x ^= p.q_sign;
+    qf[ks] = as_bf16x8(x);
+    df[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.dout + bhr * D + ks * 16 + half * 8));
+  }
+  const float l2 = p.lse2[bhr];
+  const float dl = p.delta[bhr];
+
+  const size_t kv_base = ((size_t)b * p.H_kv + g) * (size_t)N_kv * D;
+  const uint32_t head_bytes = (uint32_t)N_kv * C::ROW_BYTES;
+  const u32x4 k_rsrc = make_rsrc(p.k + kv_base, head_bytes);
+  const u32x4 v_rsrc = make_rsrc(p.v + kv_base, head_bytes);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
+  const int ld_row_in = lane / C::DC;
+  const int ld_chunk = lane % C::DC;
+  auto issue = [&](int t, int slot) {
+    const uint32_t st = lds_base + slot * C::STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      const int li = wave * C::LPW + i;
+      const int r = li * C::RPL + ld_row_in;
+      const int byte = min(t * BN + r, N_kv - 1) * C::ROW_BYTES + ((ld_chunk ^ bwd_swz<D>(r)) << 4);
+      dma_16B(k_rsrc, byte, st + li * 1024);
+      dma_16B(v_rsrc, byte, st + C::TILE_BYTES + li * 1024);
+    }
+  };
+
+  const int L16 = lane & 15;
+  int tr_off[2][D / 32];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int row = 4 * half + (L16 >> 2) + 8 * hi;
+      const int d = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
+      tr_off[hi][db] = row * C::ROW_BYTES + (((d >> 3) ^ bwd_swz<D>(row)) << 4) + (d & 7) * 2;
+    }
+
+  f32x16 dqT[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dqT[db] = f32x16{};
+  const float sl2 = p.scale_log2;
+
+  auto compute = [&](int t, int slot) {
+    const uint8_t* kt = lds + slot * C::STAGE_BYTES;
+    const uint8_t* vt = kt + C::TILE_BYTES;
+    const int key0 = t * BN;
+    const bool masked = (p.causal && key0 + BN - 1 > wave_row0 + off) || key0 + BN > N_kv;
+    // element (c, r) holds key key0 + c*32 + 8(r/4) + 4 half + r%4; visible below lim
+    const int lim = (p.causal ? min(my_row + off + 1, N_kv) : N_kv) - key0 - 4 * half;
+    bf16x8 dsb[BN / 16];
+#pragma unroll
+    for (int c = 0; c < BN / 32; ++c) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const int key = c * 32 + col;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int chunk = ((2 * ks + half) ^ bwd_swz<D>(key)) << 4;
+        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + key * C::ROW_BYTES + chunk));
+        const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + key * C::ROW_BYTES + chunk));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
+      }
+      f32x8 sf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2));
+        if (masked && c * 32 + 8 * (r >> 2) + (r & 3) >= lim) pe = 0.f;
+        sf[r & 7] = pe * (dp[r] - dl);
+        if ((r & 7) == 7) dsb[2 * c + (r >> 3)] = __builtin_convertvector(sf, bf16x8);
+      }
+    }
+    // dQ^T += K^T dS^T; k-step st covers keys 16 st .. 16 st + 15
+#pragma unroll
+    for (int st = 0; st < BN / 16; ++st)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint8_t* a = kt + (16 * st) * C::ROW_BYTES;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[0][db]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[1][db]));
+        const bf16x8 kT = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsb[st], dqT[db], 0, 0, 0);
+      }
+  };
+
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int j = 0; j < P - 1; ++j) issue(min(j, n_tiles - 1), j);
+    for (int t = 0; t < n_tiles; ++t) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 2) * C::GROUP_LOADS) : "memory");
+      __syncthreads();
+      issue(min(t + P - 1, n_tiles - 1), (t + P - 1) % P);
+      compute(t, t % P);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  if (valid) {
+    uint16_t* dqr = p.dq + bhr * D;
+    const float gs = p.grad_scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * half;
+        f32x4 f = {dqT[db][4 * g4] * gs, dqT[db][4 * g4 + 1] * gs, dqT[db][4 * g4 + 2] * gs, dqT[db][4 * g4 + 3] * gs};
+        *reinterpret_cast<u32x2*>(dqr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4));
+      }
+  }
+}
+
+}  // namespace ea02

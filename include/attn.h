@@ -1,5 +1,6 @@
 /*
- * attn.h -- C ABI of the MI355X (gfx950) fused attention forward library.
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention library (forward,
+ * split-KV forward and decode, backward).
  *
  * The operation is the forward pass of exact scaled-dot-product attention in
  * the FlashAttention-2 style: one query tile stays on chip while key/value
@@ -153,10 +154,58 @@ int64_t attn_splitkv_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_
  */
 size_t attn_splitkv_workspace_size(int64_t B, int64_t H_q, int64_t N_q, int64_t D, int64_t n_splits);
 
+/*
+ * attn_bwd -- enqueue the attention backward: dq, dk, dv of the scalar
+ * sum(dout * out) for the forward of attn_fwd / attn_fwd_splitkv (same head
+ * map, scale, mask and bottom-right alignment for N_q < N_kv).
+ *
+ * Method: page "Attention Kernel 实现与正确性验证", section 1.1 (third trick:
+ * the backward recomputes the attention from Q, K and the saved log-sum-exp
+ * instead of storing S); page "Flash Attention 与 Kernel 优化", "Autograd 包装与
+ * 反向传播" (rebuild s, mask, p, then dv, dp, ds, dq, dk).  With L = lse:
+ *   P  = exp(sm_scale q k^T - L)      (masked entries 0)
+ *   dv = P^T dout,  dP = dout v^T,  Dl = rowsum(dout * out),  dS = P * (dP - Dl)
+ *   dq = sm_scale dS k,  dk = sm_scale dS^T q
+ * dk and dv sum over the H_q / H_kv query heads of each kv head.  P and dS
+ * are rounded to bf16 for the products (fp32 accumulation), as the forward
+ * rounds P.
+ *
+ * Arguments
+ *   q, out, dout  bf16 [B, H_q, N_q, D];  k, v  bf16 [B, H_kv, N_kv, D]
+ *   lse           fp32 [B, H_q, N_q], natural log (the forward's output)
+ *   dq            bf16 [B, H_q, N_q, D], written
+ *   dk, dv        bf16 [B, H_kv, N_kv, D], written (zeros when N_q = 0)
+ *   sm_scale, is_causal as for the forward that produced out and lse
+ *   workspace     device scratch of at least attn_bwd_workspace_size(B, H_q,
+ *                 N_q) bytes, 16-byte aligned (per row: L log2 e and Dl);
+ *                 contents undefined on entry and after; calls that overlap on
+ *                 one workspace race
+ * All buffers are contiguous device memory of the current device.  Three
+ * kernels are enqueued on `stream`; the call never synchronises.  The result
+ * is deterministic (no atomics).
+ *
+ * Errors, checked in this order; nothing is enqueued on failure:
+ *   NEGATIVE_SIZE, HEAD_RATIO, HEAD_DIM, CAUSAL_FLAG, SCALE, CAUSAL_SHAPE,
+ *   SIZE_OVERFLOW (N_q or N_kv > 2^24, N_kv*D*2 > 2^31, N_q*(H_q/H_kv)*D*2 >
+ *   2^31, B*H_q*N_q >= 2^31, grid >= 2^31), then empty work (B or H_q = 0, or
+ *   N_q = N_kv = 0) returns ATTN_OK, then NO_KEYS (N_kv = 0 < N_q),
+ *   NULL_POINTER (q, out, dout, lse, dq may be NULL only when N_q = 0),
+ *   ALIGNMENT (16 bytes, lse 4), WORKSPACE, ALIAS (dq, dk, dv or the workspace
+ *   overlapping an input or each other), LAUNCH.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q, int64_t H_kv,
+             int64_t N_q, int64_t N_kv, int64_t D, float sm_scale, int is_causal, void* workspace,
+             size_t workspace_size, void* stream);
+
+/* attn_bwd_workspace_size -- bytes of workspace attn_bwd needs:
+ * B * H_q * N_q * 8 (0 for negative sizes). */
+size_t attn_bwd_workspace_size(int64_t B, int64_t H_q, int64_t N_q);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);
 
-/* Library ABI version, currently 2 (1 had attn_fwd only). */
+/* Library ABI version, currently 3 (1: attn_fwd; 2: + split-KV; 3: + backward). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
 
 
 def test_status_strings_distinct(lib):
@@ -198,3 +198,63 @@ def test_product_path_does_not_import_oracle():
             if fn.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 txt = open(os.path.join(dirpath, fn), encoding="utf-8").read()
                 assert "import oracle" not in txt and "from oracle" not in txt, fn
+
+
+# ------------------------------------------------------------ backward entry
+DO, DQ, DK, DV, WB = (0x200000000 + i * 64 * MiB for i in range(5))
+
+
+def call_bwd(lib, q=Q, k=K, v=V, o=O, do=DO, l=L, dq=DQ, dk=DK, dv=DV, B=1, H_q=4, H_kv=2, N_q=16,
+             N_kv=40, D=64, scale=0.125, causal=0, ws=WB, ws_bytes=64 * MiB):
+    return lib.attn_bwd(q, k, v, o, do, l, dq, dk, dv, B, H_q, H_kv, N_q, N_kv, D,
+                        ctypes.c_float(scale), causal, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N_q=-1), "ATTN_ERR_NEGATIVE_SIZE"),
+    (dict(H_q=5, H_kv=2), "ATTN_ERR_HEAD_RATIO"),
+    (dict(D=80), "ATTN_ERR_HEAD_DIM"),
+    (dict(causal=5), "ATTN_ERR_CAUSAL_FLAG"),
+    (dict(scale=float("nan")), "ATTN_ERR_SCALE"),
+    (dict(causal=1, N_q=41), "ATTN_ERR_CAUSAL_SHAPE"),
+    (dict(N_kv=(1 << 23) + 1, D=128), "ATTN_ERR_SIZE_OVERFLOW"),
+    (dict(N_q=1 << 20, H_q=16, H_kv=1, D=128, N_kv=1 << 20), "ATTN_ERR_SIZE_OVERFLOW"),
+    (dict(N_kv=0), "ATTN_ERR_NO_KEYS"),
+    (dict(do=0), "ATTN_ERR_NULL_POINTER"),
+    (dict(dv=0), "ATTN_ERR_NULL_POINTER"),
+    (dict(dq=DQ + 8), "ATTN_ERR_ALIGNMENT"),
+    (dict(l=L + 1), "ATTN_ERR_ALIGNMENT"),
+    (dict(ws=0), "ATTN_ERR_WORKSPACE"),
+    (dict(ws_bytes=100), "ATTN_ERR_WORKSPACE"),
+    (dict(ws=WB + 4), "ATTN_ERR_WORKSPACE"),
+    (dict(dq=Q), "ATTN_ERR_ALIAS"),
+    (dict(dk=DV), "ATTN_ERR_ALIAS"),
+    (dict(ws=DO + 16), "ATTN_ERR_ALIAS"),
+    (dict(dv=L), "ATTN_ERR_ALIAS"),
+])
+def test_bwd_invalid_arguments_rejected(lib, kw, code):
+    assert call_bwd(lib, **kw) == STATUS[code]
+
+
+def test_bwd_check_order(lib):
+    assert call_bwd(lib, D=80, q=0, causal=1, N_q=50) == STATUS["ATTN_ERR_HEAD_DIM"]
+    assert call_bwd(lib, q=0, N_kv=0) == STATUS["ATTN_ERR_NO_KEYS"]
+    assert call_bwd(lib, q=0, ws=0) == STATUS["ATTN_ERR_NULL_POINTER"]
+    assert call_bwd(lib, ws=0, dq=Q) == STATUS["ATTN_ERR_WORKSPACE"]
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H_q=0, H_kv=1), dict(N_q=0, N_kv=0)])
+def test_bwd_empty_work_is_success_without_pointers(lib, kw):
+    assert call_bwd(lib, q=0, k=0, v=0, o=0, do=0, l=0, dq=0, dk=0, dv=0, ws=0, **kw) == STATUS["ATTN_OK"]
+
+
+def test_bwd_no_query_rows_needs_only_key_buffers(lib):
+    # N_q = 0 with keys: dK = dV = 0 are still written, so k, v, dk, dv are required
+    assert call_bwd(lib, N_q=0, dk=0) == STATUS["ATTN_ERR_NULL_POINTER"]
+    assert call_bwd(lib, N_q=0, q=0, o=0, do=0, l=0, dq=0, ws=0, dk=K) == STATUS["ATTN_ERR_ALIAS"]
+
+
+def test_bwd_workspace_size():
+    assert ea.attn_bwd_workspace_size(2, 32, 1024) == 2 * 32 * 1024 * 8
+    assert ea.attn_bwd_workspace_size(1, 4, 0) == 0
+    assert ea.attn_bwd_workspace_size(-1, 4, 4) == 0

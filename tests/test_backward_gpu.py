@@ -1,0 +1,235 @@
+"""GPU parity of the attention backward (dQ, dK, dV) against the float64 CPU
+oracle.
+
+Inputs are seeded bf16 Q, K, V and dO.  Unless a case says otherwise, the
+forward output O (rounded to bf16) and the LSE (fp32) handed to the backward
+are the oracle's, so that the backward is checked on its own; the chained
+cases feed it this library's own forward instead.  The forward output is an
+operand of the backward (Dl = rowsum(dO * out)), so the oracle is given the
+same bf16 output the kernel receives.
+
+Tolerance (the pages give none for gradients; the forward's bf16 allclose of
+page "Attention Kernel 实现与正确性验证", section 1.3, made scale-free):
+element-wise |g - r| <= 2e-2 s + 2e-2 |r|, where s is the larger of the root
+mean square of the reference row (the D values of one query row of dQ, or of
+one key of dK, dV) and of the whole reference tensor, at least 1e-4 (fp32
+round-off where the reference is exactly zero); nothing non-finite.  P
+and dS are rounded to bf16 before their products (relative 2^-9 each), so the
+error of a gradient row scales with that row's own magnitude: early causal
+rows, which see few keys, have gradients ten times the tensor's typical size
+(a CPU emulation of the rounding reproduces their errors).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+G_ATOL = 2e-2   # times rms of the reference tensor
+G_RTOL = 2e-2
+G_FLOOR = 1e-4  # least row scale: fp32 round-off of gradients that are exactly zero
+
+
+@pytest.fixture(scope="module")
+def ea():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_02_amd as m
+    m.load_library()
+    return m
+
+
+def _dev():
+    return torch.device("cuda", 0)
+
+
+def _inputs(B, H_q, H_kv, N_q, N_kv, D, seed):
+    q, k, v = workloads.make_inputs(B, H_q, H_kv, N_q, D, seed, N_kv=N_kv)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed + 7919)
+    dO = torch.randn((B, H_q, N_q, D), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return q, k, v, dO
+
+
+def _check(name, got, ref, what):
+    g = got.to(torch.float64).numpy() if isinstance(got, torch.Tensor) else got
+    assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
+    if ref.size == 0:
+        return
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    s = np.maximum(np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True)), max(rms, G_FLOOR))
+    err = np.abs(g - ref)
+    bad = err > G_ATOL * s + G_RTOL * np.abs(ref)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} {name} elements out of tolerance; "
+                           f"max err {err.max():.3e}, rms(ref) {rms:.3e}")
+
+
+def _run_bwd(ea, q, k, v, o, dO, lse, causal, scale, poison=True):
+    dev = _dev()
+    t = [x.to(dev) for x in (q, k, v, o, dO)]
+    lsed = lse.to(dev)
+    dq = torch.empty_like(t[0])
+    dk = torch.empty_like(t[1])
+    dv = torch.empty_like(t[2])
+    if poison:
+        for x in (dq, dk, dv):
+            x.fill_(float("nan"))
+    B, H_q, N_q, D = q.shape
+    ws = torch.full((max(ea.attn_bwd_workspace_size(B, H_q, N_q), 1),), 0xFF, dtype=torch.uint8,
+                    device=dev)
+    ea.attn_bwd(t[0], t[1], t[2], t[3], t[4], lsed, dq, dk, dv, is_causal=causal, sm_scale=scale,
+                workspace=ws)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def _oracle_fwd_outputs(q64, k64, v64, causal, scale):
+    O, L = oracle.attention_forward(q64, k64, v64, is_causal=causal, sm_scale=scale)
+    return torch.from_numpy(O).to(torch.bfloat16), torch.from_numpy(L).to(torch.float32)
+
+
+def _case(ea, B, H_q, H_kv, N_q, N_kv, D, causal, seed, scale=None, chained=False, mutate=None):
+    q, k, v, dO = _inputs(B, H_q, H_kv, N_q, N_kv, D, seed)
+    if mutate is not None:
+        q, k, v, dO = mutate(q, k, v, dO)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    q64, k64, v64, d64 = (workloads.to_float64(x) for x in (q, k, v, dO))
+    if chained:
+        dev = _dev()
+        o, lse = ea.fwd_splitkv(q.to(dev), k.to(dev), v.to(dev), is_causal=causal,
+                                sm_scale=scale, n_splits=1)
+        o, lse = o.cpu(), lse.cpu()
+    else:
+        o, lse = _oracle_fwd_outputs(q64, k64, v64, causal, scale)
+    dq, dk, dv = _run_bwd(ea, q, k, v, o, dO, lse, causal, scale)
+    rq, rk, rv = oracle.attention_backward(q64, k64, v64, d64, is_causal=causal, sm_scale=scale,
+                                           out=workloads.to_float64(o))
+    what = f"B{B} Hq{H_q} Hkv{H_kv} Nq{N_q} Nkv{N_kv} D{D} c{int(causal)} s{scale:.3g}"
+    _check("dQ", dq, rq, what)
+    _check("dK", dk, rk, what)
+    _check("dV", dv, rv, what)
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 4, 4, 128, 128, 128), (2, 8, 2, 300, 300, 128), (1, 4, 1, 257, 257, 64),
+    (1, 6, 2, 100, 100, 128), (1, 8, 8, 64, 64, 64), (1, 3, 3, 200, 200, 128),
+], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_small(ea, shape, causal):
+    _case(ea, *shape, causal, seed=12000 + sum(shape))
+
+
+@pytest.mark.parametrize("N", [1, 2, 31, 33, 65, 129, 1000])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_ragged(ea, N, D, causal):
+    _case(ea, 1, 4, 2, N, N, D, causal, seed=12100 + N + D)
+
+
+@pytest.mark.parametrize("N_q,N_kv", [(1, 777), (64, 500), (100, 1000), (5, 33), (300, 100)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_rectangular(ea, N_q, N_kv, causal):
+    if causal and N_q > N_kv:
+        pytest.skip("causal needs N_q <= N_kv")
+    _case(ea, 1, 8, 2, N_q, N_kv, 128, causal, seed=12200 + N_q + N_kv)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
+def test_backward_scale_values(ea, scale):
+    _case(ea, 1, 4, 2, 150, 150, 128, True, seed=12300, scale=scale)
+
+
+def test_backward_workload_gqa4_b2_n1024(ea):
+    w = workloads.WORKLOADS["gqa4_b2_n1024"]
+    _case(ea, w.B, w.H_q, w.H_kv, w.N, w.N, w.D, w.causal, seed=w.seed)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_chained_with_forward(ea, causal):
+    """This library's forward output and LSE feed its backward."""
+    _case(ea, 2, 8, 2, 333, 333, 128, causal, seed=12400, chained=True)
+    _case(ea, 1, 8, 2, 40, 600, 64, causal, seed=12401, chained=True)
+
+
+def test_backward_identical_keys(ea):
+    """All keys equal: the exact dQ is zero, a total cancellation of terms
+    whose bf16 rounding does not cancel.  dK and dV follow the usual rule; dQ
+    is bounded with the row scale s taken from the reference dQ of the same Q
+    and dO with the original keys, the typical size of those terms."""
+    B, H_q, H_kv, N, D, seed = 1, 4, 2, 130, 128, 12500
+    q, k0, v, dO = _inputs(B, H_q, H_kv, N, N, D, seed)
+    k = k0[:, :, :1].expand_as(k0).contiguous()
+    sc = 1.0 / math.sqrt(D)
+    q64, k64, v64, d64 = (workloads.to_float64(x) for x in (q, k, v, dO))
+    o, lse = _oracle_fwd_outputs(q64, k64, v64, True, sc)
+    o64 = workloads.to_float64(o)
+    dq, dk, dv = _run_bwd(ea, q, k, v, o, dO, lse, True, sc)
+    rq, rk, rv = oracle.attention_backward(q64, k64, v64, d64, is_causal=True, sm_scale=sc, out=o64)
+    _check("dK", dk, rk, "identical keys")
+    _check("dV", dv, rv, "identical keys")
+    rq0, _, _ = oracle.attention_backward(q64, workloads.to_float64(k0), v64, d64, is_causal=True,
+                                          sm_scale=sc, out=o64)
+    rms0 = float(np.sqrt(np.mean(rq0 * rq0)))
+    s_row = np.maximum(np.sqrt(np.mean(rq0 * rq0, axis=-1, keepdims=True)), rms0)
+    err = np.abs(dq.to(torch.float64).numpy() - rq)
+    assert np.all(err <= G_ATOL * s_row), float((err / s_row).max())
+
+
+def test_backward_large_sampled(ea):
+    """Causal GQA-8 N=4096 at full size: dQ of sampled rows, dK/dV of sampled
+    keys of two kv heads, against the oracle's row and key entry points."""
+    w = workloads.WORKLOADS["gqa8_n4096_causal"]
+    q, k, v, dO = _inputs(w.B, w.H_q, w.H_kv, w.N, w.N, w.D, w.seed)
+    dev = _dev()
+    o, lse = ea.fwd(q.to(dev), k.to(dev), v.to(dev), is_causal=True)
+    dq, dk, dv = _run_bwd(ea, q, k, v, o.cpu(), dO, lse.cpu(), True, w.sm_scale)
+    q64, k64, v64, d64, o64 = (workloads.to_float64(x) for x in (q, k, v, dO, o.cpu()))
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 2047, 4094, 4095], rng.choice(w.N, 6, replace=False)]))
+    for h in (0, 37):
+        r = oracle.backward_rows(q64, k64, v64, d64, 0, h, rows, is_causal=True, sm_scale=w.sm_scale,
+                                 out=o64)
+        _check("dQ", dq[0, h, rows], r, f"gqa8 dQ h{h}")
+    keys = np.unique(np.concatenate([[0, 1, 127, 128, 4095], rng.choice(w.N, 5, replace=False)]))
+    for g in (0, 5):
+        rk, rv = oracle.backward_keys(q64, k64, v64, d64, 0, g, keys, is_causal=True,
+                                      sm_scale=w.sm_scale, out=o64)
+        _check("dK", dk[0, g, keys], rk, f"gqa8 dK g{g}")
+        _check("dV", dv[0, g, keys], rv, f"gqa8 dV g{g}")
+
+
+def test_backward_no_query_rows(ea):
+    dev = _dev()
+    q = torch.empty((1, 4, 0, 128), dtype=torch.bfloat16, device=dev)
+    k = torch.randn((1, 2, 50, 128), device=dev).to(torch.bfloat16)
+    lse = torch.empty((1, 4, 0), dtype=torch.float32, device=dev)
+    dq, dk, dv = ea.bwd(q, k, k, q, q, lse, is_causal=True)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_backward_deterministic_and_no_overrun(ea):
+    dev = _dev()
+    q, k, v, dO = (x.to(dev) for x in _inputs(1, 8, 2, 333, 333, 128, 12600))
+    o, lse = ea.fwd(q, k, v, is_causal=True)
+    res = []
+    for _ in range(2):
+        bufs = [torch.full((x.numel() + 4096,), 7.0, dtype=torch.bfloat16, device=dev) for x in (q, k, v)]
+        dq, dk, dv = (b[:x.numel()].view(x.shape) for b, x in zip(bufs, (q, k, v)))
+        need = ea.attn_bwd_workspace_size(1, 8, 333)
+        wb = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device=dev)
+        ea.attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, is_causal=True, workspace=wb[:need])
+        torch.cuda.synchronize()
+        for b, x in zip(bufs, (q, k, v)):
+            assert torch.all(b[x.numel():] == 7.0), "overrun"
+        assert torch.all(wb[need:] == 0x5A), "workspace overrun"
+        res.append([t.clone() for t in (dq, dk, dv)])
+    for a, b in zip(*res):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
