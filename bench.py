@@ -183,6 +183,39 @@ def time_workload(ea, torch, w, steps, warmup):
     return res, (q, k, v, out, lse)
 
 
+def time_backward(ea, torch, w, steps, warmup):
+    """attn_bwd over the whole workload: inputs Q, K, V, a seeded dO and this
+    library's own forward output and LSE, all resident before timing."""
+    dev = torch.device("cuda", 0)
+    q, k, v = workloads.workload_inputs(w)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + 7919)
+    dO = torch.randn(w.q_shape(), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), dO.to(dev)
+    out, lse = ea.fwd_splitkv(qd, kd, vd, is_causal=w.causal, sm_scale=w.sm_scale, n_splits=1)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = torch.empty((max(ea.attn_bwd_workspace_size(w.B, w.H_q, w.Nq), 1),), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        ea.attn_bwd(qd, kd, vd, out, dod, lse, dq, dk, dv, is_causal=w.causal,
+                    sm_scale=w.sm_scale, workspace=ws)
+    for _ in range(warmup):
+        step()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return {"wall_ms_per_step": wall * 1e3 / steps,
+            "event_ms": [s_.elapsed_time(e) for s_, e in zip(starts, ends)]}
+
+
 def sampled_parity(w, q, k, v, out, lse):
     """Part of the CPU-baseline leg: the timed GPU output on sampled rows
     against the oracle on the same bf16 inputs."""
@@ -224,6 +257,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sweep", action="store_true",
                     help="also time every workload and print a table to stderr")
+    ap.add_argument("--backward-sweep", action="store_true",
+                    help="time attn_bwd on the square workloads and print a table to stderr, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 512 MiB three times "
                          "(reference for scaling HBM byte counters) and exit")
@@ -249,6 +284,19 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
+        return
+
+    if args.backward_sweep:
+        # backward FLOPs: the five products of 2*D per visible (query, key) pair
+        # (S recomputed, dP, dV, dK, dQ), i.e. 2.5x the forward's count
+        for name, ww in workloads.WORKLOADS.items():
+            if ww.N_q is not None and name != "chunk_gqa4_q512_n8192":
+                continue
+            r = time_backward(ea, torch, ww, 10, 3)
+            e = float(np.median(r["event_ms"]))
+            tf = 2.5 * ww.flops() / (e * 1e-3) / 1e12
+            log(f"[bwd] {name:24s} median {e:9.4f} ms  min {min(r['event_ms']):9.4f} ms  "
+                f"{tf:8.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:5.1f}%)")
         return
 
     w = workloads.WORKLOADS[args.workload]
