@@ -24,12 +24,15 @@ from .build import LIB_PATH
 
 __all__ = ["attn_fwd", "fwd", "attn_fwd_splitkv", "fwd_splitkv", "attn_splitkv_num_splits",
            "attn_splitkv_workspace_size", "attn_bwd", "bwd", "attn_bwd_workspace_size",
+           "attn_mla_decode", "attn_mla_num_splits", "attn_mla_workspace_size", "mla_absorb_q",
+           "mla_up_project", "mla_decode",
            "attn_status_string", "attn_abi_version",
            "load_library", "AttnError", "EXPORTED_SYMBOLS"]
 
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splitkv", "attn_splitkv_num_splits",
                     "attn_splitkv_workspace_size", "attn_bwd", "attn_bwd_workspace_size",
-                    "attn_status_string", "attn_abi_version")
+                    "attn_mla_decode", "attn_mla_num_splits", "attn_mla_workspace_size",
+                    "mla_absorb_q", "mla_up_project", "attn_status_string", "attn_abi_version")
 
 _lib = None
 
@@ -65,6 +68,18 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int64] * 3
+    lib.attn_mla_decode.restype = ctypes.c_int
+    lib.attn_mla_decode.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p]
+    lib.attn_mla_num_splits.restype = ctypes.c_int64
+    lib.attn_mla_num_splits.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
+    lib.attn_mla_workspace_size.restype = ctypes.c_size_t
+    lib.attn_mla_workspace_size.argtypes = [ctypes.c_int64] * 4
+    lib.mla_absorb_q.restype = ctypes.c_int
+    lib.mla_absorb_q.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 6 + [ctypes.c_void_p]
+    lib.mla_up_project.restype = ctypes.c_int
+    lib.mla_up_project.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 5 + [ctypes.c_void_p]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_abi_version.restype = ctypes.c_int
@@ -268,3 +283,105 @@ def bwd(q, k, v, out, dout, lse, is_causal: bool = False, sm_scale: float | None
     attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, is_causal=is_causal, sm_scale=sm_scale,
              workspace=ws, stream=stream)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- MLA decode
+MLA_DC = 512
+MLA_DR = 64
+
+
+def attn_mla_num_splits(B: int, H: int, S: int, T: int, is_causal: bool = False) -> int:
+    return int(load_library().attn_mla_num_splits(B, H, S, T, int(bool(is_causal))))
+
+
+def attn_mla_workspace_size(B: int, H: int, S: int, n_splits: int) -> int:
+    return int(load_library().attn_mla_workspace_size(B, H, S, n_splits))
+
+
+def attn_mla_decode(q_lat, kv, out_lat, lse, sm_scale: float, is_causal: bool = False,
+                    n_splits: int = 0, workspace=None, stream=None) -> None:
+    """Latent attention core: q_lat [B,H,S,576], kv [B,T,576] -> out_lat [B,H,S,512], lse."""
+    import torch
+    if q_lat.dim() != 4 or kv.dim() != 3:
+        raise ValueError("q_lat must be [B, H, S, 576] and kv [B, T, 576]")
+    B, H, S, W = q_lat.shape
+    T = kv.shape[1]
+    _check_tensor(q_lat, "q_lat", (B, H, S, W), torch.bfloat16)
+    _check_tensor(kv, "kv", (B, T, W), torch.bfloat16)
+    _check_tensor(out_lat, "out_lat", (B, H, S, W - MLA_DR), torch.bfloat16)
+    _check_tensor(lse, "lse", (B, H, S), torch.float32)
+    for name, t in (("kv", kv), ("out_lat", out_lat), ("lse", lse)):
+        if t.device != q_lat.device:
+            raise ValueError(f"{name} is on {t.device}, q_lat on {q_lat.device}")
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != q_lat.device:
+            raise ValueError("workspace must be a tensor on q_lat's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    handle = _stream_handle(stream, q_lat.device)
+    with torch.cuda.device(q_lat.device):
+        st = load_library().attn_mla_decode(q_lat.data_ptr(), kv.data_ptr(), out_lat.data_ptr(),
+                                            lse.data_ptr(), B, H, S, T, W - MLA_DR, MLA_DR,
+                                            float(sm_scale), int(bool(is_causal)), int(n_splits),
+                                            ws_ptr, ws_bytes, handle)
+    if st != 0:
+        raise AttnError(st, attn_status_string(st))
+
+
+def mla_absorb_q(q_nope, q_pe, w_uk, q_lat, stream=None) -> None:
+    """q_lat [B,H,S,576] = [q_nope W_uk[h], q_pe]; w_uk [H, d_nope, 512]."""
+    import torch
+    B, H, S, dn = q_nope.shape
+    _check_tensor(q_nope, "q_nope", (B, H, S, dn), torch.bfloat16)
+    _check_tensor(q_pe, "q_pe", (B, H, S, MLA_DR), torch.bfloat16)
+    _check_tensor(w_uk, "w_uk", (H, dn, MLA_DC), torch.bfloat16)
+    _check_tensor(q_lat, "q_lat", (B, H, S, MLA_DC + MLA_DR), torch.bfloat16)
+    handle = _stream_handle(stream, q_nope.device)
+    with torch.cuda.device(q_nope.device):
+        st = load_library().mla_absorb_q(q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(),
+                                         q_lat.data_ptr(), B, H, S, dn, MLA_DC, MLA_DR, handle)
+    if st != 0:
+        raise AttnError(st, attn_status_string(st))
+
+
+def mla_up_project(out_lat, w_uv, out, stream=None) -> None:
+    """out [B,H,S,d_v] = out_lat W_uv[h]^T; w_uv [H, d_v, 512]."""
+    import torch
+    B, H, S, dc = out_lat.shape
+    d_v = w_uv.shape[1]
+    _check_tensor(out_lat, "out_lat", (B, H, S, MLA_DC), torch.bfloat16)
+    _check_tensor(w_uv, "w_uv", (H, d_v, MLA_DC), torch.bfloat16)
+    _check_tensor(out, "out", (B, H, S, d_v), torch.bfloat16)
+    handle = _stream_handle(stream, out_lat.device)
+    with torch.cuda.device(out_lat.device):
+        st = load_library().mla_up_project(out_lat.data_ptr(), w_uv.data_ptr(), out.data_ptr(),
+                                           B, H, S, MLA_DC, d_v, handle)
+    if st != 0:
+        raise AttnError(st, attn_status_string(st))
+
+
+def mla_decode(q_nope, q_pe, kv, w_uk, w_uv, sm_scale: float | None = None,
+               is_causal: bool = False, n_splits: int = 0, stream=None):
+    """Absorbed MLA decode: allocates the intermediates, returns (out [B,H,S,d_v], lse).
+
+    kv is the latent cache [B, T, 576] = [c_kv, k_pe]; sm_scale defaults to
+    1/sqrt(d_nope + 64)."""
+    import torch
+    B, H, S, dn = q_nope.shape
+    T = kv.shape[1]
+    dev = q_nope.device
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(dn + MLA_DR)
+    q_lat = torch.empty((B, H, S, MLA_DC + MLA_DR), dtype=torch.bfloat16, device=dev)
+    out_lat = torch.empty((B, H, S, MLA_DC), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    out = torch.empty((B, H, S, w_uv.shape[1]), dtype=torch.bfloat16, device=dev)
+    with torch.cuda.device(dev):
+        ns = n_splits if n_splits > 0 else attn_mla_num_splits(B, H, S, T, is_causal)
+    nbytes = attn_mla_workspace_size(B, H, S, max(ns, 1))
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev) if nbytes else None
+    mla_absorb_q(q_nope, q_pe, w_uk, q_lat, stream=stream)
+    attn_mla_decode(q_lat, kv, out_lat, lse, sm_scale, is_causal=is_causal, n_splits=max(ns, 1),
+                    workspace=ws, stream=stream)
+    mla_up_project(out_lat, w_uv, out, stream=stream)
+    return out, lse

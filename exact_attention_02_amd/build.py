@@ -14,8 +14,10 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libea02_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "attn_abi.hip"), os.path.join(CSRC, "attn_bwd.hip")]
+SOURCES = [os.path.join(CSRC, "attn_abi.hip"), os.path.join(CSRC, "attn_bwd.hip"),
+           os.path.join(CSRC, "attn_mla.hip")]
 DEPENDS = [os.path.join(CSRC, "attn_fwd_kernel.hpp"), os.path.join(CSRC, "attn_bwd_kernel.hpp"),
+           os.path.join(CSRC, "attn_mla_kernel.hpp"),
            os.path.join(os.path.dirname(PKG_DIR), "include", "attn.h")]
 
 HIPCC_FLAGS = [

@@ -1,0 +1,211 @@
+// C ABI of the MLA decode path (declared in include/attn.h): the latent
+// attention core with its key split and merge, the query absorption and the
+// value up-projection.  The library allocates nothing and never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cfloat>
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "attn_mla_kernel.hpp"
+
+namespace {
+
+using ea02::MlaParams;
+using ea02::MlaProjParams;
+constexpr int kMlaP = 3;
+constexpr int kMlaMaxSplits = 256;
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+bool mis16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+
+size_t mla_ws_bytes(int64_t B, int64_t H, int64_t S, int64_t n_splits) {
+  if (n_splits <= 1) return 0;
+  return size_t(n_splits) * size_t(B * H * S) * size_t(ea02::kMlaDc + 1) * 4;
+}
+
+// size checks shared by the core's entry points
+int mla_check_sizes(int64_t B, int64_t H, int64_t S, int64_t T, int64_t d_c, int64_t d_r, int is_causal,
+                    int64_t n_splits) {
+  if (B < 0 || H < 0 || S < 0 || T < 0 || d_c < 0 || d_r < 0 || n_splits < 0) return ATTN_ERR_NEGATIVE_SIZE;
+  if (d_c != ea02::kMlaDc || d_r != ea02::kMlaDr) return ATTN_ERR_HEAD_DIM;
+  if (is_causal != 0 && is_causal != 1) return ATTN_ERR_CAUSAL_FLAG;
+  if (n_splits > kMlaMaxSplits) return ATTN_ERR_SPLITS;
+  if (is_causal && S > T) return ATTN_ERR_CAUSAL_SHAPE;
+  if (B > (1 << 24) || H > (1 << 16) || S > (1 << 24) || T * ea02::kMlaRowBytes > (int64_t(1) << 31) ||
+      S * H > (int64_t(1) << 30) || B * H * S > INT32_MAX)
+    return ATTN_ERR_SIZE_OVERFLOW;
+  const int64_t pbs = (S * H + 31) / 32;
+  if (pbs * B * std::max<int64_t>(n_splits, 1) > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
+  return ATTN_OK;
+}
+
+int64_t mla_choose_splits(int64_t B, int64_t H, int64_t S, int64_t T) {
+  const int64_t wgs = ((S * H + 31) / 32) * B;
+  const int64_t cus = device_cus();
+  if (wgs <= 0 || wgs >= cus) return 1;
+  const int64_t tiles = (T + 31) / 32;
+  int64_t n = (cus + wgs - 1) / wgs;
+  n = std::min<int64_t>(n, tiles / 4);
+  n = std::min<int64_t>(n, kMlaMaxSplits);
+  return n < 1 ? 1 : n;
+}
+
+}  // namespace
+
+extern "C" int64_t attn_mla_num_splits(int64_t B, int64_t H, int64_t S, int64_t T, int is_causal) {
+  if (mla_check_sizes(B, H, S, T, ea02::kMlaDc, ea02::kMlaDr, is_causal, 0) != ATTN_OK) return -1;
+  if (B == 0 || H == 0 || S == 0) return 1;
+  return mla_choose_splits(B, H, S, T);
+}
+
+extern "C" size_t attn_mla_workspace_size(int64_t B, int64_t H, int64_t S, int64_t n_splits) {
+  if (B < 0 || H < 0 || S < 0 || n_splits < 0 || n_splits > kMlaMaxSplits) return 0;
+  return mla_ws_bytes(B, H, S, n_splits);
+}
+
+extern "C" int attn_mla_decode(const void* q_lat, const void* kv, void* out_lat, float* lse, int64_t B, int64_t H,
+                               int64_t S, int64_t T, int64_t d_c, int64_t d_r, float sm_scale, int is_causal,
+                               int64_t n_splits, void* workspace, size_t workspace_size, void* stream) {
+  int st = mla_check_sizes(B, H, S, T, d_c, d_r, is_causal, n_splits);
+  if (st != ATTN_OK) return st;
+  if (!std::isfinite(sm_scale)) return ATTN_ERR_SCALE;
+  if (B == 0 || H == 0 || S == 0) return ATTN_OK;
+  if (T == 0) return ATTN_ERR_NO_KEYS;
+  if (!q_lat || !kv || !out_lat || !lse) return ATTN_ERR_NULL_POINTER;
+  if (mis16(q_lat) || mis16(kv) || mis16(out_lat) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return ATTN_ERR_ALIGNMENT;
+  const int64_t ns = n_splits == 0 ? mla_choose_splits(B, H, S, T) : n_splits;
+  const size_t need = mla_ws_bytes(B, H, S, ns);
+  if (need > 0 && (!workspace || workspace_size < need || mis16(workspace))) return ATTN_ERR_WORKSPACE;
+  const size_t nq = size_t(B * H * S) * ea02::kMlaDqk * 2, nkv = size_t(B * T) * ea02::kMlaDqk * 2;
+  const size_t no = size_t(B * H * S) * ea02::kMlaDc * 2, nl = size_t(B * H * S) * 4;
+  if (overlaps(out_lat, no, q_lat, nq) || overlaps(out_lat, no, kv, nkv) || overlaps(lse, nl, q_lat, nq) ||
+      overlaps(lse, nl, kv, nkv) || overlaps(out_lat, no, lse, nl) || overlaps(workspace, need, q_lat, nq) ||
+      overlaps(workspace, need, kv, nkv) || overlaps(workspace, need, out_lat, no) ||
+      overlaps(workspace, need, lse, nl))
+    return ATTN_ERR_ALIAS;
+
+  const bool split = ns > 1;
+  const int64_t rows = B * H * S;
+  MlaParams p;
+  p.q = static_cast<const uint16_t*>(q_lat);
+  p.kv = static_cast<const uint16_t*>(kv);
+  p.o = static_cast<uint16_t*>(out_lat);
+  p.lse = lse;
+  p.o_part = split ? static_cast<float*>(workspace) : nullptr;
+  p.lse_part = split ? static_cast<float*>(workspace) + size_t(ns) * size_t(rows) * ea02::kMlaDc : nullptr;
+  p.B = static_cast<int>(B);
+  p.H = static_cast<int>(H);
+  p.S = static_cast<int>(S);
+  p.T = static_cast<int>(T);
+  p.n_pairs = static_cast<int>(S * H);
+  p.causal_off = is_causal ? static_cast<int>(T - S) : 0;
+  p.n_pair_blocks = static_cast<int>((S * H + 31) / 32);
+  p.n_splits = split ? static_cast<int>(ns) : 1;
+  p.scale_log2 = std::fmax(std::fabs(sm_scale) * ea02::kLog2e, FLT_MIN);
+  p.q_sign = (sm_scale < 0.f) ? 0x80008000u : 0u;
+  p.causal = is_causal;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(int64_t(p.n_pair_blocks) * B * p.n_splits));
+  if (split)
+    hipLaunchKernelGGL((ea02::attn_mla_kernel<kMlaP, true>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((ea02::attn_mla_kernel<kMlaP, false>), grid, dim3(256), 0, s, p);
+  if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+  if (split) {
+    ea02::MergeParams m;
+    m.o_part = p.o_part;
+    m.lse_part = p.lse_part;
+    m.o = p.o;
+    m.lse = p.lse;
+    m.rows = rows;
+    m.n_splits = p.n_splits;
+    // 128 threads per row (4 of the 512 values each) times 2 or 8 split lanes
+    if (m.n_splits <= ea02::kMergeBatch * 2)
+      hipLaunchKernelGGL((ea02::attn_merge_kernel<ea02::kMlaDc, 256>), dim3(static_cast<unsigned>(rows)), dim3(256),
+                         0, s, m);
+    else
+      hipLaunchKernelGGL((ea02::attn_merge_kernel<ea02::kMlaDc, 1024>), dim3(static_cast<unsigned>(rows)),
+                         dim3(1024), 0, s, m);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
+extern "C" int mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_uk, void* q_lat, int64_t B,
+                            int64_t H, int64_t S, int64_t d_nope, int64_t d_c, int64_t d_r, void* stream) {
+  if (B < 0 || H < 0 || S < 0 || d_nope < 0 || d_c < 0 || d_r < 0) return ATTN_ERR_NEGATIVE_SIZE;
+  if (d_c != ea02::kMlaDc || d_r != ea02::kMlaDr || d_nope < 1 || d_nope > 256) return ATTN_ERR_HEAD_DIM;
+  if (B > (1 << 24) || H > (1 << 16) || S > (1 << 24) || B * S > INT32_MAX / 2 || B * H * S > INT32_MAX)
+    return ATTN_ERR_SIZE_OVERFLOW;
+  const int64_t groups = (B * S + ea02::kProjRows - 1) / ea02::kProjRows;
+  if (groups * H > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
+  if (B == 0 || H == 0 || S == 0) return ATTN_OK;
+  if (!q_nope || !q_pe || !w_uk || !q_lat) return ATTN_ERR_NULL_POINTER;
+  if ((reinterpret_cast<uintptr_t>(q_nope) & 1u) || (reinterpret_cast<uintptr_t>(q_pe) & 3u) ||
+      (reinterpret_cast<uintptr_t>(w_uk) & 3u) || (reinterpret_cast<uintptr_t>(q_lat) & 3u))
+    return ATTN_ERR_ALIGNMENT;
+  const size_t nn = size_t(B * H * S * d_nope) * 2, npe = size_t(B * H * S) * ea02::kMlaDr * 2;
+  const size_t nw = size_t(H * d_nope) * ea02::kMlaDc * 2, nout = size_t(B * H * S) * ea02::kMlaDqk * 2;
+  if (overlaps(q_lat, nout, q_nope, nn) || overlaps(q_lat, nout, q_pe, npe) || overlaps(q_lat, nout, w_uk, nw))
+    return ATTN_ERR_ALIAS;
+  MlaProjParams p;
+  p.x = static_cast<const uint16_t*>(q_nope);
+  p.x2 = static_cast<const uint16_t*>(q_pe);
+  p.w = static_cast<const uint16_t*>(w_uk);
+  p.y = static_cast<uint16_t*>(q_lat);
+  p.B = static_cast<int>(B);
+  p.H = static_cast<int>(H);
+  p.S = static_cast<int>(S);
+  p.d_n = static_cast<int>(d_nope);
+  p.rows_per_head = static_cast<int>(B * S);
+  hipLaunchKernelGGL(ea02::mla_absorb_kernel, dim3(static_cast<unsigned>(groups * H)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), p);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+extern "C" int mla_up_project(const void* out_lat, const void* w_uv, void* out, int64_t B, int64_t H, int64_t S,
+                              int64_t d_c, int64_t d_v, void* stream) {
+  if (B < 0 || H < 0 || S < 0 || d_c < 0 || d_v < 0) return ATTN_ERR_NEGATIVE_SIZE;
+  if (d_c != ea02::kMlaDc || d_v < 32 || d_v > 1024 || d_v % 32 != 0) return ATTN_ERR_HEAD_DIM;
+  if (B > (1 << 24) || H > (1 << 16) || S > (1 << 24) || B * S > INT32_MAX / 2 || B * H * S > INT32_MAX)
+    return ATTN_ERR_SIZE_OVERFLOW;
+  const int64_t blocks = (B * S + 31) / 32 * H * (d_v / 32);
+  if (blocks > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
+  if (B == 0 || H == 0 || S == 0) return ATTN_OK;
+  if (!out_lat || !w_uv || !out) return ATTN_ERR_NULL_POINTER;
+  if (mis16(out_lat) || mis16(w_uv) || (reinterpret_cast<uintptr_t>(out) & 1u)) return ATTN_ERR_ALIGNMENT;
+  const size_t nx = size_t(B * H * S) * ea02::kMlaDc * 2, nw = size_t(H * d_v) * ea02::kMlaDc * 2;
+  const size_t ny = size_t(B * H * S * d_v) * 2;
+  if (overlaps(out, ny, out_lat, nx) || overlaps(out, ny, w_uv, nw)) return ATTN_ERR_ALIAS;
+  MlaProjParams p;
+  p.x = static_cast<const uint16_t*>(out_lat);
+  p.x2 = nullptr;
+  p.w = static_cast<const uint16_t*>(w_uv);
+  p.y = static_cast<uint16_t*>(out);
+  p.B = static_cast<int>(B);
+  p.H = static_cast<int>(H);
+  p.S = static_cast<int>(S);
+  p.d_n = static_cast<int>(d_v);
+  p.rows_per_head = static_cast<int>(B * S);
+  hipLaunchKernelGGL(ea02::mla_up_kernel, dim3(static_cast<unsigned>(blocks)), dim3(64), 0,
+                     static_cast<hipStream_t>(stream), p);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}

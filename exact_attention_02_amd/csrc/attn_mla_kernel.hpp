@@ -1,0 +1,371 @@
+// Multi-head latent attention (MLA) decode for gfx950: device code.
+//
+// Method (page "Attention Kernel 实现与正确性验证", section 2: 2.1 the
+// absorption trick, 2.2 the reference with naive and absorbed forms, 2.3 the
+// DeepSeek-V3 shapes, 2.4 FlashMLA decode with a split of the cache axis and
+// a safe-softmax merge).  With W_uk absorbed into the query, every head
+// attends over the same latent cache row kv = [c_kv (512), k_pe (64)]:
+//   q_lat = [q_nope W_uk[h], q_pe]                     (mla_absorb_kernel)
+//   out_lat = softmax(scale q_lat kv^T) c_kv           (attn_mla_kernel)
+//   out = out_lat W_uv[h]^T                            (mla_up_kernel)
+//
+// attn_mla_kernel: MQA with 576-wide scores and 512-wide values.  A workgroup
+// owns 32 (query token, head) pairs and streams 32-key tiles of the latent
+// cache through a 3-stage LDS ring.  Its four waves split the work two ways:
+//  * scores: wave w takes 9 of the 36 k-steps (16 dims each) of S^T = K Q^T
+//    for all 32 keys and pairs; the four fp32 partials meet in LDS and every
+//    wave sums them in the same order, so all waves hold the same S^T and
+//    take the same online-softmax decisions (lazy rescale, as in the
+//    forward kernel);
+//  * values: wave w accumulates O^T for dims [128 w, 128 w + 128) with
+//    O^T += V^T P^T, V^T from the LDS transpose read of the tile's first 512
+//    columns and P^T the bf16-rounded S^T accumulator.
+// The query fragments of a wave are only its 9 k-steps and its accumulator
+// only 128 dims, which is what makes 576/512-wide heads fit in registers.
+#pragma once
+
+#include "attn_fwd_kernel.hpp"
+
+namespace ea02 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMlaDc = 512;                 // latent (value) width
+constexpr int kMlaDr = 64;                  // rotary width
+constexpr int kMlaDqk = kMlaDc + kMlaDr;    // score width
+constexpr int kMlaRowBytes = kMlaDqk * 2;   // 1152
+constexpr int kMlaChunks = kMlaRowBytes / 16;  // 72
+
+struct MlaParams {
+  const uint16_t* q;   // [B, H, S, 576] bf16 (absorbed query)
+  const uint16_t* kv;  // [B, T, 576] bf16 latent cache
+  uint16_t* o;         // [B, H, S, 512] bf16 (single pass)
+  float* lse;          // [B, H, S] natural log (single pass)
+  float* o_part;       // [n_splits, B*H*S, 512] fp32 (split pass)
+  float* lse_part;     // [n_splits, B*H*S] log2 units (split pass)
+  int B, H, S, T;
+  int n_pairs;         // S * H
+  int causal_off;      // T - S when causal, else 0
+  int n_pair_blocks;   // ceil(n_pairs / 32)
+  int n_splits;
+  float scale_log2;    // max(|sm_scale| log2 e, FLT_MIN)
+  uint32_t q_sign;     // 0x80008000 when sm_scale < 0
+  int causal;
+};
+
+// Chunk swizzle of a 1152-byte latent row (72 chunks: XOR values below 8 keep
+// a chunk inside its aligned group of 8).  Rows 1152 bytes apart alternate
+// between two bank halves, so 16 rows read at one chunk need distinct XORs
+// per row parity; the transpose read (4 rows x 4 chunks per half wave) needs
+// rows r and r+2 in different 4-chunk halves.
+__device__ __forceinline__ int mla_swz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
+
+template <int P, bool SPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void attn_mla_kernel(MlaParams p) {
+  constexpr int NW = 4;
+  constexpr int BN = 32;
+  constexpr int TILE_BYTES = BN * kMlaRowBytes;          // 36 KiB
+  constexpr int LOADS = TILE_BYTES / 1024;               // 36
+  constexpr int LPW = LOADS / NW;                        // 9
+  constexpr int KSW = kMlaDqk / 16 / NW;                 // 9 k-steps per wave
+  constexpr int DVW = kMlaDc / NW;                       // 128 value dims per wave
+  constexpr int PART_BYTES = NW * 64 * 16 * 4;           // S^T partials, 16 KiB
+  static_assert(LOADS % NW == 0 && (P - 1) * LPW <= 63, "load groups");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[P * TILE_BYTES + PART_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // pair blocks of one (batch, split) are B * n_splits apart in the grid so
+  // that they share an XCD (and its L2) under round-robin dispatch
+  const int bid = blockIdx.x;
+  const int bs = bid % (p.B * p.n_splits);
+  const int pb = bid / (p.B * p.n_splits);
+  const int b = bs / p.n_splits;
+  const int split = SPLIT ? bs % p.n_splits : 0;
+  const int T = p.T;
+  const int off = p.causal_off;
+  const int last_pair = p.n_pairs - 1;
+  const int P0 = pb * 32;
+  const int row0 = min(P0, last_pair) / p.H;                 // first query token of the block
+  const int row_end = min(P0 + 31, last_pair) / p.H + 1;
+
+  const int kv_end = p.causal ? min(row_end + off, T) : T;
+  int n_tiles = (kv_end + BN - 1) / BN;
+  int kbase = 0;
+  if constexpr (SPLIT) {
+    const int per = (n_tiles + p.n_splits - 1) / p.n_splits;
+    const int t0 = min(split * per, n_tiles);
+    n_tiles = min(per, n_tiles - t0);
+    kbase = t0 * BN;
+  }
+
+  // this lane's pair and its 9 query k-steps (B operands of S^T = K Q^T)
+  const int pair = P0 + col;
+  const bool valid = pair <= last_pair;
+  const int pc = min(pair, last_pair);
+  const int my_row = pc / p.H;
+  const int h = pc - my_row * p.H;
+  const size_t bhr = ((size_t)b * p.H + h) * (size_t)p.S + my_row;
+  bf16x8 qf[KSW];
+#pragma unroll
+  for (int i = 0; i < KSW; ++i) {
+    u32x4 x = *reinterpret_cast<const u32x4*>(p.q + bhr * kMlaDqk + (wave * KSW + i) * 16 + half * 8);
+    x ^= p.q_sign;
+    qf[i] = as_bf16x8(x);
+  }
+
+  // tile loads: load li moves bytes [1024 li, 1024 li + 1024) of the tile,
+  // lane -> (row, stored chunk j) and fetches chunk j ^ swz(row) of that row
+  const u32x4 rsrc = make_rsrc(p.kv + (size_t)b * T * kMlaDqk, (uint32_t)((size_t)T * kMlaRowBytes));
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
+  int ld_row[LPW], ld_off[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int e = (wave * LPW + i) * 64 + lane;
+    ld_row[i] = e / kMlaChunks;
+    const int j = e - ld_row[i] * kMlaChunks;
+    ld_off[i] = (j ^ mla_swz(ld_row[i])) << 4;
+  }
+  auto issue = [&](int t, int slot) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int key = min(kbase + t * BN + ld_row[i], T - 1);
+      dma_16B(rsrc, key * kMlaRowBytes + ld_off[i], lds_base + slot * TILE_BYTES + (wave * LPW + i) * 1024);
+    }
+  };
+
+  // V^T transpose-read offsets: rows 16 st + 4 half + L/4 (+8), dims
+  // 128 wave + 32 db + 16 (G16 & 1) + 4 (L & 3); independent of st
+  const int L16 = lane & 15;
+  int tr_off[2][DVW / 32];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int db = 0; db < DVW / 32; ++db) {
+      const int row = 4 * half + (L16 >> 2) + 8 * hi;
+      const int d = wave * DVW + db * 32 + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
+      tr_off[hi][db] = row * kMlaRowBytes + (((d >> 3) ^ mla_swz(row)) << 4) + (d & 7) * 2;
+    }
+
+  float* part = reinterpret_cast<float*>(lds + P * TILE_BYTES);
+  f32x16 acc[DVW / 32];
+#pragma unroll
+  for (int db = 0; db < DVW / 32; ++db) acc[db] = f32x16{};
+  float m_used = -INFINITY, l_run = 0.f;
+  const float sl2 = p.scale_log2;
+
+  auto compute = [&](int t, int slot) {
+    const uint8_t* kt = lds + slot * TILE_BYTES;
+    // partial S^T over this wave's k-steps; element r holds key
+    // 8(r/4) + 4 half + r%4 of the tile for this lane's pair
+    f32x16 sp = f32x16{};
+#pragma unroll
+    for (int i = 0; i < KSW; ++i) {
+      const int chunk = (2 * (wave * KSW + i) + half) ^ mla_swz(col);
+      const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + col * kMlaRowBytes + (chunk << 4)));
+      sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[i], sp, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<f32x4*>(part + ((wave * 64 + lane) * 16 + 4 * r4)) =
+          f32x4{sp[4 * r4], sp[4 * r4 + 1], sp[4 * r4 + 2], sp[4 * r4 + 3]};
+    __syncthreads();
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(part + ((w * 64 + lane) * 16 + 4 * r4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * r4 + e] += x[e];
+      }
+    // mask: causal diagonal or the ragged end of the cache
+    const int key0 = kbase + t * BN;
+    if ((p.causal && key0 + BN - 1 > row0 + off) || key0 + BN > T) {
+      const int lim = (p.causal ? min(my_row + off + 1, T) : T) - key0 - 4 * half;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    const float mt = half_swap_max(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mt > m_used + kRescaleSlack)) {
+      const float m_new = fmaxf(m_used, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DVW / 32; ++db) acc[db] *= alpha;
+      m_used = m_new;
+    }
+    const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
+    f32x8 pf;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -m_sub));
+      pf[r & 7] = pe;
+      l_run += pe;
+      if ((r & 7) == 7) pb[r >> 3] = __builtin_convertvector(pf, bf16x8);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < DVW / 32; ++db) {
+        const uint8_t* a = kt + (16 * st) * kMlaRowBytes;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[0][db]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[1][db]));
+        const bf16x8 vT = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vT, pb[st], acc[db], 0, 0, 0);
+      }
+  };
+
+  // load ring as in the backward kernels: tile t in slot t % P, issued P-1
+  // tiles ahead, clamped re-loads past the end keep one constant vmcnt
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int j = 0; j < P - 1; ++j) issue(min(j, n_tiles - 1), j);
+    for (int t = 0; t < n_tiles; ++t) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 2) * LPW) : "memory");
+      __syncthreads();  // tile t landed; every wave is done with tile t-1 and the partials
+      issue(min(t + P - 1, n_tiles - 1), (t + P - 1) % P);
+      compute(t, t % P);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  const float l_tot = half_swap_sum(l_run);
+  if (!valid) return;
+  if constexpr (!SPLIT) {
+    const float inv = 1.f / l_tot;
+    uint16_t* orow = p.o + bhr * kMlaDc + wave * DVW;
+#pragma unroll
+    for (int db = 0; db < DVW / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * half;
+        f32x4 f = {acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv, acc[db][4 * g4 + 2] * inv,
+                   acc[db][4 * g4 + 3] * inv};
+        *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4));
+      }
+    if (wave == 0 && half == 0) p.lse[bhr] = (m_used + __log2f(l_tot)) * kLn2;
+  } else {
+    const bool seen = l_tot > 0.f;
+    const float inv = seen ? 1.f / l_tot : 0.f;
+    const size_t slot = (size_t)split * ((size_t)p.B * p.H * p.S) + bhr;
+    float* orow = p.o_part + slot * kMlaDc + wave * DVW;
+#pragma unroll
+    for (int db = 0; db < DVW / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * half;
+        *reinterpret_cast<f32x4*>(orow + d0) = f32x4{acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv,
+                                                     acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv};
+      }
+    if (wave == 0 && half == 0) p.lse_part[slot] = seen ? m_used + __log2f(l_tot) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------- projections
+// q_lat[r, c] = sum_d q_nope[r, d] W_uk[h, d, c] for the rows r of head h,
+// q_lat[r, 512 + e] = q_pe[r, e].  One block per (head, group of up to 32 rows
+// of that head); thread t owns columns 2t, 2t+1 and reads W_uk[h, d, :] rows
+// coalesced; the rows' q_nope values are staged in LDS.
+struct MlaProjParams {
+  const uint16_t* x;    // absorb: q_nope [B, H, S, d_n];  up: out_lat [B, H, S, 512]
+  const uint16_t* x2;   // absorb: q_pe [B, H, S, 64]
+  const uint16_t* w;    // absorb: W_uk [H, d_n, 512];     up: W_uv [H, d_v, 512]
+  uint16_t* y;          // absorb: q_lat [B, H, S, 576];   up: out [B, H, S, d_v]
+  int B, H, S, d_n;     // d_n: d_nope (absorb) or d_v (up)
+  int rows_per_head;    // B * S
+};
+
+constexpr int kProjRows = 32;
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 4)))
+void mla_absorb_kernel(MlaProjParams p) {
+  __shared__ float xs[kProjRows][256];
+  const int h = blockIdx.x % p.H;
+  const int r0 = (blockIdx.x / p.H) * kProjRows;
+  const int nr = min(kProjRows, p.rows_per_head - r0);
+  const int t = threadIdx.x;
+  // row r of head h is (b, s) = (r / S, r % S)
+  for (int i = t; i < nr * p.d_n; i += 256) {
+    const int r = i / p.d_n, d = i - r * p.d_n;
+    const int rr = r0 + r;
+    const size_t row = ((size_t)(rr / p.S) * p.H + h) * p.S + (rr % p.S);
+    xs[r][d] = (float)__builtin_bit_cast(__bf16, p.x[row * p.d_n + d]);
+  }
+  __syncthreads();
+  float acc[kProjRows][2];
+#pragma unroll
+  for (int r = 0; r < kProjRows; ++r) acc[r][0] = acc[r][1] = 0.f;
+  const uint16_t* wh = p.w + (size_t)h * p.d_n * kMlaDc + 2 * t;
+  for (int d = 0; d < p.d_n; ++d) {
+    const uint32_t wv = *reinterpret_cast<const uint32_t*>(wh + (size_t)d * kMlaDc);
+    const float w0 = __uint_as_float(wv << 16), w1 = __uint_as_float(wv & 0xffff0000u);
+#pragma unroll
+    for (int r = 0; r < kProjRows; ++r) {
+      acc[r][0] = __builtin_fmaf(xs[r][d], w0, acc[r][0]);
+      acc[r][1] = __builtin_fmaf(xs[r][d], w1, acc[r][1]);
+    }
+  }
+  // (a fully unrolled loop with a guard, so that acc stays in registers)
+#pragma unroll
+  for (int r = 0; r < kProjRows; ++r) {
+    if (r < nr) {
+      const int rr = r0 + r;
+      const size_t row = ((size_t)(rr / p.S) * p.H + h) * p.S + (rr % p.S);
+      const bf16x2 v = __builtin_convertvector(f32x2{acc[r][0], acc[r][1]}, bf16x2);
+      *reinterpret_cast<uint32_t*>(p.y + row * kMlaDqk + 2 * t) = __builtin_bit_cast(uint32_t, v);
+      if (t < kMlaDr / 2)
+        *reinterpret_cast<uint32_t*>(p.y + row * kMlaDqk + kMlaDc + 2 * t) =
+            *reinterpret_cast<const uint32_t*>(p.x2 + row * kMlaDr + 2 * t);
+    }
+  }
+}
+
+// out[r, v] = sum_c out_lat[r, c] W_uv[h, v, c]: one wave per (head, 32
+// values of v, 32 rows of that head) computes the 32 x 32 block with MFMA,
+// A = out_lat rows and B^T = W_uv rows, both read as 16-byte fragments
+// straight from global memory (their contiguous dimension is c, the
+// contraction).  Rows past the head's last one are clamped and not stored.
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void mla_up_kernel(MlaProjParams p) {
+  const int lane = threadIdx.x;
+  const int half = lane >> 5, col = lane & 31;
+  const int n_vb = p.d_n / 32;
+  int bid = blockIdx.x;
+  const int vb = bid % n_vb;
+  bid /= n_vb;
+  const int h = bid % p.H;
+  const int r0 = (bid / p.H) * 32;
+  // A: row r0 + col of head h; B: W_uv[h, 32 vb + col, :]
+  const int rr = min(r0 + col, p.rows_per_head - 1);
+  const size_t arow = ((size_t)(rr / p.S) * p.H + h) * p.S + (rr % p.S);
+  const uint16_t* a = p.x + arow * kMlaDc + half * 8;
+  const uint16_t* w = p.w + ((size_t)h * p.d_n + 32 * vb + col) * kMlaDc + half * 8;
+  f32x16 acc = f32x16{};
+#pragma unroll 8
+  for (int ks = 0; ks < kMlaDc / 16; ++ks) {
+    const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(a + ks * 16));
+    const bf16x8 bv = as_bf16x8(*reinterpret_cast<const u32x4*>(w + ks * 16));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  }
+  // element r holds row r0 + 8(r/4) + 4 half + r%4 and v = 32 vb + col
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int rowi = r0 + 8 * (r >> 2) + 4 * half + (r & 3);
+    if (rowi < p.rows_per_head) {
+      const size_t orow = ((size_t)(rowi / p.S) * p.H + h) * p.S + (rowi % p.S);
+      p.y[orow * p.d_n + 32 * vb + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[r]);
+    }
+  }
+}
+
+}  // namespace ea02

@@ -1,6 +1,6 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) fused attention library (forward,
- * split-KV forward and decode, backward).
+ * split-KV forward and decode, backward, MLA decode).
  *
  * The operation is the forward pass of exact scaled-dot-product attention in
  * the FlashAttention-2 style: one query tile stays on chip while key/value
@@ -202,10 +202,79 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
  * B * H_q * N_q * 8 (0 for negative sizes). */
 size_t attn_bwd_workspace_size(int64_t B, int64_t H_q, int64_t N_q);
 
+/*
+ * Multi-head latent attention (MLA) decode, absorbed form.  Page "Attention
+ * Kernel 实现与正确性验证", section 2: with the key up-projection W_uk folded
+ * into the query (2.1), every head scores against the same latent cache row
+ * kv = [c_kv (512), k_pe (64)] and takes c_kv as its values; the value
+ * up-projection W_uv is applied to the latent output (2.2).  Shapes are the
+ * DeepSeek-V3 ones of 2.3 (d_c = 512, d_R = 64); the cache axis may be split
+ * with a safe-softmax merge as in 2.4.  Three steps, three entry points:
+ *
+ *   mla_absorb_q:    q_lat[b,h,s] = [q_nope[b,h,s] W_uk[h], q_pe[b,h,s]]
+ *   attn_mla_decode: out_lat[b,h,s] = softmax_j(sm_scale q_lat[b,h,s] . kv[b,j]) c_kv[b,j]
+ *                    lse[b,h,s] = log sum_j exp(sm_scale q_lat[b,h,s] . kv[b,j])
+ *   mla_up_project:  out[b,h,s] = out_lat[b,h,s] W_uv[h]^T
+ *
+ * For S > 1 query tokens, is_causal masks bottom-right: token s sees cache
+ * positions j <= s + T - S.  The page scales scores by 1/sqrt(d_nope + d_R).
+ * All tensors are contiguous bf16 device memory (lse fp32), row-major with
+ * the last dimension fastest; products accumulate in fp32 and round to bf16
+ * (nearest even) when stored.
+ */
+
+/*
+ * attn_mla_decode -- the latent attention core.
+ *   q_lat   [B, H, S, d_c + d_r]   kv   [B, T, d_c + d_r]
+ *   out_lat [B, H, S, d_c] (written)   lse  [B, H, S] fp32 (written)
+ *   d_c must be 512 and d_r 64.  n_splits, workspace: as attn_fwd_splitkv
+ *   (0 = attn_mla_num_splits, 1 = one pass without workspace, at most 256;
+ *   workspace of attn_mla_workspace_size bytes, 16-byte aligned).
+ * Errors, in this order: NEGATIVE_SIZE, HEAD_DIM (d_c, d_r), CAUSAL_FLAG,
+ * SPLITS, CAUSAL_SHAPE (S > T), SIZE_OVERFLOW (T * 1152 > 2^31, B*H*S >=
+ * 2^31, ...), SCALE, then empty work (B, H or S = 0) returns ATTN_OK, then
+ * NO_KEYS (T = 0), NULL_POINTER, ALIGNMENT (16 bytes, lse 4), WORKSPACE,
+ * ALIAS, LAUNCH.  Two kernels are enqueued when the split count is above 1.
+ */
+int attn_mla_decode(const void* q_lat, const void* kv, void* out_lat, float* lse, int64_t B,
+                    int64_t H, int64_t S, int64_t T, int64_t d_c, int64_t d_r, float sm_scale,
+                    int is_causal, int64_t n_splits, void* workspace, size_t workspace_size,
+                    void* stream);
+
+/* Split count attn_mla_decode picks for n_splits = 0 on the current device
+ * (1 when the unsplit grid has a workgroup per CU; else about one per CU,
+ * at least four 32-key tiles per split); -1 for sizes it would reject. */
+int64_t attn_mla_num_splits(int64_t B, int64_t H, int64_t S, int64_t T, int is_causal);
+
+/* Workspace bytes of attn_mla_decode: 0 when n_splits <= 1, else
+ * n_splits * B * H * S * (512 + 1) * 4.  0 for invalid sizes. */
+size_t attn_mla_workspace_size(int64_t B, int64_t H, int64_t S, int64_t n_splits);
+
+/*
+ * mla_absorb_q -- q_lat = [q_nope W_uk[h], q_pe] per head.
+ *   q_nope [B, H, S, d_nope] (1 <= d_nope <= 256), q_pe [B, H, S, d_r],
+ *   w_uk [H, d_nope, d_c], q_lat [B, H, S, d_c + d_r] (written); d_c = 512,
+ *   d_r = 64.  Errors: NEGATIVE_SIZE, HEAD_DIM, SIZE_OVERFLOW, empty work ->
+ *   ATTN_OK, NULL_POINTER, ALIGNMENT (q_nope 2 bytes, others 4), ALIAS, LAUNCH.
+ */
+int mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_uk, void* q_lat, int64_t B,
+                 int64_t H, int64_t S, int64_t d_nope, int64_t d_c, int64_t d_r, void* stream);
+
+/*
+ * mla_up_project -- out = out_lat W_uv[h]^T per head.
+ *   out_lat [B, H, S, d_c], w_uv [H, d_v, d_c], out [B, H, S, d_v] (written);
+ *   d_c = 512, d_v a multiple of 32 in [32, 1024].  Errors: NEGATIVE_SIZE,
+ *   HEAD_DIM, SIZE_OVERFLOW, empty work -> ATTN_OK, NULL_POINTER, ALIGNMENT
+ *   (out_lat and w_uv 16 bytes, out 2), ALIAS, LAUNCH.
+ */
+int mla_up_project(const void* out_lat, const void* w_uv, void* out, int64_t B, int64_t H,
+                   int64_t S, int64_t d_c, int64_t d_v, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);
 
-/* Library ABI version, currently 3 (1: attn_fwd; 2: + split-KV; 3: + backward). */
+/* Library ABI version, currently 4 (1: attn_fwd; 2: + split-KV; 3: + backward;
+ * 4: + MLA decode). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

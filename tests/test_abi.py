@@ -38,7 +38,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
 
 
 def test_status_strings_distinct(lib):
@@ -258,3 +258,58 @@ def test_bwd_workspace_size():
     assert ea.attn_bwd_workspace_size(2, 32, 1024) == 2 * 32 * 1024 * 8
     assert ea.attn_bwd_workspace_size(1, 4, 0) == 0
     assert ea.attn_bwd_workspace_size(-1, 4, 4) == 0
+
+
+# ------------------------------------------------------------ MLA entries
+QL, KVC, OL, LL, WM = (0x300000000 + i * 64 * MiB for i in range(5))
+
+
+def call_mla(lib, q=QL, kv=KVC, o=OL, l=LL, B=1, H=16, S=1, T=100, d_c=512, d_r=64, scale=0.07,
+             causal=1, n_splits=4, ws=WM, ws_bytes=64 * MiB):
+    return lib.attn_mla_decode(q, kv, o, l, B, H, S, T, d_c, d_r, ctypes.c_float(scale), causal,
+                               n_splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), "ATTN_ERR_NEGATIVE_SIZE"),
+    (dict(d_c=256), "ATTN_ERR_HEAD_DIM"),
+    (dict(d_r=32), "ATTN_ERR_HEAD_DIM"),
+    (dict(causal=2), "ATTN_ERR_CAUSAL_FLAG"),
+    (dict(n_splits=300), "ATTN_ERR_SPLITS"),
+    (dict(S=101), "ATTN_ERR_CAUSAL_SHAPE"),
+    (dict(T=(1 << 21)), "ATTN_ERR_SIZE_OVERFLOW"),
+    (dict(scale=float("inf")), "ATTN_ERR_SCALE"),
+    (dict(T=0, causal=0), "ATTN_ERR_NO_KEYS"),
+    (dict(kv=0), "ATTN_ERR_NULL_POINTER"),
+    (dict(o=OL + 8), "ATTN_ERR_ALIGNMENT"),
+    (dict(ws=0), "ATTN_ERR_WORKSPACE"),
+    (dict(ws_bytes=1000), "ATTN_ERR_WORKSPACE"),
+    (dict(o=KVC + 1024), "ATTN_ERR_ALIAS"),
+    (dict(ws=QL), "ATTN_ERR_ALIAS"),
+])
+def test_mla_invalid_arguments_rejected(lib, kw, code):
+    assert call_mla(lib, **kw) == STATUS[code]
+
+
+def test_mla_empty_and_sizes(lib):
+    assert call_mla(lib, q=0, kv=0, o=0, l=0, ws=0, B=0) == STATUS["ATTN_OK"]
+    assert call_mla(lib, q=0, kv=0, o=0, l=0, ws=0, S=0) == STATUS["ATTN_OK"]
+    assert ea.attn_mla_workspace_size(2, 128, 1, 8) == 8 * 2 * 128 * 513 * 4
+    assert ea.attn_mla_workspace_size(2, 128, 1, 1) == 0
+    assert ea.attn_mla_num_splits(1, 128, 1, 16384, True) >= 2
+    assert ea.attn_mla_num_splits(64, 128, 1, 16384, True) == 1
+    assert ea.attn_mla_num_splits(1, 128, 2, 1, True) == -1
+
+
+def test_mla_projection_arguments_rejected(lib):
+    ok = dict(B=1, H=4, S=1)
+    assert lib.mla_absorb_q(QL, KVC, WM, OL, 1, 4, 1, 128, 256, 64, None) == STATUS["ATTN_ERR_HEAD_DIM"]
+    assert lib.mla_absorb_q(QL, KVC, WM, OL, 1, 4, 1, 300, 512, 64, None) == STATUS["ATTN_ERR_HEAD_DIM"]
+    assert lib.mla_absorb_q(QL, 0, WM, OL, 1, 4, 1, 128, 512, 64, None) == STATUS["ATTN_ERR_NULL_POINTER"]
+    assert lib.mla_absorb_q(QL, KVC, WM, QL, 1, 4, 1, 128, 512, 64, None) == STATUS["ATTN_ERR_ALIAS"]
+    assert lib.mla_absorb_q(0, 0, 0, 0, 0, 4, 1, 128, 512, 64, None) == STATUS["ATTN_OK"]
+    assert lib.mla_up_project(QL, WM, OL, 1, 4, 1, 512, 100, None) == STATUS["ATTN_ERR_HEAD_DIM"]
+    assert lib.mla_up_project(QL + 4, WM, OL, 1, 4, 1, 512, 128, None) == STATUS["ATTN_ERR_ALIGNMENT"]
+    assert lib.mla_up_project(QL, WM, WM, 1, 4, 1, 512, 128, None) == STATUS["ATTN_ERR_ALIAS"]
+    assert lib.mla_up_project(QL, WM, OL, -1, 4, 1, 512, 128, None) == STATUS["ATTN_ERR_NEGATIVE_SIZE"]
+    assert ok

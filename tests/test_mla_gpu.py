@@ -1,0 +1,174 @@
+"""GPU parity of the MLA decode path (absorbed form) against the float64 CPU
+oracle.
+
+Inputs are the seeded recipe of workloads.make_mla_inputs (DeepSeek-V3 shapes
+of page "Attention Kernel 实现与正确性验证", section 2.3, or smaller).  Each
+step is checked against the oracle on the same bf16 operands, and the whole
+pipeline against the oracle's naive form (keys and values reconstructed per
+head, the definition):
+  * latent core: out_lat within 2e-2 + 2e-2 |ref|, LSE within 1e-3;
+  * projections and the pipeline: the forward's allclose made scale-free,
+    |y - ref| <= 2e-2 rms(ref) + 2e-2 |ref|, because the absorbed query and
+    the latent output are rounded to bf16 between the steps.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ea():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_02_amd as m
+    m.load_library()
+    return m
+
+
+def _dev():
+    return torch.device("cuda", 0)
+
+
+def _f64(t):
+    return workloads.to_float64(t)
+
+
+def _check_attn(o, l, O_ref, L_ref, what):
+    o = o.to(torch.float64).numpy()
+    l = l.to(torch.float64).numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), f"{what}: non-finite"
+    err = np.abs(o - O_ref)
+    bad = err > 2e-2 + 2e-2 * np.abs(O_ref)
+    assert not bad.any(), f"{what}: {int(bad.sum())} out of tolerance, max {err.max():.3e}"
+    assert np.abs(l - L_ref).max() <= 1e-3, f"{what}: lse err {np.abs(l - L_ref).max():.3e}"
+
+
+def _check_scaled(y, ref, what):
+    y = y.to(torch.float64).numpy()
+    assert np.all(np.isfinite(y)), f"{what}: non-finite"
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(y - ref)
+    bad = err > 2e-2 * rms + 2e-2 * np.abs(ref)
+    assert not bad.any(), f"{what}: {int(bad.sum())} out of tolerance, max {err.max():.3e} rms {rms:.3e}"
+
+
+def _latent_inputs(B, H, S, T, seed):
+    c_kv, k_pe, q_nope, q_pe, W_uk, W_uv = workloads.make_mla_inputs(B, H, S, T, seed)
+    kv = torch.cat([c_kv, k_pe], dim=-1).contiguous()
+    q_lat = torch.from_numpy(oracle.mla_absorb_q(_f64(q_nope), _f64(q_pe), _f64(W_uk))).to(torch.bfloat16)
+    return q_lat, kv
+
+
+def _run_core(ea, q_lat, kv, scale, causal, n_splits):
+    dev = _dev()
+    B, H, S, _ = q_lat.shape
+    T = kv.shape[1]
+    out = torch.full((B, H, S, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=dev)
+    ns = n_splits if n_splits > 0 else ea.attn_mla_num_splits(B, H, S, T, causal)
+    nbytes = ea.attn_mla_workspace_size(B, H, S, ns)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev) if nbytes else None
+    ea.attn_mla_decode(q_lat.to(dev), kv.to(dev), out, lse, scale, is_causal=causal,
+                       n_splits=n_splits, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 100, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n_splits", [1, 3, 0])
+def test_latent_core(ea, T, causal, n_splits):
+    B, H, S = 2, 16, 1
+    q_lat, kv = _latent_inputs(B, H, S, T, seed=13000 + T)
+    sc = 1 / math.sqrt(192)
+    o, l = _run_core(ea, q_lat, kv, sc, causal, n_splits)
+    O, L = oracle.mla_latent_attention(_f64(q_lat), _f64(kv), 512, is_causal=causal, sm_scale=sc)
+    _check_attn(o, l, O, L, f"T{T} c{int(causal)} s{n_splits}")
+
+
+@pytest.mark.parametrize("H,S,T", [(128, 1, 300), (128, 2, 129), (7, 5, 70), (3, 4, 4), (40, 3, 65)])
+@pytest.mark.parametrize("n_splits", [1, 4])
+def test_latent_core_heads_and_tokens(ea, H, S, T, n_splits):
+    """Pair blocks that mix query tokens, head counts that do not divide 32,
+    several causal query tokens (bottom-right)."""
+    q_lat, kv = _latent_inputs(1, H, S, T, seed=13100 + H + S)
+    sc = 1 / math.sqrt(192)
+    for causal in (False, True):
+        o, l = _run_core(ea, q_lat, kv, sc, causal, n_splits)
+        O, L = oracle.mla_latent_attention(_f64(q_lat), _f64(kv), 512, is_causal=causal, sm_scale=sc)
+        _check_attn(o, l, O, L, f"H{H} S{S} T{T} c{int(causal)}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.05, 0.3])
+def test_latent_core_scales(ea, scale):
+    q_lat, kv = _latent_inputs(1, 32, 1, 500, seed=13200)
+    o, l = _run_core(ea, q_lat, kv, scale, True, 3)
+    O, L = oracle.mla_latent_attention(_f64(q_lat), _f64(kv), 512, is_causal=True, sm_scale=scale)
+    _check_attn(o, l, O, L, f"scale {scale}")
+
+
+def test_projections(ea):
+    dev = _dev()
+    B, H, S = 3, 8, 2
+    c_kv, k_pe, q_nope, q_pe, W_uk, W_uv = workloads.make_mla_inputs(B, H, S, 10, 13300)
+    q_lat = torch.empty((B, H, S, 576), dtype=torch.bfloat16, device=dev)
+    ea.mla_absorb_q(q_nope.to(dev), q_pe.to(dev), W_uk.to(dev), q_lat)
+    ref = oracle.mla_absorb_q(_f64(q_nope), _f64(q_pe), _f64(W_uk))
+    _check_scaled(q_lat.cpu()[..., :512], ref[..., :512], "absorb")
+    assert torch.equal(q_lat.cpu()[..., 512:].view(torch.int16), q_pe.view(torch.int16)), "q_pe copy"
+    g = torch.Generator(device="cpu")
+    g.manual_seed(13301)
+    x = torch.randn((B, H, S, 512), generator=g).to(torch.bfloat16)
+    y = torch.empty((B, H, S, 128), dtype=torch.bfloat16, device=dev)
+    ea.mla_up_project(x.to(dev), W_uv.to(dev), y)
+    _check_scaled(y.cpu(), oracle.mla_up_project(_f64(x), _f64(W_uv)), "up")
+
+
+@pytest.mark.parametrize("B,H,S,T,causal", [(2, 16, 1, 200, True), (1, 128, 1, 300, True),
+                                            (1, 8, 3, 50, True), (33, 4, 1, 40, False)])
+def test_pipeline_against_naive(ea, B, H, S, T, causal):
+    """absorb -> latent core -> up-projection against the naive definition."""
+    dev = _dev()
+    c_kv, k_pe, q_nope, q_pe, W_uk, W_uv = workloads.make_mla_inputs(B, H, S, T, 13400 + B + H)
+    kv = torch.cat([c_kv, k_pe], dim=-1).contiguous()
+    out, lse = ea.mla_decode(q_nope.to(dev), q_pe.to(dev), kv.to(dev), W_uk.to(dev), W_uv.to(dev),
+                             is_causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.mla_naive(_f64(c_kv), _f64(k_pe), _f64(q_nope), _f64(q_pe), _f64(W_uk), _f64(W_uv),
+                           is_causal=causal, sm_scale=1 / math.sqrt(192))
+    _check_scaled(out.cpu(), ref, f"pipeline B{B} H{H} S{S} T{T}")
+
+
+@pytest.mark.parametrize("name", sorted(workloads.MLA_WORKLOADS))
+def test_mla_workloads(ea, name):
+    """The decode workloads at full size: every head of the first and last
+    batch element, pipeline against the oracle's absorbed form (pinned equal to
+    the naive form)."""
+    w = workloads.MLA_WORKLOADS[name]
+    dev = _dev()
+    c_kv, k_pe, q_nope, q_pe, W_uk, W_uv = workloads.make_mla_inputs(w.B, w.H, w.S, w.T, w.seed)
+    kv = torch.cat([c_kv, k_pe], dim=-1).contiguous()
+    out, _ = ea.mla_decode(q_nope.to(dev), q_pe.to(dev), kv.to(dev), W_uk.to(dev), W_uv.to(dev),
+                           is_causal=w.causal)
+    torch.cuda.synchronize()
+    for b in sorted({0, w.B - 1}):
+        sl = slice(b, b + 1)
+        ref = oracle.mla_absorbed(_f64(c_kv[sl]), _f64(k_pe[sl]), _f64(q_nope[sl]), _f64(q_pe[sl]),
+                                  _f64(W_uk), _f64(W_uv), is_causal=w.causal, sm_scale=w.sm_scale)
+        _check_scaled(out.cpu()[sl], ref, f"{name} b{b}")
+
+
+def test_mla_deterministic(ea):
+    q_lat, kv = _latent_inputs(1, 128, 1, 3000, seed=13500)
+    a = _run_core(ea, q_lat, kv, 0.07, True, 0)
+    b = _run_core(ea, q_lat, kv, 0.07, True, 0)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])

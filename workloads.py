@@ -121,3 +121,65 @@ def workload_inputs(w: Workload):
 def to_float64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of a bf16 (or fp32) CPU tensor to a float64 NumPy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+# ---------------------------------------------------------------- MLA decode
+@dataclasses.dataclass(frozen=True)
+class MlaWorkload:
+    """Absorbed MLA decode, DeepSeek-V3 shapes of page "Attention Kernel 实现与
+    正确性验证", section 2.3: H=128 heads, latent d_c=512, rotary d_R=64,
+    d_nope = d_v = 128, S query tokens against a T-token latent cache."""
+    name: str
+    B: int
+    S: int
+    T: int
+    seed: int
+    H: int = 128
+    d_c: int = 512
+    d_r: int = 64
+    d_nope: int = 128
+    d_v: int = 128
+    causal: bool = True
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_nope + self.d_r)
+
+    def core_flops(self) -> float:
+        """Latent attention: 2*(d_c + d_r) + 2*d_c per visible (token, head, key)."""
+        pairs = float(self.S) * self.T - (float(self.S) * (self.S - 1) / 2 if self.causal else 0.0)
+        return self.B * self.H * pairs * 2.0 * (2 * self.d_c + self.d_r)
+
+    def core_bytes(self) -> int:
+        """Latent cache read once, absorbed queries read, latent outputs and LSE written."""
+        kv = self.B * self.T * (self.d_c + self.d_r) * 2
+        q = self.B * self.H * self.S * (self.d_c + self.d_r) * 2
+        o = self.B * self.H * self.S * (self.d_c * 2 + 4)
+        return kv + q + o
+
+
+MLA_WORKLOADS = {w.name: w for w in [
+    MlaWorkload("mla_decode_t4096", 1, 1, 4096, 701),
+    MlaWorkload("mla_decode_t16384", 1, 1, 16384, 702),
+    MlaWorkload("mla_decode_b8_t4096", 8, 1, 4096, 703),
+    MlaWorkload("mla_decode_b32_t4096", 32, 1, 4096, 704),
+]}
+
+
+def make_mla_inputs(B: int, H: int, S: int, T: int, seed: int, d_c: int = 512, d_r: int = 64,
+                    d_nope: int = 128, d_v: int = 128):
+    """Draw bf16 c_kv [B,T,d_c], k_pe [B,T,d_r], q_nope [B,H,S,d_nope],
+    q_pe [B,H,S,d_r], W_uk [H,d_nope,d_c], W_uv [H,d_v,d_c] on the CPU, in that
+    order from one seeded generator: i.i.d. N(0,1), the two projections scaled
+    by 1/sqrt(d_c) so that reconstructed keys and values are about N(0,1)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    shapes = [(B, T, d_c), (B, T, d_r), (B, H, S, d_nope), (B, H, S, d_r), (H, d_nope, d_c),
+              (H, d_v, d_c)]
+    out = []
+    for i, s in enumerate(shapes):
+        t = torch.randn(s, generator=g, dtype=torch.float32)
+        if i >= 4:
+            t = t / math.sqrt(d_c)
+        out.append(t.to(torch.bfloat16))
+    return tuple(out)
