@@ -257,6 +257,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sweep", action="store_true",
                     help="also time every workload and print a table to stderr")
+    ap.add_argument("--mla-sweep", action="store_true",
+                    help="time the MLA decode workloads and print a table to stderr, then exit")
     ap.add_argument("--backward-sweep", action="store_true",
                     help="time attn_bwd on the square workloads and print a table to stderr, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -284,6 +286,49 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
+        return
+
+    if args.mla_sweep:
+        # MLA decode (absorbed): the three steps timed together, plus the
+        # latent core alone; core FLOPs 2*(2*512+64) per visible (token, head, key)
+        dev = torch.device("cuda", 0)
+        for name, mw in workloads.MLA_WORKLOADS.items():
+            c_kv, k_pe, q_nope, q_pe, W_uk, W_uv = workloads.make_mla_inputs(mw.B, mw.H, mw.S, mw.T, mw.seed)
+            kv = torch.cat([c_kv, k_pe], -1).contiguous().to(dev)
+            qn, qp, wk, wv = q_nope.to(dev), q_pe.to(dev), W_uk.to(dev), W_uv.to(dev)
+            q_lat = torch.empty((mw.B, mw.H, mw.S, 576), dtype=torch.bfloat16, device=dev)
+            out_lat = torch.empty((mw.B, mw.H, mw.S, 512), dtype=torch.bfloat16, device=dev)
+            lse_m = torch.empty((mw.B, mw.H, mw.S), dtype=torch.float32, device=dev)
+            out_m = torch.empty((mw.B, mw.H, mw.S, mw.d_v), dtype=torch.bfloat16, device=dev)
+            ns = ea.attn_mla_num_splits(mw.B, mw.H, mw.S, mw.T, mw.causal)
+            nb = ea.attn_mla_workspace_size(mw.B, mw.H, mw.S, ns)
+            ws_m = torch.empty((max(nb, 1),), dtype=torch.uint8, device=dev)
+
+            def core():
+                ea.attn_mla_decode(q_lat, kv, out_lat, lse_m, mw.sm_scale, is_causal=mw.causal,
+                                   n_splits=ns, workspace=ws_m)
+
+            def full():
+                ea.mla_absorb_q(qn, qp, wk, q_lat)
+                core()
+                ea.mla_up_project(out_lat, wv, out_m)
+            res_t = {}
+            for label, fn in (("core", core), ("full", full)):
+                for _ in range(3):
+                    fn()
+                ev = []
+                for _ in range(20):
+                    s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    s_.record()
+                    fn()
+                    e_.record()
+                    ev.append((s_, e_))
+                torch.cuda.synchronize()
+                res_t[label] = float(np.median([a.elapsed_time(b_) for a, b_ in ev]))
+            t = res_t["core"]
+            log(f"[mla] {name:22s} splits {ns:3d}  core {t * 1e3:8.1f} us  "
+                f"{mw.core_bytes() / t / 1e6:7.0f} GB/s  {mw.core_flops() / t / 1e9:7.1f} TFLOP/s   "
+                f"absorb+core+up {res_t['full'] * 1e3:8.1f} us")
         return
 
     if args.backward_sweep:

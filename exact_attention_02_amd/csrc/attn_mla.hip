@@ -16,7 +16,8 @@ namespace {
 
 using ea02::MlaParams;
 using ea02::MlaProjParams;
-constexpr int kMlaP = 3;
+constexpr int kMlaP = 4;
+constexpr int kMlaPairs = 64;  // (token, head) pairs per workgroup
 constexpr int kMlaMaxSplits = 256;
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -50,13 +51,13 @@ int mla_check_sizes(int64_t B, int64_t H, int64_t S, int64_t T, int64_t d_c, int
   if (B > (1 << 24) || H > (1 << 16) || S > (1 << 24) || T * ea02::kMlaRowBytes > (int64_t(1) << 31) ||
       S * H > (int64_t(1) << 30) || B * H * S > INT32_MAX)
     return ATTN_ERR_SIZE_OVERFLOW;
-  const int64_t pbs = (S * H + 31) / 32;
+  const int64_t pbs = (S * H + kMlaPairs - 1) / kMlaPairs;
   if (pbs * B * std::max<int64_t>(n_splits, 1) > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
   return ATTN_OK;
 }
 
 int64_t mla_choose_splits(int64_t B, int64_t H, int64_t S, int64_t T) {
-  const int64_t wgs = ((S * H + 31) / 32) * B;
+  const int64_t wgs = ((S * H + kMlaPairs - 1) / kMlaPairs) * B;
   const int64_t cus = device_cus();
   if (wgs <= 0 || wgs >= cus) return 1;
   const int64_t tiles = (T + 31) / 32;
@@ -116,7 +117,7 @@ extern "C" int attn_mla_decode(const void* q_lat, const void* kv, void* out_lat,
   p.T = static_cast<int>(T);
   p.n_pairs = static_cast<int>(S * H);
   p.causal_off = is_causal ? static_cast<int>(T - S) : 0;
-  p.n_pair_blocks = static_cast<int>((S * H + 31) / 32);
+  p.n_pair_blocks = static_cast<int>((S * H + kMlaPairs - 1) / kMlaPairs);
   p.n_splits = split ? static_cast<int>(ns) : 1;
   p.scale_log2 = std::fmax(std::fabs(sm_scale) * ea02::kLog2e, FLT_MIN);
   p.q_sign = (sm_scale < 0.f) ? 0x80008000u : 0u;

@@ -10,18 +10,18 @@
 //   out = out_lat W_uv[h]^T                            (mla_up_kernel)
 //
 // attn_mla_kernel: MQA with 576-wide scores and 512-wide values.  A workgroup
-// owns 32 (query token, head) pairs and streams 32-key tiles of the latent
-// cache through a 3-stage LDS ring.  Its four waves split the work two ways:
-//  * scores: wave w takes 9 of the 36 k-steps (16 dims each) of S^T = K Q^T
-//    for all 32 keys and pairs; the four fp32 partials meet in LDS and every
-//    wave sums them in the same order, so all waves hold the same S^T and
-//    take the same online-softmax decisions (lazy rescale, as in the
-//    forward kernel);
-//  * values: wave w accumulates O^T for dims [128 w, 128 w + 128) with
-//    O^T += V^T P^T, V^T from the LDS transpose read of the tile's first 512
-//    columns and P^T the bf16-rounded S^T accumulator.
-// The query fragments of a wave are only its 9 k-steps and its accumulator
-// only 128 dims, which is what makes 576/512-wide heads fit in registers.
+// of four waves owns 64 (query token, head) pairs and streams 32-key tiles of
+// the latent cache through a 4-stage LDS ring.  Wave w works on pair block
+// w & 1 (32 pairs) and half h = w >> 1 of the problem:
+//  * scores: k-steps [18 h, 18 h + 18) of S^T = K Q^T (16 dims each); the
+//    two halves' fp32 partials meet in LDS and both waves add them (fp32
+//    addition is commutative, so both hold the same S^T and take the same
+//    online-softmax decisions: lazy rescale, as in the forward kernel);
+//  * values: O^T for dims [256 h, 256 h + 256) with O^T += V^T P^T, V^T from
+//    the LDS transpose read of the tile's first 512 columns and P^T the
+//    bf16-rounded S^T accumulator.
+// A wave thus holds 18 query k-steps and 256 value dims: 72 + 128 registers,
+// where all 36 k-steps and 512 dims of a pair block in one wave would not fit.
 #pragma once
 
 #include "attn_fwd_kernel.hpp"
@@ -68,10 +68,12 @@ void attn_mla_kernel(MlaParams p) {
   constexpr int TILE_BYTES = BN * kMlaRowBytes;          // 36 KiB
   constexpr int LOADS = TILE_BYTES / 1024;               // 36
   constexpr int LPW = LOADS / NW;                        // 9
-  constexpr int KSW = kMlaDqk / 16 / NW;                 // 9 k-steps per wave
-  constexpr int DVW = kMlaDc / NW;                       // 128 value dims per wave
+  constexpr int KSH = kMlaDqk / 16 / 2;                  // 18 k-steps per half
+  constexpr int NDB = kMlaDc / 32 / 2;                   // 8 value blocks of 32 per half
+  constexpr int PPW = 64;                                // pairs per workgroup
   constexpr int PART_BYTES = NW * 64 * 16 * 4;           // S^T partials, 16 KiB
   static_assert(LOADS % NW == 0 && (P - 1) * LPW <= 63, "load groups");
+  static_assert(P * TILE_BYTES + PART_BYTES <= 160 * 1024, "LDS fits the 160 KiB of a CU");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[P * TILE_BYTES + PART_BYTES];
 
   const int tid = threadIdx.x;
@@ -79,6 +81,8 @@ void attn_mla_kernel(MlaParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int col = lane & 31;
+  const int pbw = wave & 1;   // pair block of this wave
+  const int kh = wave >> 1;   // half of the k-steps and of the value dims
 
   // pair blocks of one (batch, split) are B * n_splits apart in the grid so
   // that they share an XCD (and its L2) under round-robin dispatch
@@ -90,9 +94,10 @@ void attn_mla_kernel(MlaParams p) {
   const int T = p.T;
   const int off = p.causal_off;
   const int last_pair = p.n_pairs - 1;
-  const int P0 = pb * 32;
-  const int row0 = min(P0, last_pair) / p.H;                 // first query token of the block
-  const int row_end = min(P0 + 31, last_pair) / p.H + 1;
+  const int P0 = pb * PPW;
+  const int wp0 = P0 + 32 * pbw;
+  const int wave_row0 = min(wp0, last_pair) / p.H;          // first query token of this wave
+  const int row_end = min(P0 + PPW - 1, last_pair) / p.H + 1;
 
   const int kv_end = p.causal ? min(row_end + off, T) : T;
   int n_tiles = (kv_end + BN - 1) / BN;
@@ -104,17 +109,17 @@ void attn_mla_kernel(MlaParams p) {
     kbase = t0 * BN;
   }
 
-  // this lane's pair and its 9 query k-steps (B operands of S^T = K Q^T)
-  const int pair = P0 + col;
+  // this lane's pair and its half of the query k-steps
+  const int pair = wp0 + col;
   const bool valid = pair <= last_pair;
   const int pc = min(pair, last_pair);
   const int my_row = pc / p.H;
   const int h = pc - my_row * p.H;
   const size_t bhr = ((size_t)b * p.H + h) * (size_t)p.S + my_row;
-  bf16x8 qf[KSW];
+  bf16x8 qf[KSH];
 #pragma unroll
-  for (int i = 0; i < KSW; ++i) {
-    u32x4 x = *reinterpret_cast<const u32x4*>(p.q + bhr * kMlaDqk + (wave * KSW + i) * 16 + half * 8);
+  for (int i = 0; i < KSH; ++i) {
+    u32x4 x = *reinterpret_cast<const u32x4*>(p.q + bhr * kMlaDqk + (kh * KSH + i) * 16 + half * 8);
     x ^= p.q_sign;
     qf[i] = as_bf16x8(x);
   }
@@ -123,70 +128,68 @@ void attn_mla_kernel(MlaParams p) {
   // lane -> (row, stored chunk j) and fetches chunk j ^ swz(row) of that row
   const u32x4 rsrc = make_rsrc(p.kv + (size_t)b * T * kMlaDqk, (uint32_t)((size_t)T * kMlaRowBytes));
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
-  int ld_row[LPW], ld_off[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int e = (wave * LPW + i) * 64 + lane;
-    ld_row[i] = e / kMlaChunks;
-    const int j = e - ld_row[i] * kMlaChunks;
-    ld_off[i] = (j ^ mla_swz(ld_row[i])) << 4;
-  }
   auto issue = [&](int t, int slot) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int key = min(kbase + t * BN + ld_row[i], T - 1);
-      dma_16B(rsrc, key * kMlaRowBytes + ld_off[i], lds_base + slot * TILE_BYTES + (wave * LPW + i) * 1024);
+      const int e = (wave * LPW + i) * 64 + lane;
+      const int row = e / kMlaChunks;
+      const int j = e - row * kMlaChunks;
+      const int key = min(kbase + t * BN + row, T - 1);
+      dma_16B(rsrc, key * kMlaRowBytes + ((j ^ mla_swz(row)) << 4),
+              lds_base + slot * TILE_BYTES + (wave * LPW + i) * 1024);
     }
   };
 
-  // V^T transpose-read offsets: rows 16 st + 4 half + L/4 (+8), dims
-  // 128 wave + 32 db + 16 (G16 & 1) + 4 (L & 3); independent of st
+  // V^T transpose-read offsets: rows 4 half + L/4 (+8 for the second read),
+  // dims 32 db + 16 (G16 & 1) + 4 (L & 3), i.e. chunk 4 db + c_low with
+  // c_low = 2 (G16 & 1) + (L & 3) / 2.  With x = swz(row) < 8 the stored chunk
+  // is 4 (db ^ (x >> 2)) + (c_low ^ (x & 3)): for even db that is 4 db + 4 e +
+  // ..., for odd db 4 db - 4 e + ..., e = x >> 2, so one base per parity of
+  // db plus the immediate 64 db gives every block's address.
   const int L16 = lane & 15;
-  int tr_off[2][DVW / 32];
+  const int c_low = 2 * ((lane >> 4) & 1) + ((L16 & 3) >> 1);
+  const int inner = ((4 * (L16 & 3)) & 7) * 2;
+  int tr_base[2][2];
 #pragma unroll
-  for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-    for (int db = 0; db < DVW / 32; ++db) {
-      const int row = 4 * half + (L16 >> 2) + 8 * hi;
-      const int d = wave * DVW + db * 32 + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
-      tr_off[hi][db] = row * kMlaRowBytes + (((d >> 3) ^ mla_swz(row)) << 4) + (d & 7) * 2;
-    }
+  for (int hi = 0; hi < 2; ++hi) {
+    const int row = 4 * half + (L16 >> 2) + 8 * hi;
+    const int x = mla_swz(row);
+    const int base = row * kMlaRowBytes + ((c_low ^ (x & 3)) << 4) + inner;
+    tr_base[hi][0] = base + 64 * (x >> 2);
+    tr_base[hi][1] = base - 64 * (x >> 2);
+  }
 
   float* part = reinterpret_cast<float*>(lds + P * TILE_BYTES);
-  f32x16 acc[DVW / 32];
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int db = 0; db < DVW / 32; ++db) acc[db] = f32x16{};
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
   float m_used = -INFINITY, l_run = 0.f;
   const float sl2 = p.scale_log2;
 
   auto compute = [&](int t, int slot) {
     const uint8_t* kt = lds + slot * TILE_BYTES;
-    // partial S^T over this wave's k-steps; element r holds key
-    // 8(r/4) + 4 half + r%4 of the tile for this lane's pair
-    f32x16 sp = f32x16{};
+    // S^T partial: element r holds key 8(r/4) + 4 half + r%4 of the tile
+    f32x16 s = f32x16{};
 #pragma unroll
-    for (int i = 0; i < KSW; ++i) {
-      const int chunk = (2 * (wave * KSW + i) + half) ^ mla_swz(col);
+    for (int i = 0; i < KSH; ++i) {
+      const int chunk = (2 * (kh * KSH + i) + half) ^ mla_swz(col);
       const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + col * kMlaRowBytes + (chunk << 4)));
-      sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[i], sp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[i], s, 0, 0, 0);
     }
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
       *reinterpret_cast<f32x4*>(part + ((wave * 64 + lane) * 16 + 4 * r4)) =
-          f32x4{sp[4 * r4], sp[4 * r4 + 1], sp[4 * r4 + 2], sp[4 * r4 + 3]};
+          f32x4{s[4 * r4], s[4 * r4 + 1], s[4 * r4 + 2], s[4 * r4 + 3]};
     __syncthreads();
-    f32x16 s = f32x16{};
+    const int other = wave ^ 2;  // same pair block, other half
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(part + ((other * 64 + lane) * 16 + 4 * r4));
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(part + ((w * 64 + lane) * 16 + 4 * r4));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[4 * r4 + e] += x[e];
-      }
-    // mask: causal diagonal or the ragged end of the cache
+      for (int e = 0; e < 4; ++e) s[4 * r4 + e] += x[e];
+    }
     const int key0 = kbase + t * BN;
-    if ((p.causal && key0 + BN - 1 > row0 + off) || key0 + BN > T) {
+    if ((p.causal && key0 + BN - 1 > wave_row0 + off) || key0 + BN > T) {
       const int lim = (p.causal ? min(my_row + off + 1, T) : T) - key0 - 4 * half;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -201,33 +204,32 @@ void attn_mla_kernel(MlaParams p) {
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DVW / 32; ++db) acc[db] *= alpha;
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
       m_used = m_new;
     }
     const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
     f32x8 pf;
-    bf16x8 pb[2];
+    bf16x8 pb2[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -m_sub));
       pf[r & 7] = pe;
       l_run += pe;
-      if ((r & 7) == 7) pb[r >> 3] = __builtin_convertvector(pf, bf16x8);
+      if ((r & 7) == 7) pb2[r >> 3] = __builtin_convertvector(pf, bf16x8);
     }
+    // O^T += V^T P^T over this half's 256 value dims
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int db = 0; db < DVW / 32; ++db) {
-        const uint8_t* a = kt + (16 * st) * kMlaRowBytes;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[0][db]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[1][db]));
+      for (int db = 0; db < NDB; ++db) {
+        const uint8_t* a = kt + (16 * st) * kMlaRowBytes + 64 * (kh * NDB + db);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_base[0][db & 1]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_base[1][db & 1]));
         const bf16x8 vT = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vT, pb[st], acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vT, pb2[st], acc[db], 0, 0, 0);
       }
   };
 
-  // load ring as in the backward kernels: tile t in slot t % P, issued P-1
-  // tiles ahead, clamped re-loads past the end keep one constant vmcnt
   if (n_tiles > 0) {
 #pragma unroll
     for (int j = 0; j < P - 1; ++j) issue(min(j, n_tiles - 1), j);
@@ -242,11 +244,12 @@ void attn_mla_kernel(MlaParams p) {
 
   const float l_tot = half_swap_sum(l_run);
   if (!valid) return;
+  const int dbase = kh * (kMlaDc / 2);
   if constexpr (!SPLIT) {
     const float inv = 1.f / l_tot;
-    uint16_t* orow = p.o + bhr * kMlaDc + wave * DVW;
+    uint16_t* orow = p.o + bhr * kMlaDc + dbase;
 #pragma unroll
-    for (int db = 0; db < DVW / 32; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = db * 32 + 8 * g4 + 4 * half;
@@ -254,21 +257,21 @@ void attn_mla_kernel(MlaParams p) {
                    acc[db][4 * g4 + 3] * inv};
         *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4));
       }
-    if (wave == 0 && half == 0) p.lse[bhr] = (m_used + __log2f(l_tot)) * kLn2;
+    if (kh == 0 && half == 0) p.lse[bhr] = (m_used + __log2f(l_tot)) * kLn2;
   } else {
     const bool seen = l_tot > 0.f;
     const float inv = seen ? 1.f / l_tot : 0.f;
     const size_t slot = (size_t)split * ((size_t)p.B * p.H * p.S) + bhr;
-    float* orow = p.o_part + slot * kMlaDc + wave * DVW;
+    float* orow = p.o_part + slot * kMlaDc + dbase;
 #pragma unroll
-    for (int db = 0; db < DVW / 32; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = db * 32 + 8 * g4 + 4 * half;
         *reinterpret_cast<f32x4*>(orow + d0) = f32x4{acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv,
                                                      acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv};
       }
-    if (wave == 0 && half == 0) p.lse_part[slot] = seen ? m_used + __log2f(l_tot) : -INFINITY;
+    if (kh == 0 && half == 0) p.lse_part[slot] = seen ? m_used + __log2f(l_tot) : -INFINITY;
   }
 }
 
