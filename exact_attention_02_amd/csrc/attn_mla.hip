@@ -160,8 +160,7 @@ extern "C" int mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_
   if (groups * H > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
   if (B == 0 || H == 0 || S == 0) return ATTN_OK;
   if (!q_nope || !q_pe || !w_uk || !q_lat) return ATTN_ERR_NULL_POINTER;
-  if ((reinterpret_cast<uintptr_t>(q_nope) & 1u) || (reinterpret_cast<uintptr_t>(q_pe) & 3u) ||
-      (reinterpret_cast<uintptr_t>(w_uk) & 3u) || (reinterpret_cast<uintptr_t>(q_lat) & 3u))
+  if ((reinterpret_cast<uintptr_t>(q_nope) & 1u) || mis16(q_pe) || mis16(w_uk) || mis16(q_lat))
     return ATTN_ERR_ALIGNMENT;
   const size_t nn = size_t(B * H * S * d_nope) * 2, npe = size_t(B * H * S) * ea02::kMlaDr * 2;
   const size_t nw = size_t(H * d_nope) * ea02::kMlaDc * 2, nout = size_t(B * H * S) * ea02::kMlaDqk * 2;
@@ -177,9 +176,32 @@ extern "C" int mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_
   p.S = static_cast<int>(S);
   p.d_n = static_cast<int>(d_nope);
   p.rows_per_head = static_cast<int>(B * S);
-  hipLaunchKernelGGL(ea02::mla_absorb_kernel, dim3(static_cast<unsigned>(groups * H)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), p);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // passes of kProjRows rows of every head, then one pass over the remaining rows
+  const int64_t rows = B * S;
+  const int64_t full = rows / ea02::kProjRows;
+  const int rem = static_cast<int>(rows - full * ea02::kProjRows);
+  if (full > 0) {
+    p.row_base = 0;
+    hipLaunchKernelGGL(ea02::mla_absorb_kernel<ea02::kProjRows>, dim3(static_cast<unsigned>(full * H)), dim3(256),
+                       0, s, p);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  if (rem > 0) {
+    p.row_base = static_cast<int>(full * ea02::kProjRows);
+    const dim3 g(static_cast<unsigned>(H));
+    switch (rem) {
+      case 1: hipLaunchKernelGGL(ea02::mla_absorb_kernel<1>, g, dim3(256), 0, s, p); break;
+      case 2: hipLaunchKernelGGL(ea02::mla_absorb_kernel<2>, g, dim3(256), 0, s, p); break;
+      case 3: hipLaunchKernelGGL(ea02::mla_absorb_kernel<3>, g, dim3(256), 0, s, p); break;
+      case 4: hipLaunchKernelGGL(ea02::mla_absorb_kernel<4>, g, dim3(256), 0, s, p); break;
+      case 5: hipLaunchKernelGGL(ea02::mla_absorb_kernel<5>, g, dim3(256), 0, s, p); break;
+      case 6: hipLaunchKernelGGL(ea02::mla_absorb_kernel<6>, g, dim3(256), 0, s, p); break;
+      default: hipLaunchKernelGGL(ea02::mla_absorb_kernel<7>, g, dim3(256), 0, s, p); break;
+    }
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
 }
 
 extern "C" int mla_up_project(const void* out_lat, const void* w_uv, void* out, int64_t B, int64_t H, int64_t S,
@@ -206,6 +228,7 @@ extern "C" int mla_up_project(const void* out_lat, const void* w_uv, void* out, 
   p.S = static_cast<int>(S);
   p.d_n = static_cast<int>(d_v);
   p.rows_per_head = static_cast<int>(B * S);
+  p.row_base = 0;
   hipLaunchKernelGGL(ea02::mla_up_kernel, dim3(static_cast<unsigned>(blocks)), dim3(64), 0,
                      static_cast<hipStream_t>(stream), p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;

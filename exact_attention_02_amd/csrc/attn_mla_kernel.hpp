@@ -276,10 +276,6 @@ void attn_mla_kernel(MlaParams p) {
 }
 
 // ---------------------------------------------------------------- projections
-// q_lat[r, c] = sum_d q_nope[r, d] W_uk[h, d, c] for the rows r of head h,
-// q_lat[r, 512 + e] = q_pe[r, e].  One block per (head, group of up to 32 rows
-// of that head); thread t owns columns 2t, 2t+1 and reads W_uk[h, d, :] rows
-// coalesced; the rows' q_nope values are staged in LDS.
 struct MlaProjParams {
   const uint16_t* x;    // absorb: q_nope [B, H, S, d_n];  up: out_lat [B, H, S, 512]
   const uint16_t* x2;   // absorb: q_pe [B, H, S, 64]
@@ -287,50 +283,89 @@ struct MlaProjParams {
   uint16_t* y;          // absorb: q_lat [B, H, S, 576];   up: out [B, H, S, d_v]
   int B, H, S, d_n;     // d_n: d_nope (absorb) or d_v (up)
   int rows_per_head;    // B * S
+  int row_base;         // absorb: first row of this launch's passes
 };
 
-constexpr int kProjRows = 32;
+constexpr int kProjRows = 8;       // query rows per absorb pass
+constexpr int kAbsorbDG = 4;       // d-groups per absorb block
+constexpr int kAbsorbUnroll = 8;   // weight rows in flight per thread
 
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 4)))
-void mla_absorb_kernel(MlaProjParams p) {
+// q_lat[r, c] = sum_d q_nope[r, d] W_uk[h, d, c] for up to 8 rows r of head h,
+// q_lat[r, 512 + e] = q_pe[r, e].  A block of 256 threads covers one head and
+// one group of rows: thread t owns columns 8 (t % 64) .. +8 and every 4th
+// weight row d = t / 64 + 4 i, reading 16 bytes of W_uk per row with 8 rows
+// in flight (the weights are read once and streamed), and the four d-groups
+// are added through LDS.  R is the number of rows of the pass (1..8).
+template <int R>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void mla_absorb_kernel(MlaProjParams p) {
   __shared__ float xs[kProjRows][256];
+  __shared__ f32x4 red[kAbsorbDG - 1][64][R][2];
   const int h = blockIdx.x % p.H;
-  const int r0 = (blockIdx.x / p.H) * kProjRows;
-  const int nr = min(kProjRows, p.rows_per_head - r0);
+  const int r0 = p.row_base + (blockIdx.x / p.H) * kProjRows;
   const int t = threadIdx.x;
+  const int cg = t % 64, dg = t / 64;
   // row r of head h is (b, s) = (r / S, r % S)
-  for (int i = t; i < nr * p.d_n; i += 256) {
-    const int r = i / p.d_n, d = i - r * p.d_n;
+  auto row_index = [&](int r) {
     const int rr = r0 + r;
-    const size_t row = ((size_t)(rr / p.S) * p.H + h) * p.S + (rr % p.S);
-    xs[r][d] = (float)__builtin_bit_cast(__bf16, p.x[row * p.d_n + d]);
+    return ((size_t)(rr / p.S) * p.H + h) * p.S + (rr % p.S);
+  };
+  for (int i = t; i < R * p.d_n; i += 256) {
+    const int r = i / p.d_n, d = i - r * p.d_n;
+    xs[r][d] = (float)__builtin_bit_cast(__bf16, p.x[row_index(r) * p.d_n + d]);
   }
   __syncthreads();
-  float acc[kProjRows][2];
+  f32x4 acc[R][2];
 #pragma unroll
-  for (int r = 0; r < kProjRows; ++r) acc[r][0] = acc[r][1] = 0.f;
-  const uint16_t* wh = p.w + (size_t)h * p.d_n * kMlaDc + 2 * t;
-  for (int d = 0; d < p.d_n; ++d) {
-    const uint32_t wv = *reinterpret_cast<const uint32_t*>(wh + (size_t)d * kMlaDc);
-    const float w0 = __uint_as_float(wv << 16), w1 = __uint_as_float(wv & 0xffff0000u);
+  for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* wh = p.w + (size_t)h * p.d_n * kMlaDc + 8 * cg;
+  for (int d0 = dg; d0 < p.d_n; d0 += kAbsorbDG * kAbsorbUnroll) {
+    u32x4 wv[kAbsorbUnroll];
 #pragma unroll
-    for (int r = 0; r < kProjRows; ++r) {
-      acc[r][0] = __builtin_fmaf(xs[r][d], w0, acc[r][0]);
-      acc[r][1] = __builtin_fmaf(xs[r][d], w1, acc[r][1]);
+    for (int u = 0; u < kAbsorbUnroll; ++u) {
+      const int d = min(d0 + kAbsorbDG * u, p.d_n - 1);
+      wv[u] = *reinterpret_cast<const u32x4*>(wh + (size_t)d * kMlaDc);
+    }
+#pragma unroll
+    for (int u = 0; u < kAbsorbUnroll; ++u) {
+      const int d = d0 + kAbsorbDG * u;
+      if (d < p.d_n) {
+        const bf16x8 wb = as_bf16x8(wv[u]);
+        f32x4 w0 = {(float)wb[0], (float)wb[1], (float)wb[2], (float)wb[3]};
+        f32x4 w1 = {(float)wb[4], (float)wb[5], (float)wb[6], (float)wb[7]};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float xv = xs[r][d];
+          acc[r][0] += xv * w0;
+          acc[r][1] += xv * w1;
+        }
+      }
     }
   }
-  // (a fully unrolled loop with a guard, so that acc stays in registers)
+  if (dg > 0) {
 #pragma unroll
-  for (int r = 0; r < kProjRows; ++r) {
-    if (r < nr) {
-      const int rr = r0 + r;
-      const size_t row = ((size_t)(rr / p.S) * p.H + h) * p.S + (rr % p.S);
-      const bf16x2 v = __builtin_convertvector(f32x2{acc[r][0], acc[r][1]}, bf16x2);
-      *reinterpret_cast<uint32_t*>(p.y + row * kMlaDqk + 2 * t) = __builtin_bit_cast(uint32_t, v);
-      if (t < kMlaDr / 2)
-        *reinterpret_cast<uint32_t*>(p.y + row * kMlaDqk + kMlaDc + 2 * t) =
-            *reinterpret_cast<const uint32_t*>(p.x2 + row * kMlaDr + 2 * t);
+    for (int r = 0; r < R; ++r) {
+      red[dg - 1][cg][r][0] = acc[r][0];
+      red[dg - 1][cg][r][1] = acc[r][1];
     }
+  }
+  __syncthreads();
+  if (dg != 0) return;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int g = 0; g < kAbsorbDG - 1; ++g) {
+      acc[r][0] += red[g][cg][r][0];
+      acc[r][1] += red[g][cg][r][1];
+    }
+    const size_t row = row_index(r);
+    const bf16x4 lo = __builtin_convertvector(acc[r][0], bf16x4);
+    const bf16x4 hi = __builtin_convertvector(acc[r][1], bf16x4);
+    *reinterpret_cast<u32x4*>(p.y + row * kMlaDqk + 8 * cg) =
+        u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+              __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+    if (cg < kMlaDr / 8)
+      *reinterpret_cast<u32x4*>(p.y + row * kMlaDqk + kMlaDc + 8 * cg) =
+          *reinterpret_cast<const u32x4*>(p.x2 + row * kMlaDr + 8 * cg);
   }
 }
 

@@ -255,7 +255,7 @@ size_t attn_mla_workspace_size(int64_t B, int64_t H, int64_t S, int64_t n_splits
  *   q_nope [B, H, S, d_nope] (1 <= d_nope <= 256), q_pe [B, H, S, d_r],
  *   w_uk [H, d_nope, d_c], q_lat [B, H, S, d_c + d_r] (written); d_c = 512,
  *   d_r = 64.  Errors: NEGATIVE_SIZE, HEAD_DIM, SIZE_OVERFLOW, empty work ->
- *   ATTN_OK, NULL_POINTER, ALIGNMENT (q_nope 2 bytes, others 4), ALIAS, LAUNCH.
+ *   ATTN_OK, NULL_POINTER, ALIGNMENT (q_nope 2 bytes, others 16), ALIAS, LAUNCH.
  */
 int mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_uk, void* q_lat, int64_t B,
                  int64_t H, int64_t S, int64_t d_nope, int64_t d_c, int64_t d_r, void* stream);

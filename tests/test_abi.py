@@ -297,7 +297,7 @@ def test_mla_empty_and_sizes(lib):
     assert ea.attn_mla_workspace_size(2, 128, 1, 8) == 8 * 2 * 128 * 513 * 4
     assert ea.attn_mla_workspace_size(2, 128, 1, 1) == 0
     assert ea.attn_mla_num_splits(1, 128, 1, 16384, True) >= 2
-    assert ea.attn_mla_num_splits(64, 128, 1, 16384, True) == 1
+    assert ea.attn_mla_num_splits(256, 128, 1, 16384, True) == 1
     assert ea.attn_mla_num_splits(1, 128, 2, 1, True) == -1
 
 
