@@ -27,11 +27,13 @@
 //  * A ring of P LDS stages for K and for V: after the barrier that opens tile
 //    t the loads of tile t+P are issued into the stage tile t-1 used, so P-1
 //    tiles are in flight while one is computed; one barrier per tile.
-//  * Lazy rescaling: the max used in the exponent is raised only when some
-//    row's true max exceeds it by more than 2^8 (a wave-uniform branch), so
-//    P <= 256 and the accumulator is rescaled on a few tiles only.  The final
-//    O = acc / l and LSE use the same max, so the result is exact up to
-//    rounding.
+//  * Lazy, optimistic rescaling: the first tile sets the max used in the
+//    exponent; later tiles take their exponentials against it without
+//    computing their own max, and only when a tile's sum of P exceeds 2^24
+//    (some score more than 24 above the max in use, or an overflow; a
+//    wave-uniform branch) is that tile's true max taken, the state rescaled
+//    and the tile's exponentials recomputed.  The final O = acc / l and LSE
+//    use the same max, so the result is exact up to rounding.
 //  * GQA/MQA: a workgroup serves one kv head.  Its MFMA columns enumerate
 //    (query row, query head) pairs of that kv group, row-major with the G =
 //    H_q/H_kv heads fastest, so every K/V tile in LDS serves all G heads and a
@@ -97,6 +99,7 @@ struct BoolTag {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays <= 2^8
+constexpr float kOverflowSum = 16777216.0f;  // 2^24: largest tile sum of P taken without a rescale
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 for gfx9 (untyped dword access)
 
 // instruction classes for __builtin_amdgcn_sched_group_barrier
@@ -400,17 +403,21 @@ void attn_fwd_kernel(FwdParams p) {
   // of S(t+1).
   auto step = [&](int t, Scores& sc, Scores& sn, auto has_next_tag) {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
-    float m_sub[QB];
+    float m_sub[QB], l_t[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) m_sub[qb] = (m_used[qb] == -INFINITY) ? 0.f : m_used[qb];
+    for (int qb = 0; qb < QB; ++qb) {
+      m_sub[qb] = (m_used[qb] == -INFINITY) ? 0.f : m_used[qb];
+      l_t[qb] = 0.f;
+    }
     bf16x8 pb[QB][BN / 16];
     f32x8 pf[QB];
-    // exponential number j of this tile: query block j / NV, element j % NV
+    // exponential number j of this tile: query block j / NV, element j % NV,
+    // taken against the max in use (no max of this tile is computed here)
     auto p_elem = [&](int j) {
       const int qb = j / NV, e = j % NV;
       const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 4][qb][e & 15], sl2, -m_sub[qb]));
       pf[qb][e & 7] = pe;
-      l_run[qb] += pe;
+      l_t[qb] += pe;
       if ((e & 7) == 7) pb[qb][e >> 3] = __builtin_convertvector(pf[qb], bf16x8);
     };
     if constexpr (HAS_NEXT) {
@@ -436,13 +443,37 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < QB * NV; ++j) p_elem(j);
     }
+    // A tile sum above 2^24 means some score exceeds the max in use by more
+    // than 24 (log2 units), or overflowed: take this tile's true max, rescale
+    // the state and recompute the tile's exponentials (rare: the first tile
+    // sets the max, and scores rarely climb that far above it).
+    bool big = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) big |= !(l_t[qb] <= kOverflowSum);
+    if (__builtin_amdgcn_ballot_w64(big)) {
+      float mx[QB];
+      lane_max(sc, mx);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mt = half_swap_max(mx[qb]) * sl2;
+        const float m_new = fmaxf(m_used[qb], mt);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used[qb] - m_new);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db][qb] *= alpha;
+        m_used[qb] = m_new;
+        m_sub[qb] = (m_new == -INFINITY) ? 0.f : m_new;
+        l_t[qb] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < QB * NV; ++j) p_elem(j);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += l_t[qb];
     // O^T += V^T P^T; k-step st covers keys 16 st .. 16 st + 15
     bf16x8 vx[PF + 1];
 #pragma unroll
     for (int i = 0; i < PF; ++i) vx[i] = v_read(t, i);
-    float mx[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mx[qb] = HAS_NEXT ? sn[0][qb][0] : 0.f;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       if (i + PF < NP) vx[(i + PF) % (PF + 1)] = v_read(t, i + PF);
@@ -450,23 +481,10 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx[i % (PF + 1)], pb[qb][st], acc[db][qb], 0, 0, 0);
-      if constexpr (HAS_NEXT) {
-#pragma unroll
-        for (int e = 0; e < MPR; ++e) {
-          const int j = i * MPR + e;
-          const int qb = j / NV, el = j % NV;
-          if (el > 0) mx[qb] = fmaxf(mx[qb], sn[el >> 4][qb][el & 15]);
-        }
-      }
     }
+    // a diagonal or ragged next tile is masked before its exponentials
     if constexpr (HAS_NEXT) {
-      // the max above ran over unmasked scores; a diagonal or ragged tile is
-      // masked here (rare) and its max taken again
-      if (needs_mask(t + 1)) {
-        apply_mask(t + 1, sn);
-        lane_max(sn, mx);
-      }
-      update_max(mx);
+      if (needs_mask(t + 1)) apply_mask(t + 1, sn);
     }
   };
 
