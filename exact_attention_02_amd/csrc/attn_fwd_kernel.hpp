@@ -244,21 +244,23 @@ void attn_fwd_kernel(FwdParams p) {
   // ---- query fragments (B operands of S^T = K Q^T): in query block qb the
   //      lane holds pair wp0 + 32 qb + col = (row, head g*G + j), d = 16*ks +
   //      8*half .. +8.  Pairs past the end are clamped to the last one.
+  // (b * H_q + h) * N_q + row of query block qb's pair (recomputed where
+  // needed rather than kept live through the tile loop)
+  auto bhr_of = [&](int qb) {
+    const int pc = min(wp0 + 32 * qb + col, last_pair);
+    const int row = pc / G;
+    const int h = g * G + (pc - row * G);
+    return ((size_t)b * p.H_q + h) * (size_t)p.N_q + row;
+  };
   int my_row[QB];
-  bool my_valid[QB];
-  size_t my_bhr[QB];  // (b * H_q + h) * N_q + row
   bf16x8 qf[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int pair = wp0 + 32 * qb + col;
-    my_valid[qb] = pair <= last_pair;
-    const int pc = min(pair, last_pair);
-    my_row[qb] = pc / G;
-    const int h = g * G + (pc - my_row[qb] * G);
-    my_bhr[qb] = ((size_t)b * p.H_q + h) * (size_t)p.N_q + my_row[qb];
+    my_row[qb] = min(wp0 + 32 * qb + col, last_pair) / G;
+    const size_t bhr = bhr_of(qb);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(p.q + my_bhr[qb] * D + ks * 16 + half * 8);
+      u32x4 x = *reinterpret_cast<const u32x4*>(p.q + bhr * D + ks * 16 + half * 8);
       x ^= p.q_sign;
       qf[qb][ks] = as_bf16x8(x);
     }
@@ -553,10 +555,11 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = half_swap_sum(l_run[qb]);
-    if (!my_valid[qb]) continue;
+    if (wp0 + 32 * qb + col > last_pair) continue;
+    const size_t bhr = bhr_of(qb);
     if constexpr (!SPLIT) {
       const float inv = 1.f / l_tot;
-      uint16_t* orow = p.o + my_bhr[qb] * D;
+      uint16_t* orow = p.o + bhr * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -567,11 +570,11 @@ void attn_fwd_kernel(FwdParams p) {
           const bf16x4 bv = __builtin_convertvector(f, bf16x4);
           *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, bv);
         }
-      if (half == 0) p.lse[my_bhr[qb]] = (m_used[qb] + __log2f(l_tot)) * kLn2;
+      if (half == 0) p.lse[bhr] = (m_used[qb] + __log2f(l_tot)) * kLn2;
     } else {
       const bool seen = l_tot > 0.f;
       const float inv = seen ? 1.f / l_tot : 0.f;
-      const size_t slot = (size_t)split * ((size_t)p.B * p.H_q * p.N_q) + my_bhr[qb];
+      const size_t slot = (size_t)split * ((size_t)p.B * p.H_q * p.N_q) + bhr;
       float* orow = p.o_part + slot * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
