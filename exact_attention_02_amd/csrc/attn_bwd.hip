@@ -16,10 +16,11 @@ namespace {
 using ea02::BwdParams;
 
 // dK/dV: four waves of 32 keys (128 keys per workgroup), 64-row tiles of Q and
-// dO, four LDS stages (136 KiB at D=128).  dQ: four waves of 32 (row, head)
-// pairs, 64-key tiles of K and V, four stages (128 KiB at D=128).
+// dO, four LDS stages (136 KiB at D=128).  dQ: eight waves of 32 (row, head)
+// pairs (256 per workgroup, two waves per SIMD), 64-key tiles of K and V, four
+// stages (128 KiB at D=128).
 constexpr int kKvNW = 4, kKvP = 4, kKvBP = 64;
-constexpr int kQNW = 4, kQP = 4, kQBN = 64;
+constexpr int kQNW = 8, kQP = 4, kQBN = 64;
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || !na || !nb) return false;
