@@ -194,12 +194,13 @@ def time_backward(ea, torch, w, steps, warmup):
     qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), dO.to(dev)
     out, lse = ea.fwd_splitkv(qd, kd, vd, is_causal=w.causal, sm_scale=w.sm_scale, n_splits=1)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-    ws = torch.empty((max(ea.attn_bwd_workspace_size(w.B, w.H_q, w.Nq), 1),), dtype=torch.uint8,
-                     device=dev)
+    ns = max(ea.attn_bwd_num_splits(w.B, w.H_q, w.H_kv, w.Nq, w.N, w.D, w.causal), 1)
+    ws = torch.empty((max(ea.attn_bwd_workspace_size(w.B, w.H_q, w.H_kv, w.Nq, w.N, w.D, ns), 1),),
+                     dtype=torch.uint8, device=dev)
 
     def step():
         ea.attn_bwd(qd, kd, vd, out, dod, lse, dq, dk, dv, is_causal=w.causal,
-                    sm_scale=w.sm_scale, workspace=ws)
+                    sm_scale=w.sm_scale, n_splits=ns, workspace=ws)
     for _ in range(warmup):
         step()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -212,7 +213,7 @@ def time_backward(ea, torch, w, steps, warmup):
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return {"wall_ms_per_step": wall * 1e3 / steps,
+    return {"wall_ms_per_step": wall * 1e3 / steps, "n_splits": ns,
             "event_ms": [s_.elapsed_time(e) for s_, e in zip(starts, ends)]}
 
 
@@ -341,7 +342,7 @@ def main():
             e = float(np.median(r["event_ms"]))
             tf = 2.5 * ww.flops() / (e * 1e-3) / 1e12
             log(f"[bwd] {name:24s} median {e:9.4f} ms  min {min(r['event_ms']):9.4f} ms  "
-                f"{tf:8.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:5.1f}%)")
+                f"{tf:8.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:5.1f}%)  splits {r['n_splits']}")
         return
 
     w = workloads.WORKLOADS[args.workload]

@@ -23,14 +23,16 @@ import os
 from .build import LIB_PATH
 
 __all__ = ["attn_fwd", "fwd", "attn_fwd_splitkv", "fwd_splitkv", "attn_splitkv_num_splits",
-           "attn_splitkv_workspace_size", "attn_bwd", "bwd", "attn_bwd_workspace_size",
+           "attn_splitkv_workspace_size", "attn_bwd", "bwd", "attn_bwd_num_splits",
+           "attn_bwd_workspace_size",
            "attn_mla_decode", "attn_mla_num_splits", "attn_mla_workspace_size", "mla_absorb_q",
            "mla_up_project", "mla_decode",
            "attn_status_string", "attn_abi_version",
            "load_library", "AttnError", "EXPORTED_SYMBOLS"]
 
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splitkv", "attn_splitkv_num_splits",
-                    "attn_splitkv_workspace_size", "attn_bwd", "attn_bwd_workspace_size",
+                    "attn_splitkv_workspace_size", "attn_bwd", "attn_bwd_num_splits",
+                    "attn_bwd_workspace_size",
                     "attn_mla_decode", "attn_mla_num_splits", "attn_mla_workspace_size",
                     "mla_absorb_q", "mla_up_project", "attn_status_string", "attn_abi_version")
 
@@ -65,9 +67,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 5
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 6 + [
-        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_bwd_num_splits.restype = ctypes.c_int64
+    lib.attn_bwd_num_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
-    lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int64] * 3
+    lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int64] * 7
     lib.attn_mla_decode.restype = ctypes.c_int
     lib.attn_mla_decode.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t,
@@ -225,14 +229,24 @@ def fwd_splitkv(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
     return out, lse
 
 
-def attn_bwd_workspace_size(B: int, H_q: int, N_q: int) -> int:
-    """Workspace bytes attn_bwd needs (per query row: log2-unit LSE and rowsum(dO*O))."""
-    return int(load_library().attn_bwd_workspace_size(B, H_q, N_q))
+def attn_bwd_num_splits(B: int, H_q: int, H_kv: int, N_q: int, N_kv: int, D: int,
+                        is_causal: bool = False) -> int:
+    """Row-range split count attn_bwd picks for n_splits=0 on the current device."""
+    return int(load_library().attn_bwd_num_splits(B, H_q, H_kv, N_q, N_kv, D, int(bool(is_causal))))
+
+
+def attn_bwd_workspace_size(B: int, H_q: int, H_kv: int, N_q: int, N_kv: int, D: int,
+                            n_splits: int = 1) -> int:
+    """Workspace bytes attn_bwd needs with n_splits row ranges (per query row:
+    log2-unit LSE and rowsum(dO*O); per range: fp32 partial dK and dV)."""
+    return int(load_library().attn_bwd_workspace_size(B, H_q, H_kv, N_q, N_kv, D, n_splits))
 
 
 def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, is_causal: bool = False,
-             sm_scale: float | None = None, workspace=None, stream=None) -> None:
-    """Enqueue the backward into dq, dk, dv (workspace: attn_bwd_workspace_size bytes)."""
+             sm_scale: float | None = None, n_splits: int = 1, workspace=None,
+             stream=None) -> None:
+    """Enqueue the backward into dq, dk, dv (workspace: attn_bwd_workspace_size
+    bytes for the split count used; n_splits=0 lets the library choose)."""
     import torch
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, D]")
@@ -265,23 +279,28 @@ def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, is_causal: bool = False,
         st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                           B, H_q, H_kv, N_q, N_kv, D, float(sm_scale), int(bool(is_causal)),
-                          ws_ptr, ws_bytes, handle)
+                          int(n_splits), ws_ptr, ws_bytes, handle)
     if st != 0:
         raise AttnError(st, attn_status_string(st))
 
 
 def bwd(q, k, v, out, dout, lse, is_causal: bool = False, sm_scale: float | None = None,
         stream=None):
-    """Allocate dq, dk, dv and the workspace, run attn_bwd, return (dq, dk, dv)."""
+    """Allocate dq, dk, dv and the workspace, run attn_bwd with the library's
+    split count, return (dq, dk, dv)."""
     import torch
     B, H_q, N_q, D = q.shape
+    H_kv, N_kv = k.shape[1], k.shape[2]
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    nbytes = attn_bwd_workspace_size(B, H_q, N_q)
+    with torch.cuda.device(q.device):
+        ns = attn_bwd_num_splits(B, H_q, H_kv, N_q, N_kv, D, is_causal)
+    ns = max(ns, 1)
+    nbytes = attn_bwd_workspace_size(B, H_q, H_kv, N_q, N_kv, D, ns)
     ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
     attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, is_causal=is_causal, sm_scale=sm_scale,
-             workspace=ws, stream=stream)
+             n_splits=ns, workspace=ws, stream=stream)
     return dq, dk, dv
 
 

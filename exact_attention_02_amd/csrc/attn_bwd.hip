@@ -6,6 +6,7 @@
 #include <cfloat>
 #include <cmath>
 #include <cstddef>
+#include <algorithm>
 #include <cstdint>
 
 #include "../../include/attn.h"
@@ -22,14 +23,99 @@ using ea02::BwdParams;
 constexpr int kKvNW = 4, kKvP = 4, kKvBP = 64;
 constexpr int kQNW = 8, kQP = 4, kQBN = 64;
 
+// Row-range splits of the dK/dV kernel: at most this many per key block.
+constexpr int64_t kMaxBwdSplits = 64;
+// Partial sums of the library's own choice take at most this much workspace.
+constexpr int64_t kAutoPartBytes = int64_t(1) << 30;
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || !na || !nb) return false;
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
 }
 
-// Prep, dK/dV, dQ.  With no query rows only the dK/dV kernel runs: every key
-// block then has no row tile and writes zeros.
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+
+struct Shape {
+  int64_t B, H_q, H_kv, N_q, N_kv, D;
+  int causal;
+};
+
+// Size checks shared by attn_bwd and attn_bwd_num_splits (everything up to
+// and including SIZE_OVERFLOW); *empty is set when there is nothing to do.
+int check_sizes(const Shape& a, int64_t n_splits, float sm_scale, bool* empty) {
+  *empty = false;
+  if (a.B < 0 || a.H_q < 0 || a.H_kv < 0 || a.N_q < 0 || a.N_kv < 0 || a.D < 0 || n_splits < 0)
+    return ATTN_ERR_NEGATIVE_SIZE;
+  if (a.H_kv < 1 || a.H_q % a.H_kv != 0) return ATTN_ERR_HEAD_RATIO;
+  if (a.D != 64 && a.D != 128) return ATTN_ERR_HEAD_DIM;
+  if (a.causal != 0 && a.causal != 1) return ATTN_ERR_CAUSAL_FLAG;
+  if (!std::isfinite(sm_scale)) return ATTN_ERR_SCALE;
+  if (n_splits > kMaxBwdSplits) return ATTN_ERR_SPLITS;
+  if (a.causal && a.N_q > a.N_kv) return ATTN_ERR_CAUSAL_SHAPE;
+  const int64_t lim24 = int64_t(1) << 24;
+  const int64_t G = a.H_q / a.H_kv;
+  // one kv group's Q / dO rows and one kv head's K / V rows take 32-bit byte offsets
+  if (a.N_q > lim24 || a.N_kv > lim24 || a.B > lim24 || a.H_q > (int64_t(1) << 16) ||
+      a.N_kv * a.D * 2 > (int64_t(1) << 31) || a.N_q * G * a.D * 2 > (int64_t(1) << 31) ||
+      a.B * a.H_q * a.N_q > INT32_MAX)
+    return ATTN_ERR_SIZE_OVERFLOW;
+  const int64_t key_blocks = (a.N_kv + 32 * kKvNW - 1) / (32 * kKvNW);
+  const int64_t pair_blocks = (a.N_q * G + 32 * kQNW - 1) / (32 * kQNW);
+  const int64_t splits = n_splits > 1 ? n_splits : 1;
+  if (a.B * a.H_kv * key_blocks * splits > INT32_MAX || a.B * a.H_kv * pair_blocks > INT32_MAX)
+    return ATTN_ERR_SIZE_OVERFLOW;
+  if (a.B == 0 || a.H_q == 0 || (a.N_q == 0 && a.N_kv == 0)) *empty = true;
+  return ATTN_OK;
+}
+
+// Row tiles (BP query rows of one head) that key block kb visits.
+int64_t kv_block_tiles(const Shape& a, int64_t kb) {
+  const int64_t off = a.causal ? a.N_kv - a.N_q : 0;
+  const int64_t r_start = a.causal ? std::max<int64_t>(0, kb * 32 * kKvNW - off) : 0;
+  return (a.H_q / a.H_kv) * ((a.N_q - r_start + kKvBP - 1) / kKvBP);
+}
+
+// The library's split count: 1 while the key blocks already fill every CU
+// (one dK/dV workgroup per CU); otherwise the heaviest key block is cut into
+// ranges no longer than an even share of all tiles per CU (and at least 4
+// tiles), capped at kMaxBwdSplits and at 1 GiB of partial sums.
+int64_t choose_kv_splits(const Shape& a) {
+  if (a.N_q == 0 || a.N_kv == 0 || a.B == 0 || a.H_q == 0) return 1;
+  const int64_t key_blocks = (a.N_kv + 32 * kKvNW - 1) / (32 * kKvNW);
+  const int64_t heads = a.B * a.H_kv;
+  const int64_t cus = device_cus();
+  if (heads * key_blocks >= cus) return 1;
+  int64_t total = 0;
+  for (int64_t kb = 0; kb < key_blocks; ++kb) total += kv_block_tiles(a, kb);
+  total *= heads;
+  const int64_t tiles_max = kv_block_tiles(a, 0);
+  const int64_t share = std::max<int64_t>((total + cus - 1) / cus, 4);
+  int64_t n = (tiles_max + share - 1) / share;
+  n = std::min({n, tiles_max, kMaxBwdSplits});
+  const int64_t plane2 = 2 * heads * a.N_kv * a.D * 4;
+  n = std::min(n, kAutoPartBytes / plane2);
+  return std::max<int64_t>(n, 1);
+}
+
+size_t row_stat_bytes(int64_t B, int64_t H_q, int64_t N_q) { return size_t(B) * size_t(H_q) * size_t(N_q) * 8; }
+
+size_t part_offset(int64_t B, int64_t H_q, int64_t N_q) { return (row_stat_bytes(B, H_q, N_q) + 255) & ~size_t(255); }
+
+size_t workspace_bytes(const Shape& a, int64_t n_splits) {
+  const size_t stats = row_stat_bytes(a.B, a.H_q, a.N_q);
+  if (n_splits <= 1) return stats;
+  return part_offset(a.B, a.H_q, a.N_q) + size_t(n_splits) * 2 * size_t(a.B * a.H_kv * a.N_kv * a.D) * 4;
+}
+
+// Prep, dK/dV (+ the sum of its splits), dQ.  With no query rows only the
+// dK/dV kernel runs: every key block then has no row tile and writes zeros.
 template <int D>
 hipError_t launch_all(const BwdParams& p, hipStream_t s) {
   hipError_t e;
@@ -39,8 +125,15 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL((ea02::attn_bwd_dkdv_kernel<D, kKvNW, kKvP, kKvBP>),
-                     dim3(static_cast<unsigned>(p.n_heads_wg * p.n_key_blocks)), dim3(kKvNW * 64), 0, s, p);
+                     dim3(static_cast<unsigned>(p.n_heads_wg * p.n_key_blocks * p.n_kv_splits)), dim3(kKvNW * 64),
+                     0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.n_kv_splits > 1) {
+    const int64_t quads = int64_t(p.n_heads_wg) * p.N_kv * D / 4;
+    hipLaunchKernelGGL((ea02::attn_bwd_kv_reduce_kernel<D>), dim3(static_cast<unsigned>((quads + 255) / 256)), dim3(256),
+                       0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (p.rows > 0) {
     hipLaunchKernelGGL((ea02::attn_bwd_dq_kernel<D, kQNW, kQP, kQBN>),
                        dim3(static_cast<unsigned>(p.n_heads_wg * p.n_pair_blocks)), dim3(kQNW * 64), 0, s, p);
@@ -51,32 +144,35 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s) {
 
 }  // namespace
 
-extern "C" size_t attn_bwd_workspace_size(int64_t B, int64_t H_q, int64_t N_q) {
-  if (B < 0 || H_q < 0 || N_q < 0) return 0;
-  return size_t(B) * size_t(H_q) * size_t(N_q) * 8;
+extern "C" int64_t attn_bwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t D,
+                                       int is_causal) {
+  const Shape a{B, H_q, H_kv, N_q, N_kv, D, is_causal};
+  bool empty = false;
+  if (check_sizes(a, 0, 1.f, &empty) != ATTN_OK) return -1;
+  if (empty) return 1;
+  return choose_kv_splits(a);
+}
+
+extern "C" size_t attn_bwd_workspace_size(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv,
+                                          int64_t D, int64_t n_splits) {
+  if (B < 0 || H_q < 0 || H_kv < 0 || N_q < 0 || N_kv < 0 || D < 0 || n_splits < 0 || n_splits > kMaxBwdSplits)
+    return 0;
+  if (B > (int64_t(1) << 24) || H_q > (int64_t(1) << 16) || N_q > (int64_t(1) << 24) ||
+      N_kv > (int64_t(1) << 24) || D > 128)
+    return 0;
+  const Shape a{B, H_q, H_kv, N_q, N_kv, D, 0};
+  return workspace_bytes(a, n_splits);
 }
 
 extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                         const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q, int64_t H_kv,
-                        int64_t N_q, int64_t N_kv, int64_t D, float sm_scale, int is_causal, void* workspace,
-                        size_t workspace_size, void* stream) {
-  if (B < 0 || H_q < 0 || H_kv < 0 || N_q < 0 || N_kv < 0 || D < 0) return ATTN_ERR_NEGATIVE_SIZE;
-  if (H_kv < 1 || H_q % H_kv != 0) return ATTN_ERR_HEAD_RATIO;
-  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
-  if (is_causal != 0 && is_causal != 1) return ATTN_ERR_CAUSAL_FLAG;
-  if (!std::isfinite(sm_scale)) return ATTN_ERR_SCALE;
-  if (is_causal && N_q > N_kv) return ATTN_ERR_CAUSAL_SHAPE;
-  const int64_t lim24 = int64_t(1) << 24;
-  const int64_t G = H_kv > 0 ? H_q / H_kv : 0;
-  // one kv group's Q / dO rows and one kv head's K / V rows take 32-bit byte offsets
-  if (N_q > lim24 || N_kv > lim24 || B > lim24 || H_q > (int64_t(1) << 16) ||
-      N_kv * D * 2 > (int64_t(1) << 31) || N_q * G * D * 2 > (int64_t(1) << 31) ||
-      B * H_q * N_q > INT32_MAX)
-    return ATTN_ERR_SIZE_OVERFLOW;
-  const int64_t key_blocks = (N_kv + 32 * kKvNW - 1) / (32 * kKvNW);
-  const int64_t pair_blocks = (N_q * G + 32 * kQNW - 1) / (32 * kQNW);
-  if (B * H_kv * key_blocks > INT32_MAX || B * H_kv * pair_blocks > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
-  if (B == 0 || H_q == 0 || (N_q == 0 && N_kv == 0)) return ATTN_OK;
+                        int64_t N_q, int64_t N_kv, int64_t D, float sm_scale, int is_causal, int64_t n_splits,
+                        void* workspace, size_t workspace_size, void* stream) {
+  const Shape a{B, H_q, H_kv, N_q, N_kv, D, is_causal};
+  bool empty = false;
+  int st = check_sizes(a, n_splits, sm_scale, &empty);
+  if (st != ATTN_OK) return st;
+  if (empty) return ATTN_OK;
   if (N_kv == 0) return ATTN_ERR_NO_KEYS;
   // with no query rows q, out, dout, lse and dq are empty and may be NULL
   if (!k || !v || !dk || !dv || (N_q > 0 && (!q || !out || !dout || !lse || !dq))) return ATTN_ERR_NULL_POINTER;
@@ -84,9 +180,12 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   if (mis16(q) || mis16(k) || mis16(v) || mis16(out) || mis16(dout) || mis16(dq) || mis16(dk) || mis16(dv) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u))
     return ATTN_ERR_ALIGNMENT;
-  const size_t need = attn_bwd_workspace_size(B, H_q, N_q);
+  // no query rows: nothing to split (the key blocks write zeros)
+  const int64_t splits = N_q == 0 ? 1 : (n_splits == 0 ? choose_kv_splits(a) : n_splits);
+  const size_t need = workspace_bytes(a, splits);
   if (need > 0 && (!workspace || workspace_size < need || (reinterpret_cast<uintptr_t>(workspace) & 15u)))
     return ATTN_ERR_WORKSPACE;
+  const int64_t G = H_q / H_kv;
   const size_t nq = size_t(B * H_q * N_q * D) * 2, nkv = size_t(B * H_kv * N_kv * D) * 2;
   const size_t nl = size_t(B * H_q * N_q) * 4;
   const void* ins[6] = {q, k, v, out, dout, lse};
@@ -112,6 +211,8 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   p.dv = static_cast<uint16_t*>(dv);
   p.lse2 = static_cast<float*>(workspace);
   p.delta = static_cast<float*>(workspace) + size_t(B * H_q * N_q);
+  p.kv_part = splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + part_offset(B, H_q, N_q))
+                         : nullptr;
   p.B = static_cast<int>(B);
   p.H_q = static_cast<int>(H_q);
   p.H_kv = static_cast<int>(H_kv);
@@ -122,8 +223,9 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   p.causal_off = is_causal ? static_cast<int>(N_kv - N_q) : 0;
   p.causal = is_causal;
   p.n_heads_wg = static_cast<int>(B * H_kv);
-  p.n_key_blocks = static_cast<int>(key_blocks);
-  p.n_pair_blocks = static_cast<int>(pair_blocks);
+  p.n_key_blocks = static_cast<int>((N_kv + 32 * kKvNW - 1) / (32 * kKvNW));
+  p.n_kv_splits = static_cast<int>(splits);
+  p.n_pair_blocks = static_cast<int>((N_q * G + 32 * kQNW - 1) / (32 * kQNW));
   // as in the forward: a zero scale becomes FLT_MIN in the exponent (uniform
   // weights, no 0 * inf); the gradient factors use the scale as given
   p.scale_log2 = std::fmax(std::fabs(sm_scale) * ea02::kLog2e, FLT_MIN);

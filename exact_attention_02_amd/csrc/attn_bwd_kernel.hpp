@@ -15,7 +15,11 @@
 //  * attn_bwd_dkdv_kernel: a workgroup owns 32 keys per wave of one kv head;
 //    K and V of those keys stay in registers while the query rows of every
 //    head of the group stream through LDS (head-major, so each tile is
-//    contiguous rows of one head).  Products are taken with the rows of the
+//    contiguous rows of one head).  When the key blocks alone are too few to
+//    fill the device (one kv head, short sequences), a key block's sequence
+//    of row tiles is cut into n_kv_splits contiguous ranges, one workgroup
+//    each, writing fp32 partial sums; attn_bwd_kv_reduce_kernel adds them in
+//    range order (still deterministic).  Products are taken with the rows of the
 //    MFMA accumulator being query rows and its columns keys (a lane owns one
 //    key): S = Q K^T and dP = dO V^T read Q and dO from LDS as A operands;
 //    dV^T = dO^T P and dK^T = Q^T dS read dO^T and Q^T with the LDS transpose
@@ -46,6 +50,8 @@ struct BwdParams {
   uint16_t* dv;          // [B, H_kv, N_kv, D]
   float* lse2;           // [B, H_q, N_q] workspace: L log2(e)
   float* delta;          // [B, H_q, N_q] workspace: rowsum(dO * O)
+  float* kv_part;        // [n_kv_splits, 2, B, H_kv, N_kv, D] fp32 workspace (dK scaled, dV)
+                         // of the row-range splits; unused when n_kv_splits == 1
   int B, H_q, H_kv, N_q, N_kv;
   int G;                 // H_q / H_kv
   int n_pairs;           // N_q * G
@@ -53,6 +59,7 @@ struct BwdParams {
   int causal;
   int n_heads_wg;        // B * H_kv
   int n_key_blocks;      // dK/dV kernel: ceil(N_kv / keys per workgroup)
+  int n_kv_splits;       // dK/dV kernel: workgroups sharing one key block's row tiles
   int n_pair_blocks;     // dQ kernel: ceil(n_pairs / pairs per workgroup)
   float scale_log2;      // max(|sm_scale| log2(e), FLT_MIN)
   float grad_scale;      // sm_scale (signed): factor of dQ and dK
@@ -135,10 +142,13 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // heaviest key blocks first (causal: block 0 sees every row), kv heads fastest
+  // heaviest key blocks first (causal: block 0 sees every row), kv heads
+  // fastest, then the row-range splits of one key block
   const int bid = blockIdx.x;
   const int head_wg = bid % p.n_heads_wg;
-  const int kb = bid / p.n_heads_wg;
+  const int rest = bid / p.n_heads_wg;
+  const int split = rest % p.n_kv_splits;
+  const int kb = rest / p.n_kv_splits;
   const int g = head_wg % p.H_kv;
   const int b = head_wg / p.H_kv;
   const int G = p.G;
@@ -152,6 +162,9 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   const int r_start = p.causal ? max(0, k0 - off) : 0;
   const int n_rt = (N_q - r_start + BP - 1) / BP;
   const int n_tiles = G * n_rt;
+  // this workgroup's contiguous range of the G * n_rt (head, row tile) tiles
+  const int t_lo = (int)(((int64_t)n_tiles * split) / p.n_kv_splits);
+  const int t_hi = (int)(((int64_t)n_tiles * (split + 1)) / p.n_kv_splits);
 
   // K and V of this lane's key: B operands of S = Q K^T and dP = dO V^T
   const size_t kv_base = ((size_t)b * p.H_kv + g) * (size_t)N_kv * D;
@@ -285,22 +298,42 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // Load ring: tile t goes to slot t % P, issued P-1 tiles ahead; past the
-  // last tile a clamped tile is re-loaded so every wait is one constant vmcnt.
-  if (n_tiles > 0) {
+  // Load ring: the i-th tile of the range goes to slot i % P, issued P-1
+  // tiles ahead; past the range's end a clamped tile is re-loaded so every
+  // wait is one constant vmcnt.
+  const int n_mine = t_hi - t_lo;
+  if (n_mine > 0) {
 #pragma unroll
-    for (int j = 0; j < P - 1; ++j) issue(min(j, n_tiles - 1), j);
-    for (int t = 0; t < n_tiles; ++t) {
+    for (int j = 0; j < P - 1; ++j) issue(t_lo + min(j, n_mine - 1), j);
+    for (int i = 0; i < n_mine; ++i) {
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 2) * C::GROUP_LOADS) : "memory");
       __syncthreads();
-      issue(min(t + P - 1, n_tiles - 1), (t + P - 1) % P);
-      compute(t, t % P);
+      issue(t_lo + min(i + P - 1, n_mine - 1), (i + P - 1) % P);
+      compute(t_lo + i, i % P);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may outlive the workgroup
   }
 
-  // dK^T, dV^T: the lane holds key my_key, d = db*32 + 8(r/4) + 4 half + r%4
-  if (my_key < N_kv) {
+  // dK^T, dV^T: the lane holds key my_key, d = db*32 + 8(r/4) + 4 half + r%4.
+  // A split writes its fp32 partial sums (a range with no tile writes zeros).
+  if (p.n_kv_splits > 1) {
+    if (my_key < N_kv) {
+      const size_t plane = (size_t)p.n_heads_wg * N_kv * D;
+      float* pk = p.kv_part + 2 * (size_t)split * plane + kv_base + (size_t)my_key * D;
+      float* pv = pk + plane;
+      const float gs = p.grad_scale;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * half;
+          f32x4 fk = {dkT[db][4 * g4] * gs, dkT[db][4 * g4 + 1] * gs, dkT[db][4 * g4 + 2] * gs, dkT[db][4 * g4 + 3] * gs};
+          f32x4 fv = {dvT[db][4 * g4], dvT[db][4 * g4 + 1], dvT[db][4 * g4 + 2], dvT[db][4 * g4 + 3]};
+          *reinterpret_cast<f32x4*>(pk + d0) = fk;
+          *reinterpret_cast<f32x4*>(pv + d0) = fv;
+        }
+    }
+  } else if (my_key < N_kv) {
     uint16_t* dkr = p.dk + kv_base + (size_t)my_key * D;
     uint16_t* dvr = p.dv + kv_base + (size_t)my_key * D;
     const float gs = p.grad_scale;
@@ -315,6 +348,24 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
         *reinterpret_cast<u32x2*>(dvr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(fv, bf16x4));
       }
   }
+}
+
+// ---------------------------------------------------------------- split sums
+// dK, dV = sum over the row-range splits of the partials, in split order;
+// 4 elements per thread (16-byte loads), rounded to bf16 when stored.
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void attn_bwd_kv_reduce_kernel(BwdParams p) {
+  const size_t plane = (size_t)p.n_heads_wg * p.N_kv * D;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= plane) return;
+  f32x4 sk = *reinterpret_cast<const f32x4*>(p.kv_part + i);
+  f32x4 sv = *reinterpret_cast<const f32x4*>(p.kv_part + plane + i);
+  for (int s = 1; s < p.n_kv_splits; ++s) {
+    sk += *reinterpret_cast<const f32x4*>(p.kv_part + 2 * (size_t)s * plane + i);
+    sv += *reinterpret_cast<const f32x4*>(p.kv_part + (2 * (size_t)s + 1) * plane + i);
+  }
+  *reinterpret_cast<u32x2*>(p.dk + i) = __builtin_bit_cast(u32x2, __builtin_convertvector(sk, bf16x4));
+  *reinterpret_cast<u32x2*>(p.dv + i) = __builtin_bit_cast(u32x2, __builtin_convertvector(sv, bf16x4));
 }
 
 // ---------------------------------------------------------------- dQ

@@ -47,7 +47,7 @@ enum attn_status {
   ATTN_ERR_LAUNCH = 10,        /* the HIP runtime rejected the kernel launch   */
   ATTN_ERR_CAUSAL_SHAPE = 11,  /* is_causal with more query rows than keys     */
   ATTN_ERR_NO_KEYS = 12,       /* N_kv = 0 while there are query rows          */
-  ATTN_ERR_SPLITS = 13,        /* n_splits above 256                           */
+  ATTN_ERR_SPLITS = 13,        /* n_splits above the entry point's maximum   */
   ATTN_ERR_WORKSPACE = 14      /* split workspace NULL, too small or misaligned */
 };
 
@@ -176,18 +176,26 @@ size_t attn_splitkv_workspace_size(int64_t B, int64_t H_q, int64_t N_q, int64_t 
  *   dq            bf16 [B, H_q, N_q, D], written
  *   dk, dv        bf16 [B, H_kv, N_kv, D], written (zeros when N_q = 0)
  *   sm_scale, is_causal as for the forward that produced out and lse
+ *   n_splits      0 = the library's choice (attn_bwd_num_splits), 1 = none,
+ *                 2..64 = the query heads and rows a kv head's key block sees
+ *                 are cut into that many contiguous ranges, one workgroup
+ *                 each, whose fp32 partial dk and dv are summed in range order
+ *                 by one more kernel (a range may be empty)
  *   workspace     device scratch of at least attn_bwd_workspace_size(B, H_q,
- *                 N_q) bytes, 16-byte aligned (per row: L log2 e and Dl);
- *                 contents undefined on entry and after; calls that overlap on
- *                 one workspace race
+ *                 H_kv, N_q, N_kv, D, n_splits') bytes, 16-byte aligned, where
+ *                 n_splits' is the split count used (1 when N_q = 0): per row
+ *                 L log2 e and Dl, then the partial sums; contents undefined
+ *                 on entry and after; calls that overlap on one workspace race
  * All buffers are contiguous device memory of the current device.  Three
- * kernels are enqueued on `stream`; the call never synchronises.  The result
- * is deterministic (no atomics).
+ * kernels are enqueued on `stream` (four with splits); the call never
+ * synchronises.  The result is deterministic (no atomics) for a given split
+ * count; different split counts round differently.
  *
  * Errors, checked in this order; nothing is enqueued on failure:
- *   NEGATIVE_SIZE, HEAD_RATIO, HEAD_DIM, CAUSAL_FLAG, SCALE, CAUSAL_SHAPE,
- *   SIZE_OVERFLOW (N_q or N_kv > 2^24, N_kv*D*2 > 2^31, N_q*(H_q/H_kv)*D*2 >
- *   2^31, B*H_q*N_q >= 2^31, grid >= 2^31), then empty work (B or H_q = 0, or
+ *   NEGATIVE_SIZE (any size or n_splits < 0), HEAD_RATIO, HEAD_DIM,
+ *   CAUSAL_FLAG, SCALE, SPLITS (n_splits > 64), CAUSAL_SHAPE, SIZE_OVERFLOW
+ *   (N_q or N_kv > 2^24, N_kv*D*2 > 2^31, N_q*(H_q/H_kv)*D*2 > 2^31,
+ *   B*H_q*N_q >= 2^31, grid >= 2^31), then empty work (B or H_q = 0, or
  *   N_q = N_kv = 0) returns ATTN_OK, then NO_KEYS (N_kv = 0 < N_q),
  *   NULL_POINTER (q, out, dout, lse, dq may be NULL only when N_q = 0),
  *   ALIGNMENT (16 bytes, lse 4), WORKSPACE, ALIAS (dq, dk, dv or the workspace
@@ -195,12 +203,30 @@ size_t attn_splitkv_workspace_size(int64_t B, int64_t H_q, int64_t N_q, int64_t 
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H_q, int64_t H_kv,
-             int64_t N_q, int64_t N_kv, int64_t D, float sm_scale, int is_causal, void* workspace,
-             size_t workspace_size, void* stream);
+             int64_t N_q, int64_t N_kv, int64_t D, float sm_scale, int is_causal, int64_t n_splits,
+             void* workspace, size_t workspace_size, void* stream);
 
-/* attn_bwd_workspace_size -- bytes of workspace attn_bwd needs:
- * B * H_q * N_q * 8 (0 for negative sizes). */
-size_t attn_bwd_workspace_size(int64_t B, int64_t H_q, int64_t N_q);
+/*
+ * attn_bwd_num_splits -- the split count attn_bwd uses for n_splits = 0 on
+ * the current device: 1 when the dK/dV key blocks already give every CU a
+ * workgroup, otherwise enough ranges that the heaviest key block's share is
+ * no longer than an even share of all row tiles per CU (at least 4 tiles per
+ * range), at most 64 and at most 1 GiB of partial sums.  Returns -1 when the
+ * sizes fail attn_bwd's size checks (NEGATIVE_SIZE .. SIZE_OVERFLOW), 1 for
+ * empty work.  Queries the current device's CU count; enqueues nothing.
+ */
+int64_t attn_bwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t D,
+                            int is_causal);
+
+/*
+ * attn_bwd_workspace_size -- bytes of workspace attn_bwd needs with n_splits
+ * ranges: B * H_q * N_q * 8 when n_splits <= 1; otherwise that rounded up to
+ * a multiple of 256, plus n_splits * 2 * B * H_kv * N_kv * D * 4 (fp32 partial
+ * dk, then dv, per range).  0 for negative or too large sizes and for
+ * n_splits > 64.
+ */
+size_t attn_bwd_workspace_size(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t D,
+                               int64_t n_splits);
 
 /*
  * Multi-head latent attention (MLA) decode, absorbed form.  Page "Attention
@@ -273,8 +299,8 @@ int mla_up_project(const void* out_lat, const void* w_uv, void* out, int64_t B, 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);
 
-/* Library ABI version, currently 4 (1: attn_fwd; 2: + split-KV; 3: + backward;
- * 4: + MLA decode). */
+/* Library ABI version, currently 5 (1: attn_fwd; 2: + split-KV; 3: + backward;
+ * 4: + MLA decode; 5: backward row-range splits, attn_bwd_num_splits). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

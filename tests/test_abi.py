@@ -38,7 +38,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 4
+    assert lib.attn_abi_version() == 5
 
 
 def test_status_strings_distinct(lib):
@@ -205,9 +205,9 @@ DO, DQ, DK, DV, WB = (0x200000000 + i * 64 * MiB for i in range(5))
 
 
 def call_bwd(lib, q=Q, k=K, v=V, o=O, do=DO, l=L, dq=DQ, dk=DK, dv=DV, B=1, H_q=4, H_kv=2, N_q=16,
-             N_kv=40, D=64, scale=0.125, causal=0, ws=WB, ws_bytes=64 * MiB):
+             N_kv=40, D=64, scale=0.125, causal=0, n_splits=1, ws=WB, ws_bytes=64 * MiB):
     return lib.attn_bwd(q, k, v, o, do, l, dq, dk, dv, B, H_q, H_kv, N_q, N_kv, D,
-                        ctypes.c_float(scale), causal, ws, ws_bytes, None)
+                        ctypes.c_float(scale), causal, n_splits, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -216,6 +216,8 @@ def call_bwd(lib, q=Q, k=K, v=V, o=O, do=DO, l=L, dq=DQ, dk=DK, dv=DV, B=1, H_q=
     (dict(D=80), "ATTN_ERR_HEAD_DIM"),
     (dict(causal=5), "ATTN_ERR_CAUSAL_FLAG"),
     (dict(scale=float("nan")), "ATTN_ERR_SCALE"),
+    (dict(n_splits=-1), "ATTN_ERR_NEGATIVE_SIZE"),
+    (dict(n_splits=65), "ATTN_ERR_SPLITS"),
     (dict(causal=1, N_q=41), "ATTN_ERR_CAUSAL_SHAPE"),
     (dict(N_kv=(1 << 23) + 1, D=128), "ATTN_ERR_SIZE_OVERFLOW"),
     (dict(N_q=1 << 20, H_q=16, H_kv=1, D=128, N_kv=1 << 20), "ATTN_ERR_SIZE_OVERFLOW"),
@@ -227,6 +229,8 @@ def call_bwd(lib, q=Q, k=K, v=V, o=O, do=DO, l=L, dq=DQ, dk=DK, dv=DV, B=1, H_q=
     (dict(ws=0), "ATTN_ERR_WORKSPACE"),
     (dict(ws_bytes=100), "ATTN_ERR_WORKSPACE"),
     (dict(ws=WB + 4), "ATTN_ERR_WORKSPACE"),
+    (dict(n_splits=4, ws_bytes=4 * 2 * 2 * 40 * 64 * 4), "ATTN_ERR_WORKSPACE"),
+    (dict(n_splits=4, ws=DO - 1024), "ATTN_ERR_ALIAS"),
     (dict(dq=Q), "ATTN_ERR_ALIAS"),
     (dict(dk=DV), "ATTN_ERR_ALIAS"),
     (dict(ws=DO + 16), "ATTN_ERR_ALIAS"),
@@ -241,6 +245,11 @@ def test_bwd_check_order(lib):
     assert call_bwd(lib, q=0, N_kv=0) == STATUS["ATTN_ERR_NO_KEYS"]
     assert call_bwd(lib, q=0, ws=0) == STATUS["ATTN_ERR_NULL_POINTER"]
     assert call_bwd(lib, ws=0, dq=Q) == STATUS["ATTN_ERR_WORKSPACE"]
+    assert call_bwd(lib, n_splits=65, causal=1, N_q=41) == STATUS["ATTN_ERR_SPLITS"]
+    assert call_bwd(lib, n_splits=65, scale=float("inf")) == STATUS["ATTN_ERR_SCALE"]
+    # no query rows: nothing is split, so no workspace is needed whatever n_splits
+    # says (the call gets past the workspace check to the alias check)
+    assert call_bwd(lib, N_q=0, q=0, o=0, do=0, l=0, dq=0, ws=0, n_splits=8, dk=K) == STATUS["ATTN_ERR_ALIAS"]
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H_q=0, H_kv=1), dict(N_q=0, N_kv=0)])
@@ -255,9 +264,27 @@ def test_bwd_no_query_rows_needs_only_key_buffers(lib):
 
 
 def test_bwd_workspace_size():
-    assert ea.attn_bwd_workspace_size(2, 32, 1024) == 2 * 32 * 1024 * 8
-    assert ea.attn_bwd_workspace_size(1, 4, 0) == 0
-    assert ea.attn_bwd_workspace_size(-1, 4, 4) == 0
+    assert ea.attn_bwd_workspace_size(2, 32, 8, 1024, 1024, 128) == 2 * 32 * 1024 * 8
+    assert ea.attn_bwd_workspace_size(2, 32, 8, 1024, 1024, 128, 1) == 2 * 32 * 1024 * 8
+    assert ea.attn_bwd_workspace_size(1, 4, 4, 0, 10, 64) == 0
+    assert ea.attn_bwd_workspace_size(-1, 4, 4, 4, 4, 64) == 0
+    assert ea.attn_bwd_workspace_size(1, 4, 1, 4, 4, 64, 65) == 0
+    # row statistics rounded up to 256 bytes, then fp32 dK and dV partials per range
+    assert ea.attn_bwd_workspace_size(1, 3, 1, 5, 70, 64, 3) == 256 + 3 * 2 * 70 * 64 * 4
+    assert ea.attn_bwd_workspace_size(1, 16, 1, 512, 512, 128, 32) == 65536 + 32 * 2 * 512 * 128 * 4
+
+
+def test_bwd_num_splits():
+    # large grids are not split; one kv head over a short sequence is
+    assert ea.attn_bwd_num_splits(1, 32, 8, 32768, 32768, 128, True) == 1
+    assert ea.attn_bwd_num_splits(1, 16, 1, 512, 512, 128, True) > 1
+    assert 1 <= ea.attn_bwd_num_splits(1, 16, 1, 512, 512, 128, False) <= 64
+    assert ea.attn_bwd_num_splits(1, 4, 4, 0, 100, 64, True) == 1
+    assert ea.attn_bwd_num_splits(0, 4, 4, 10, 100, 64, True) == 1
+    assert ea.attn_bwd_num_splits(1, 5, 2, 10, 100, 64, True) == -1
+    assert ea.attn_bwd_num_splits(1, 4, 4, 10, 5, 64, True) == -1
+    # at most one range per row tile of the heaviest key block (4 heads x 1 tile)
+    assert ea.attn_bwd_num_splits(1, 4, 1, 64, 64, 64, False) <= 4
 
 
 # ------------------------------------------------------------ MLA entries

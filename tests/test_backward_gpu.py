@@ -71,7 +71,7 @@ def _check(name, got, ref, what):
                            f"max err {err.max():.3e}, rms(ref) {rms:.3e}")
 
 
-def _run_bwd(ea, q, k, v, o, dO, lse, causal, scale, poison=True):
+def _run_bwd(ea, q, k, v, o, dO, lse, causal, scale, poison=True, n_splits=0):
     dev = _dev()
     t = [x.to(dev) for x in (q, k, v, o, dO)]
     lsed = lse.to(dev)
@@ -82,10 +82,12 @@ def _run_bwd(ea, q, k, v, o, dO, lse, causal, scale, poison=True):
         for x in (dq, dk, dv):
             x.fill_(float("nan"))
     B, H_q, N_q, D = q.shape
-    ws = torch.full((max(ea.attn_bwd_workspace_size(B, H_q, N_q), 1),), 0xFF, dtype=torch.uint8,
-                    device=dev)
+    H_kv, N_kv = k.shape[1], k.shape[2]
+    ns = n_splits if n_splits > 0 else max(ea.attn_bwd_num_splits(B, H_q, H_kv, N_q, N_kv, D, causal), 1)
+    nbytes = ea.attn_bwd_workspace_size(B, H_q, H_kv, N_q, N_kv, D, ns)
+    ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device=dev)
     ea.attn_bwd(t[0], t[1], t[2], t[3], t[4], lsed, dq, dk, dv, is_causal=causal, sm_scale=scale,
-                workspace=ws)
+                n_splits=n_splits, workspace=ws)
     torch.cuda.synchronize()
     return dq.cpu(), dk.cpu(), dv.cpu()
 
@@ -95,7 +97,8 @@ def _oracle_fwd_outputs(q64, k64, v64, causal, scale):
     return torch.from_numpy(O).to(torch.bfloat16), torch.from_numpy(L).to(torch.float32)
 
 
-def _case(ea, B, H_q, H_kv, N_q, N_kv, D, causal, seed, scale=None, chained=False, mutate=None):
+def _case(ea, B, H_q, H_kv, N_q, N_kv, D, causal, seed, scale=None, chained=False, mutate=None,
+          n_splits=0):
     q, k, v, dO = _inputs(B, H_q, H_kv, N_q, N_kv, D, seed)
     if mutate is not None:
         q, k, v, dO = mutate(q, k, v, dO)
@@ -108,10 +111,10 @@ def _case(ea, B, H_q, H_kv, N_q, N_kv, D, causal, seed, scale=None, chained=Fals
         o, lse = o.cpu(), lse.cpu()
     else:
         o, lse = _oracle_fwd_outputs(q64, k64, v64, causal, scale)
-    dq, dk, dv = _run_bwd(ea, q, k, v, o, dO, lse, causal, scale)
+    dq, dk, dv = _run_bwd(ea, q, k, v, o, dO, lse, causal, scale, n_splits=n_splits)
     rq, rk, rv = oracle.attention_backward(q64, k64, v64, d64, is_causal=causal, sm_scale=scale,
                                            out=workloads.to_float64(o))
-    what = f"B{B} Hq{H_q} Hkv{H_kv} Nq{N_q} Nkv{N_kv} D{D} c{int(causal)} s{scale:.3g}"
+    what = f"B{B} Hq{H_q} Hkv{H_kv} Nq{N_q} Nkv{N_kv} D{D} c{int(causal)} s{scale:.3g} ns{n_splits}"
     _check("dQ", dq, rq, what)
     _check("dK", dk, rk, what)
     _check("dV", dv, rv, what)
@@ -144,6 +147,25 @@ def test_backward_rectangular(ea, N_q, N_kv, causal):
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
 def test_backward_scale_values(ea, scale):
     _case(ea, 1, 4, 2, 150, 150, 128, True, seed=12300, scale=scale)
+
+
+@pytest.mark.parametrize("n_splits", [1, 2, 3, 7, 64])
+@pytest.mark.parametrize("shape", [
+    (1, 16, 1, 512, 512, 128, True), (1, 6, 2, 100, 100, 64, False), (2, 4, 1, 70, 300, 128, True),
+    (1, 3, 1, 1, 129, 128, True), (1, 8, 2, 200, 200, 128, False),
+], ids=lambda s: "x".join(map(str, s)))
+def test_backward_row_range_splits(ea, shape, n_splits):
+    """dK/dV with a key block's (head, row tile) sequence cut into n_splits
+    ranges (more ranges than tiles leaves some empty) and summed in order."""
+    B, H_q, H_kv, N_q, N_kv, D, causal = shape
+    _case(ea, B, H_q, H_kv, N_q, N_kv, D, causal, seed=12700 + N_q + n_splits, n_splits=n_splits)
+
+
+def test_backward_mqa_workload(ea):
+    """Causal MQA N=512 (16 query heads on one kv head) with the library's split."""
+    w = workloads.WORKLOADS["mqa_n512"]
+    assert ea.attn_bwd_num_splits(w.B, w.H_q, w.H_kv, w.N, w.N, w.D, w.causal) > 1
+    _case(ea, w.B, w.H_q, w.H_kv, w.N, w.N, w.D, w.causal, seed=w.seed)
 
 
 def test_backward_workload_gqa4_b2_n1024(ea):
@@ -223,9 +245,9 @@ def test_backward_deterministic_and_no_overrun(ea):
     for _ in range(2):
         bufs = [torch.full((x.numel() + 4096,), 7.0, dtype=torch.bfloat16, device=dev) for x in (q, k, v)]
         dq, dk, dv = (b[:x.numel()].view(x.shape) for b, x in zip(bufs, (q, k, v)))
-        need = ea.attn_bwd_workspace_size(1, 8, 333)
+        need = ea.attn_bwd_workspace_size(1, 8, 2, 333, 333, 128, 5)
         wb = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device=dev)
-        ea.attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, is_causal=True, workspace=wb[:need])
+        ea.attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, is_causal=True, n_splits=5, workspace=wb[:need])
         torch.cuda.synchronize()
         for b, x in zip(bufs, (q, k, v)):
             assert torch.all(b[x.numel():] == 7.0), "overrun"
