@@ -159,6 +159,22 @@ def make_step(ea, torch, w, qd, kd, vd, out, lse):
                                         sm_scale=w.sm_scale, n_splits=ns, workspace=ws)), ns
 
 
+def auto_counts(torch, step, steps, warmup):
+    """steps/warmup of None: enough launches for at least 100 ms of warm-up
+    (the shader clock settles under load) and 200 ms of timed work, at least
+    20 timed launches."""
+    if steps is not None and warmup is not None:
+        return steps, warmup
+    step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    dt = max(time.perf_counter() - t0, 1e-6)
+    return (steps if steps is not None else min(max(20, math.ceil(0.2 / dt)), 5000),
+            warmup if warmup is not None else min(max(3, math.ceil(0.1 / dt)), 5000))
+
+
 def time_workload(ea, torch, w, steps, warmup):
     dev = torch.device("cuda", 0)
     q, k, v = workloads.workload_inputs(w)
@@ -166,6 +182,7 @@ def time_workload(ea, torch, w, steps, warmup):
     out = torch.empty(w.q_shape(), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.H_q, w.Nq), dtype=torch.float32, device=dev)
     step, n_splits = make_step(ea, torch, w, qd, kd, vd, out, lse)
+    steps, warmup = auto_counts(torch, step, steps, warmup)
     for _ in range(warmup):
         step()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -201,6 +218,7 @@ def time_backward(ea, torch, w, steps, warmup):
     def step():
         ea.attn_bwd(qd, kd, vd, out, dod, lse, dq, dk, dv, is_causal=w.causal,
                     sm_scale=w.sm_scale, n_splits=ns, workspace=ws)
+    steps, warmup = auto_counts(torch, step, steps, warmup)
     for _ in range(warmup):
         step()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -338,11 +356,12 @@ def main():
         for name, ww in workloads.WORKLOADS.items():
             if ww.N_q is not None and name != "chunk_gqa4_q512_n8192":
                 continue
-            r = time_backward(ea, torch, ww, 10, 3)
+            r = time_backward(ea, torch, ww, None, None)
             e = float(np.median(r["event_ms"]))
             tf = 2.5 * ww.flops() / (e * 1e-3) / 1e12
             log(f"[bwd] {name:24s} median {e:9.4f} ms  min {min(r['event_ms']):9.4f} ms  "
-                f"{tf:8.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:5.1f}%)  splits {r['n_splits']}")
+                f"{tf:8.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:5.1f}%)  splits {r['n_splits']}  "
+                f"({len(r['event_ms'])} launches)")
         return
 
     w = workloads.WORKLOADS[args.workload]
@@ -358,13 +377,13 @@ def main():
 
     if args.sweep:
         for name, ww in workloads.WORKLOADS.items():
-            r, _ = time_workload(ea, torch, ww, 10, 3)
+            r, _ = time_workload(ea, torch, ww, None, None)
             e = r["event_ms"]
             tf = ww.flops() / (float(np.median(e)) * 1e-3) / 1e12
             gbs = ww.algorithmic_bytes() / (float(np.median(e)) * 1e-3) / 1e9
             log(f"[sweep] {name:24s} median {float(np.median(e)):9.4f} ms  min {min(e):9.4f} ms  "
                 f"{tf:8.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:5.1f}%)  {gbs:7.0f} GB/s "
-                f"({100 * gbs / PEAK_HBM_GBS:5.1f}%)  splits {r['n_splits']}")
+                f"({100 * gbs / PEAK_HBM_GBS:5.1f}%)  splits {r['n_splits']}  ({len(e)} launches)")
 
     cpu = parity = None
     if not args.no_cpu_baseline:

@@ -82,16 +82,18 @@ int64_t kv_block_tiles(const Shape& a, int64_t kb) {
   return (a.H_q / a.H_kv) * ((a.N_q - r_start + kKvBP - 1) / kKvBP);
 }
 
-// The library's split count: 1 while the key blocks already fill every CU
-// (one dK/dV workgroup per CU); otherwise the heaviest key block is cut into
-// ranges no longer than an even share of all tiles per CU (and at least 4
-// tiles), capped at kMaxBwdSplits and at 1 GiB of partial sums.
+// The library's split count: the heaviest key block (causal: block 0, which
+// sees every row) is cut into ranges no longer than an even share of all row
+// tiles per CU (one dK/dV workgroup runs per CU at a time), at least 4 tiles
+// each, capped at kMaxBwdSplits and at 1 GiB of partial sums.  This is 1 when
+// the key blocks are many and balanced (long sequences), and above 1 both for
+// few key blocks (one kv head, short sequences) and for a causal grid of about
+// one workgroup per CU, whose time the heaviest block would otherwise set.
 int64_t choose_kv_splits(const Shape& a) {
   if (a.N_q == 0 || a.N_kv == 0 || a.B == 0 || a.H_q == 0) return 1;
   const int64_t key_blocks = (a.N_kv + 32 * kKvNW - 1) / (32 * kKvNW);
   const int64_t heads = a.B * a.H_kv;
   const int64_t cus = device_cus();
-  if (heads * key_blocks >= cus) return 1;
   int64_t total = 0;
   for (int64_t kb = 0; kb < key_blocks; ++kb) total += kv_block_tiles(a, kb);
   total *= heads;

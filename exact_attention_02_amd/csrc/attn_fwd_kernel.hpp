@@ -400,10 +400,12 @@ void attn_fwd_kernel(FwdParams p) {
   };
 
   // One pipelined step over tile t (its scores already in sc, masked, max
-  // applied): P(t) = 2^(S(t) sl2 - m) interleaved with S(t+1) = K(t+1) Q^T
-  // into sn (when HAS_NEXT), then O += V(t) P(t) interleaved with the lane max
-  // of S(t+1).
-  auto step = [&](int t, Scores& sc, Scores& sn, auto has_next_tag) {
+  // applied), in two phases: P(t) = 2^(S(t) sl2 - m) interleaved with
+  // S(t+1) = K(t+1) Q^T into sn (when HAS_NEXT), then O += V(t) P(t).  P(t)
+  // passes between them in pbf, declared outside both (fewer registers live
+  // across the step than a local of one lambda).
+  bf16x8 pbf[QB][BN / 16];
+  auto phase_x = [&](int t, Scores& sc, Scores& sn, auto has_next_tag) {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     float m_sub[QB], l_t[QB];
 #pragma unroll
@@ -411,7 +413,6 @@ void attn_fwd_kernel(FwdParams p) {
       m_sub[qb] = (m_used[qb] == -INFINITY) ? 0.f : m_used[qb];
       l_t[qb] = 0.f;
     }
-    bf16x8 pb[QB][BN / 16];
     f32x8 pf[QB];
     // exponential number j of this tile: query block j / NV, element j % NV,
     // taken against the max in use (no max of this tile is computed here)
@@ -420,7 +421,7 @@ void attn_fwd_kernel(FwdParams p) {
       const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 4][qb][e & 15], sl2, -m_sub[qb]));
       pf[qb][e & 7] = pe;
       l_t[qb] += pe;
-      if ((e & 7) == 7) pb[qb][e >> 3] = __builtin_convertvector(pf[qb], bf16x8);
+      if ((e & 7) == 7) pbf[qb][e >> 3] = __builtin_convertvector(pf[qb], bf16x8);
     };
     if constexpr (HAS_NEXT) {
 #pragma unroll
@@ -472,6 +473,12 @@ void attn_fwd_kernel(FwdParams p) {
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_run[qb] += l_t[qb];
+    // a diagonal or ragged next tile is masked before its exponentials
+    if constexpr (HAS_NEXT) {
+      if (needs_mask(t + 1)) apply_mask(t + 1, sn);
+    }
+  };
+  auto phase_y = [&](int t) {
     // O^T += V^T P^T; k-step st covers keys 16 st .. 16 st + 15
     bf16x8 vx[PF + 1];
 #pragma unroll
@@ -482,12 +489,12 @@ void attn_fwd_kernel(FwdParams p) {
       const int st = i / (D / 32), db = i % (D / 32);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx[i % (PF + 1)], pb[qb][st], acc[db][qb], 0, 0, 0);
+        acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx[i % (PF + 1)], pbf[qb][st], acc[db][qb], 0, 0, 0);
     }
-    // a diagonal or ragged next tile is masked before its exponentials
-    if constexpr (HAS_NEXT) {
-      if (needs_mask(t + 1)) apply_mask(t + 1, sn);
-    }
+  };
+  auto step = [&](int t, Scores& sc, Scores& sn, auto has_next_tag) {
+    phase_x(t, sc, sn, has_next_tag);
+    phase_y(t);
   };
 
   // Load schedule.  Group j loads K(j) into K slot j % P and V(j-1) into V

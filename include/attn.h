@@ -208,10 +208,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
 
 /*
  * attn_bwd_num_splits -- the split count attn_bwd uses for n_splits = 0 on
- * the current device: 1 when the dK/dV key blocks already give every CU a
- * workgroup, otherwise enough ranges that the heaviest key block's share is
+ * the current device: enough ranges that the heaviest key block's share is
  * no longer than an even share of all row tiles per CU (at least 4 tiles per
- * range), at most 64 and at most 1 GiB of partial sums.  Returns -1 when the
+ * range), at most 64 and at most 1 GiB of partial sums; 1 when the key blocks
+ * are already many and balanced.  Returns -1 when the
  * sizes fail attn_bwd's size checks (NEGATIVE_SIZE .. SIZE_OVERFLOW), 1 for
  * empty work.  Queries the current device's CU count; enqueues nothing.
  */
