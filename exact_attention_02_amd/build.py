@@ -9,6 +9,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
@@ -21,10 +22,15 @@ DEPENDS = [os.path.join(CSRC, "attn_fwd_kernel.hpp"), os.path.join(CSRC, "attn_b
            os.path.join(os.path.dirname(PKG_DIR), "include", "attn.h")]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 VALU instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source flags.  The backward's score MFMAs (S, dP) return their results
+# in VGPRs, where the softmax reads them; its dK/dV accumulators are pinned to
+# AGPRs in the source.  Without this the compiler gives every MFMA of the file
+# AGPR results and copies S and dP back on every tile.
+SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -34,16 +40,32 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: install ROCm or set HIPCC")
 
 
-def build_library(verbose: bool = False, extra_flags=None) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), *SOURCES, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+def _check(r, cmd, verbose):
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build_library(verbose: bool = False, extra_flags=None) -> str:
+    """Compile each source to an object (in parallel), then link."""
+    tmp = LIB_PATH + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="ea02_build_") as d:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(d, os.path.basename(src) + ".o")
+            cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []),
+                   *(extra_flags or []), "-c", src, "-o", obj]
+            procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                                text=True)))
+            objs.append(obj)
+        for cmd, pr in procs:
+            out, err = pr.communicate()
+            _check(subprocess.CompletedProcess(cmd, pr.returncode, out, err), cmd, verbose)
+        cmd = [hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp]
+        _check(subprocess.run(cmd, capture_output=True, text=True), cmd, verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -109,6 +109,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void attn_bwd_
   }
 }
 
+// acc += a b with the accumulator pinned to AGPRs.  With one wave per SIMD the
+// dK/dV kernel holds 128 accumulator registers beside K, V and the score
+// tiles; in AGPRs they leave the VGPRs to the S and dP products (which the
+// build keeps in VGPRs, where the softmax reads them) and no copies between
+// the two files remain in the tile loop.  The compiler does not look inside
+// the asm for MFMA hazards: the two wait states cover a VALU write of an
+// operand just before, and the kernel waits before it reads the AGPRs.
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 // ---------------------------------------------------------------- dK, dV
 template <int D, int NW, int P, int BP>
 struct BwdKvCfg {
@@ -292,8 +303,8 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(dot + c * 32 * C::ROW_BYTES, st, db), pb[st], dvT[db], 0, 0, 0);
-          dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qt + c * 32 * C::ROW_BYTES, st, db), dsb[st], dkT[db], 0, 0, 0);
+          mfma_agpr(dvT[db], tr_read(dot + c * 32 * C::ROW_BYTES, st, db), pb[st]);
+          mfma_agpr(dkT[db], tr_read(qt + c * 32 * C::ROW_BYTES, st, db), dsb[st]);
         }
     }
   };
@@ -314,6 +325,13 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may outlive the workgroup
   }
 
+  // the last accumulation has landed before the AGPRs are read (the
+  // accumulators pass through the asm, so no read moves above it)
+  if constexpr (D == 128)
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(dkT[0]), "+a"(dkT[1]), "+a"(dkT[2]), "+a"(dkT[3]),
+                 "+a"(dvT[0]), "+a"(dvT[1]), "+a"(dvT[2]), "+a"(dvT[3]));
+  else
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(dkT[0]), "+a"(dkT[1]), "+a"(dvT[0]), "+a"(dvT[1]));
   // dK^T, dV^T: the lane holds key my_key, d = db*32 + 8(r/4) + 4 half + r%4.
   // A split writes its fp32 partial sums (a range with no tile writes zeros).
   if (p.n_kv_splits > 1) {
