@@ -29,7 +29,9 @@ HIPCC_FLAGS = [
 # Per-source flags.  The backward's score MFMAs (S, dP) return their results
 # in VGPRs, where the softmax reads them; its dK/dV accumulators are pinned to
 # AGPRs in the source.  Without this the compiler gives every MFMA of the file
-# AGPR results and copies S and dP back on every tile.
+# AGPR results and copies S and dP back on every tile.  (The same treatment of
+# the MLA core removes its copies too but measured slower: that kernel is
+# bound by latency, not issue.)
 SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
