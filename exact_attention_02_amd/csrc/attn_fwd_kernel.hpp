@@ -19,9 +19,9 @@
 //    lane scalar.  The S^T accumulator rounded to bf16 is directly the B
 //    operand of the PV product.
 //  * Query fragments stay in VGPRs for the whole kernel (B operand of S^T).
-//  * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
-//    staging registers), each 16-byte chunk of a row XOR-swizzled by the row
-//    index.  K fragments are 128-bit LDS reads; V^T fragments come from the
+//  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 with the
+//    lds modifier on a buffer resource per kv head, no staging registers),
+//    each 16-byte chunk of a row XOR-swizzled by the row index.  K fragments are 128-bit LDS reads; V^T fragments come from the
 //    LDS transpose read ds_read_b64_tr_b16 on the untransposed V tile, two per
 //    MFMA, in the key order the S^T accumulator layout implies.
 //  * A ring of P LDS stages for K and for V: after the barrier that opens tile
@@ -102,10 +102,6 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays <= 2^8
 constexpr float kOverflowSum = 16777216.0f;  // 2^24: largest tile sum of P taken without a rescale
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 for gfx9 (untyped dword access)
 
-// instruction classes for __builtin_amdgcn_sched_group_barrier
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 // v_permlane32_swap exchanges lanes 32..63 of the first operand with lanes
@@ -138,12 +134,6 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ void dma_16B(u32x4 rsrc, int voff, uint32_t lds_addr) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
                : "memory");
-}
-
-// x *= a in place (tied operand), so the rescale of the accumulator keeps the
-// accumulator's registers and needs no copies around the branch.
-__device__ __forceinline__ void mul_inplace(float& x, float a) {
-  asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(a));
 }
 
 template <int D, int NW_, int P_, int QB_, int BN_>
