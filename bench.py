@@ -333,10 +333,11 @@ def main():
                 ea.mla_up_project(out_lat, wv, out_m)
             res_t = {}
             for label, fn in (("core", core), ("full", full)):
-                for _ in range(3):
+                steps, warmup = auto_counts(torch, fn, None, None)
+                for _ in range(warmup):
                     fn()
                 ev = []
-                for _ in range(20):
+                for _ in range(steps):
                     s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     s_.record()
                     fn()
