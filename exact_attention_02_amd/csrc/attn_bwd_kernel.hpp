@@ -10,7 +10,8 @@
 //   dQ = scale dS K,   dK = scale dS^T Q          (dK, dV summed over the
 //                                                  query heads of a kv head)
 //
-// Three kernels, no atomics (the result is deterministic):
+// Three kernels, and a fourth that sums row-range splits; no atomics (the
+// result is deterministic for a given split count):
 //  * attn_bwd_prep_kernel: Dl = rowsum(dO * O) and L2 = L log2(e) per row.
 //  * attn_bwd_dkdv_kernel: a workgroup owns 32 keys per wave of one kv head;
 //    K and V of those keys stay in registers while the query rows of every
