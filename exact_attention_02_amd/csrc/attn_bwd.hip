@@ -103,6 +103,7 @@ int64_t choose_kv_splits(const Shape& a) {
   n = std::min({n, tiles_max, kMaxBwdSplits});
   const int64_t plane2 = 2 * heads * a.N_kv * a.D * 4;
   n = std::min(n, kAutoPartBytes / plane2);
+  n = std::min(n, int64_t(INT32_MAX) / (heads * key_blocks));  // the grid stays below 2^31
   return std::max<int64_t>(n, 1);
 }
 
