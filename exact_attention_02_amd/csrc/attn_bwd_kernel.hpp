@@ -284,15 +284,20 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
       }
       f32x8 pf, sf;
       bf16x8 pb[2], dsb[2];
-      const int lo_vis = my_key - off - row0 - c * 32 - 4 * half;  // visible: index >= lo_vis
-      const int hi_vis = N_q - row0 - c * 32 - 4 * half;           // and index < hi_vis
+      // masked tiles only (a wave-uniform branch): invisible scores become
+      // -inf, so their P and dS are 0 with no per-element test below
+      if (masked) {
+        const int lo_vis = my_key - off - row0 - c * 32 - 4 * half;  // visible: index >= lo_vis
+        const int hi_vis = N_q - row0 - c * 32 - 4 * half;           // and index < hi_vis
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int idx = 8 * (r >> 2) + (r & 3);
+          if ((p.causal && idx < lo_vis) || idx >= hi_vis) s[r] = -INFINITY;
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[r >> 2][r & 3]));
-        if (masked) {
-          const int idx = 8 * (r >> 2) + (r & 3);
-          if ((p.causal && idx < lo_vis) || idx >= hi_vis) pe = 0.f;
-        }
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[r >> 2][r & 3]));
         pf[r & 7] = pe;
         sf[r & 7] = pe * (dp[r] - d4[r >> 2][r & 3]);
         if ((r & 7) == 7) {
@@ -511,11 +516,17 @@ void attn_bwd_dq_kernel(BwdParams p) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
       }
+      // masked tiles only (a wave-uniform branch): invisible scores become
+      // -inf, so their dS is 0 with no per-element test below
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (c * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
+      }
       f32x8 sf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2));
-        if (masked && c * 32 + 8 * (r >> 2) + (r & 3) >= lim) pe = 0.f;
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2));
         sf[r & 7] = pe * (dp[r] - dl);
         if ((r & 7) == 7) dsb[2 * c + (r >> 3)] = __builtin_convertvector(sf, bf16x8);
       }
