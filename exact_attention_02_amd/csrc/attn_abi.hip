@@ -152,7 +152,9 @@ int device_cus() {
 
 // Number of key splits the library picks: none while the unsplit grid already
 // fills every workgroup slot of the device; otherwise enough splits for about
-// two workgroups per CU, each split keeping at least 8 key tiles.
+// two workgroups per CU, or one for the eight-wave shape (one fits a CU: a
+// second round of workgroups measured slower than fewer, longer splits), each
+// split keeping at least 8 key tiles.
 int64_t choose_splits(const Problem& a) {
   const int64_t n_pairs = a.N_q * (a.H_q / a.H_kv);
   const Shape sh = pick_shape(n_pairs, a.D);
@@ -160,7 +162,8 @@ int64_t choose_splits(const Problem& a) {
   const int64_t cus = device_cus();
   if (wgs <= 0 || wgs >= cus * sh.wg_per_cu) return 1;
   const int64_t tiles = (a.N_kv + sh.bn - 1) / sh.bn;
-  int64_t n = (2 * cus + wgs - 1) / wgs;
+  const int64_t target = std::min<int64_t>(2, sh.wg_per_cu) * cus;
+  int64_t n = (target + wgs - 1) / wgs;
   n = std::min<int64_t>(n, tiles / 8);
   n = std::min<int64_t>(n, kMaxSplits);
   return n < 1 ? 1 : n;

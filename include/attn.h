@@ -140,7 +140,9 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, flo
  * attn_splitkv_num_splits -- the split count attn_fwd_splitkv uses for
  * n_splits = 0 on the current device: 1 when the unsplit launch already fills
  * every workgroup slot, otherwise enough splits for about two workgroups per
- * CU, with at least eight key tiles per split and at most 256.  Returns -1 when the
+ * CU (one per CU for the eight-wave shape of more than 64 (row, head) pairs
+ * per kv head, which fits one workgroup per CU), with at least eight key
+ * tiles per split and at most 256.  Returns -1 when the
  * sizes fail attn_fwd_splitkv's size checks (NEGATIVE_SIZE .. SIZE_OVERFLOW).
  * Queries the current device's CU count; enqueues nothing.
  */

@@ -170,6 +170,9 @@ def test_num_splits_choice():
     assert 65536 // 32 // n >= 8
     # too few keys to split
     assert ea.attn_splitkv_num_splits(1, 32, 32, 1, 100, 128, False) == 1
+    # eight-wave shape (512 rows x 4 heads per kv head): one workgroup per CU, so
+    # 64 workgroups take 4 splits on 256 CUs (this CPU run sees no device: 256 assumed)
+    assert ea.attn_splitkv_num_splits(1, 32, 8, 512, 8192, 128, True) == 4
     assert ea.attn_splitkv_num_splits(1, 32, 32, 0, 100, 128, False) == 1
     assert ea.attn_splitkv_num_splits(1, 32, 32, 1, 100, 96, False) == -1
     assert ea.attn_splitkv_num_splits(1, 4, 4, 20, 10, 64, True) == -1
