@@ -212,7 +212,7 @@ def time_backward(ea, torch, w, steps, warmup):
     out, lse = ea.fwd_splitkv(qd, kd, vd, is_causal=w.causal, sm_scale=w.sm_scale, n_splits=1)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     ns = max(ea.attn_bwd_num_splits(w.B, w.H_q, w.H_kv, w.Nq, w.N, w.D, w.causal), 1)
-    ws = torch.empty((max(ea.attn_bwd_workspace_size(w.B, w.H_q, w.H_kv, w.Nq, w.N, w.D, ns), 1),),
+    ws = torch.empty((max(ea.attn_bwd_workspace_size(w.B, w.H_q, w.H_kv, w.Nq, w.N, w.D, w.causal, ns), 1),),
                      dtype=torch.uint8, device=dev)
 
     def step():

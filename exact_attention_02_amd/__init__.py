@@ -71,7 +71,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd_num_splits.restype = ctypes.c_int64
     lib.attn_bwd_num_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
-    lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int64] * 7
+    lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int64]
     lib.attn_mla_decode.restype = ctypes.c_int
     lib.attn_mla_decode.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t,
@@ -236,10 +236,12 @@ def attn_bwd_num_splits(B: int, H_q: int, H_kv: int, N_q: int, N_kv: int, D: int
 
 
 def attn_bwd_workspace_size(B: int, H_q: int, H_kv: int, N_q: int, N_kv: int, D: int,
-                            n_splits: int = 1) -> int:
-    """Workspace bytes attn_bwd needs with n_splits row ranges (per query row:
-    log2-unit LSE and rowsum(dO*O); per range: fp32 partial dK and dV)."""
-    return int(load_library().attn_bwd_workspace_size(B, H_q, H_kv, N_q, N_kv, D, n_splits))
+                            is_causal: bool = False, n_splits: int = 1) -> int:
+    """Workspace bytes attn_bwd needs with n_splits dK/dV row ranges on the
+    current device (per query row: log2-unit LSE and rowsum(dO*O); per range:
+    fp32 partial dK and dV; fp32 partial dQ of the library's dQ splits)."""
+    return int(load_library().attn_bwd_workspace_size(B, H_q, H_kv, N_q, N_kv, D,
+                                                      int(bool(is_causal)), n_splits))
 
 
 def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, is_causal: bool = False,
@@ -295,9 +297,8 @@ def bwd(q, k, v, out, dout, lse, is_causal: bool = False, sm_scale: float | None
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     with torch.cuda.device(q.device):
-        ns = attn_bwd_num_splits(B, H_q, H_kv, N_q, N_kv, D, is_causal)
-    ns = max(ns, 1)
-    nbytes = attn_bwd_workspace_size(B, H_q, H_kv, N_q, N_kv, D, ns)
+        ns = max(attn_bwd_num_splits(B, H_q, H_kv, N_q, N_kv, D, is_causal), 1)
+        nbytes = attn_bwd_workspace_size(B, H_q, H_kv, N_q, N_kv, D, is_causal, ns)
     ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
     attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, is_causal=is_causal, sm_scale=sm_scale,
              n_splits=ns, workspace=ws, stream=stream)

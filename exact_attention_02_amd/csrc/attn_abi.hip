@@ -295,4 +295,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" int attn_abi_version(void) { return 5; }
+extern "C" int attn_abi_version(void) { return 6; }

@@ -27,6 +27,24 @@ constexpr int kQNW = 8, kQP = 4, kQBN = 64;
 constexpr int64_t kMaxBwdSplits = 64;
 // Partial sums of the library's own choice take at most this much workspace.
 constexpr int64_t kAutoPartBytes = int64_t(1) << 30;
+// Cost model for the library's split choice (MI355X measurements of these
+// kernels): about 2 us per row tile of the dK/dV kernel or key tile of the dQ
+// kernel; partial sums written, read back and reduced at about 5 bytes/ps (5
+// TB/s); about 5 us for the extra launch.
+constexpr double kTileUs = 2.0;
+constexpr double kPartBytesPerUs = 5.0e6;
+constexpr double kLaunchUs = 5.0;
+
+// Keep n splits only if the time taken off the heaviest workgroup (it walks
+// tiles_max tiles unsplit, max(share, tiles_max / n) split) exceeds the cost
+// of its fp32 partials (part_bytes per split, plus out_bytes of final output).
+int64_t worth_splitting(int64_t n, int64_t tiles_max, int64_t share, double part_bytes, double out_bytes) {
+  if (n <= 1) return 1;
+  const int64_t split_max = std::max<int64_t>(share, (tiles_max + n - 1) / n);
+  const double saved = double(std::max<int64_t>(tiles_max - split_max, 0)) * kTileUs;
+  const double cost = (2.0 * n * part_bytes + out_bytes) / kPartBytesPerUs + kLaunchUs;
+  return saved > cost ? n : 1;
+}
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || !na || !nb) return false;
@@ -85,10 +103,12 @@ int64_t kv_block_tiles(const Shape& a, int64_t kb) {
 // The library's split count: the heaviest key block (causal: block 0, which
 // sees every row) is cut into ranges no longer than an even share of all row
 // tiles per CU (one dK/dV workgroup runs per CU at a time), at least 4 tiles
-// each, capped at kMaxBwdSplits and at 1 GiB of partial sums.  This is 1 when
-// the key blocks are many and balanced (long sequences), and above 1 both for
-// few key blocks (one kv head, short sequences) and for a causal grid of about
-// one workgroup per CU, whose time the heaviest block would otherwise set.
+// each, capped at kMaxBwdSplits and at 1 GiB of partial sums, and kept only
+// when the cost model above says the split pays for its partial sums.  This
+// is 1 when the key blocks are many and balanced (long sequences), and above 1
+// both for few key blocks (one kv head, short sequences) and for a causal
+// grid of about one workgroup per CU, whose time the heaviest block would
+// otherwise set.
 int64_t choose_kv_splits(const Shape& a) {
   if (a.N_q == 0 || a.N_kv == 0 || a.B == 0 || a.H_q == 0) return 1;
   const int64_t key_blocks = (a.N_kv + 32 * kKvNW - 1) / (32 * kKvNW);
@@ -104,17 +124,61 @@ int64_t choose_kv_splits(const Shape& a) {
   const int64_t plane2 = 2 * heads * a.N_kv * a.D * 4;
   n = std::min(n, kAutoPartBytes / plane2);
   n = std::min(n, int64_t(INT32_MAX) / (heads * key_blocks));  // the grid stays below 2^31
-  return std::max<int64_t>(n, 1);
+  return worth_splitting(n, tiles_max, share, double(plane2), double(plane2) / 2);
 }
 
-size_t row_stat_bytes(int64_t B, int64_t H_q, int64_t N_q) { return size_t(B) * size_t(H_q) * size_t(N_q) * 8; }
+// Key tiles (kQBN keys) that dQ pair block pb visits.
+int64_t q_block_tiles(const Shape& a, int64_t pb) {
+  const int64_t G = a.H_q / a.H_kv;
+  const int64_t last = std::min(pb * 32 * kQNW + 32 * kQNW - 1, a.N_q * G - 1);
+  const int64_t row_end = last / G + 1;
+  const int64_t kv_end = a.causal ? std::min(row_end + a.N_kv - a.N_q, a.N_kv) : a.N_kv;
+  return (kv_end + kQBN - 1) / kQBN;
+}
 
-size_t part_offset(int64_t B, int64_t H_q, int64_t N_q) { return (row_stat_bytes(B, H_q, N_q) + 255) & ~size_t(255); }
+// The dQ kernel's key-range splits, by the same rule as the dK/dV splits: the
+// heaviest pair block (causal: the last rows) is cut into ranges no longer
+// than an even share of all key tiles per CU (one dQ workgroup per CU at a
+// time), at least 4 tiles each, at most kMaxBwdSplits, at most 1 GiB of
+// partial sums, and only when the cost model says it pays.  1 when the pair
+// blocks are many and balanced.
+int64_t choose_q_splits(const Shape& a) {
+  if (a.N_q == 0 || a.N_kv == 0 || a.B == 0 || a.H_q == 0) return 1;
+  const int64_t pair_blocks = (a.N_q * (a.H_q / a.H_kv) + 32 * kQNW - 1) / (32 * kQNW);
+  const int64_t heads = a.B * a.H_kv;
+  const int64_t cus = device_cus();
+  int64_t total = 0;
+  for (int64_t pb = 0; pb < pair_blocks; ++pb) total += q_block_tiles(a, pb);
+  total *= heads;
+  const int64_t tiles_max = q_block_tiles(a, pair_blocks - 1);
+  const int64_t share = std::max<int64_t>((total + cus - 1) / cus, 4);
+  int64_t n = (tiles_max + share - 1) / share;
+  n = std::min({n, tiles_max, kMaxBwdSplits});
+  const int64_t plane = a.B * a.H_q * a.N_q * a.D * 4;
+  n = std::min(n, kAutoPartBytes / plane);
+  n = std::min(n, int64_t(INT32_MAX) / (heads * pair_blocks));
+  return worth_splitting(n, tiles_max, share, double(plane), double(plane) / 2);
+}
 
-size_t workspace_bytes(const Shape& a, int64_t n_splits) {
-  const size_t stats = row_stat_bytes(a.B, a.H_q, a.N_q);
-  if (n_splits <= 1) return stats;
-  return part_offset(a.B, a.H_q, a.N_q) + size_t(n_splits) * 2 * size_t(a.B * a.H_kv * a.N_kv * a.D) * 4;
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace: per-row L2 and Dl, then (256-byte aligned) the dK/dV partials
+// when split, then the dQ partials when split.  Offsets of the partials are
+// returned through kv_off and q_off.
+size_t workspace_layout(const Shape& a, int64_t n_kv, int64_t n_q, size_t* kv_off = nullptr,
+                        size_t* q_off = nullptr) {
+  size_t cur = size_t(a.B) * size_t(a.H_q) * size_t(a.N_q) * 8;
+  if (n_kv > 1) {
+    cur = align256(cur);
+    if (kv_off) *kv_off = cur;
+    cur += size_t(n_kv) * 2 * size_t(a.B * a.H_kv * a.N_kv * a.D) * 4;
+  }
+  if (n_q > 1) {
+    cur = align256(cur);
+    if (q_off) *q_off = cur;
+    cur += size_t(n_q) * size_t(a.B * a.H_q * a.N_q * a.D) * 4;
+  }
+  return cur;
 }
 
 // Prep, dK/dV (+ the sum of its splits), dQ.  With no query rows only the
@@ -139,8 +203,15 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s) {
   }
   if (p.rows > 0) {
     hipLaunchKernelGGL((ea02::attn_bwd_dq_kernel<D, kQNW, kQP, kQBN>),
-                       dim3(static_cast<unsigned>(p.n_heads_wg * p.n_pair_blocks)), dim3(kQNW * 64), 0, s, p);
-    e = hipGetLastError();
+                       dim3(static_cast<unsigned>(p.n_heads_wg * p.n_pair_blocks * p.n_q_splits)),
+                       dim3(kQNW * 64), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.n_q_splits > 1) {
+      const int64_t quads = p.rows * D / 4;
+      hipLaunchKernelGGL((ea02::attn_bwd_q_reduce_kernel<D>), dim3(static_cast<unsigned>((quads + 255) / 256)),
+                         dim3(256), 0, s, p);
+      e = hipGetLastError();
+    }
   }
   return e;
 }
@@ -157,14 +228,11 @@ extern "C" int64_t attn_bwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int
 }
 
 extern "C" size_t attn_bwd_workspace_size(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv,
-                                          int64_t D, int64_t n_splits) {
-  if (B < 0 || H_q < 0 || H_kv < 0 || N_q < 0 || N_kv < 0 || D < 0 || n_splits < 0 || n_splits > kMaxBwdSplits)
-    return 0;
-  if (B > (int64_t(1) << 24) || H_q > (int64_t(1) << 16) || N_q > (int64_t(1) << 24) ||
-      N_kv > (int64_t(1) << 24) || D > 128)
-    return 0;
-  const Shape a{B, H_q, H_kv, N_q, N_kv, D, 0};
-  return workspace_bytes(a, n_splits);
+                                          int64_t D, int is_causal, int64_t n_splits) {
+  const Shape a{B, H_q, H_kv, N_q, N_kv, D, is_causal};
+  bool empty = false;
+  if (check_sizes(a, n_splits, 1.f, &empty) != ATTN_OK || empty || N_q == 0 || N_kv == 0) return 0;
+  return workspace_layout(a, n_splits, choose_q_splits(a));
 }
 
 extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -185,7 +253,9 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     return ATTN_ERR_ALIGNMENT;
   // no query rows: nothing to split (the key blocks write zeros)
   const int64_t splits = N_q == 0 ? 1 : (n_splits == 0 ? choose_kv_splits(a) : n_splits);
-  const size_t need = workspace_bytes(a, splits);
+  const int64_t q_splits = choose_q_splits(a);
+  size_t kv_off = 0, q_off = 0;
+  const size_t need = N_q == 0 ? 0 : workspace_layout(a, splits, q_splits, &kv_off, &q_off);
   if (need > 0 && (!workspace || workspace_size < need || (reinterpret_cast<uintptr_t>(workspace) & 15u)))
     return ATTN_ERR_WORKSPACE;
   const int64_t G = H_q / H_kv;
@@ -214,8 +284,8 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   p.dv = static_cast<uint16_t*>(dv);
   p.lse2 = static_cast<float*>(workspace);
   p.delta = static_cast<float*>(workspace) + size_t(B * H_q * N_q);
-  p.kv_part = splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + part_offset(B, H_q, N_q))
-                         : nullptr;
+  p.kv_part = splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kv_off) : nullptr;
+  p.q_part = q_splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + q_off) : nullptr;
   p.B = static_cast<int>(B);
   p.H_q = static_cast<int>(H_q);
   p.H_kv = static_cast<int>(H_kv);
@@ -229,6 +299,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   p.n_key_blocks = static_cast<int>((N_kv + 32 * kKvNW - 1) / (32 * kKvNW));
   p.n_kv_splits = static_cast<int>(splits);
   p.n_pair_blocks = static_cast<int>((N_q * G + 32 * kQNW - 1) / (32 * kQNW));
+  p.n_q_splits = static_cast<int>(q_splits);
   // as in the forward: a zero scale becomes FLT_MIN in the exponent (uniform
   // weights, no 0 * inf); the gradient factors use the scale as given
   p.scale_log2 = std::fmax(std::fabs(sm_scale) * ea02::kLog2e, FLT_MIN);

@@ -53,6 +53,8 @@ struct BwdParams {
   float* delta;          // [B, H_q, N_q] workspace: rowsum(dO * O)
   float* kv_part;        // [n_kv_splits, 2, B, H_kv, N_kv, D] fp32 workspace (dK scaled, dV)
                          // of the row-range splits; unused when n_kv_splits == 1
+  float* q_part;         // [n_q_splits, B, H_q, N_q, D] fp32 workspace (dQ scaled) of the
+                         // key-range splits; unused when n_q_splits == 1
   int B, H_q, H_kv, N_q, N_kv;
   int G;                 // H_q / H_kv
   int n_pairs;           // N_q * G
@@ -62,6 +64,7 @@ struct BwdParams {
   int n_key_blocks;      // dK/dV kernel: ceil(N_kv / keys per workgroup)
   int n_kv_splits;       // dK/dV kernel: workgroups sharing one key block's row tiles
   int n_pair_blocks;     // dQ kernel: ceil(n_pairs / pairs per workgroup)
+  int n_q_splits;        // dQ kernel: workgroups sharing one pair block's key tiles
   float scale_log2;      // max(|sm_scale| log2(e), FLT_MIN)
   float grad_scale;      // sm_scale (signed): factor of dQ and dK
   uint32_t k_sign;       // 0x80008000 when sm_scale < 0: K negated in S (dK/dV kernel)
@@ -392,6 +395,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void attn_bwd_
   *reinterpret_cast<u32x2*>(p.dv + i) = __builtin_bit_cast(u32x2, __builtin_convertvector(sv, bf16x4));
 }
 
+// dQ = sum over the key-range splits of the partials, in split order; 4
+// elements per thread, rounded to bf16 when stored.
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void attn_bwd_q_reduce_kernel(BwdParams p) {
+  const size_t plane = (size_t)p.rows * D;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= plane) return;
+  f32x4 s = *reinterpret_cast<const f32x4*>(p.q_part + i);
+  for (int sp = 1; sp < p.n_q_splits; ++sp) s += *reinterpret_cast<const f32x4*>(p.q_part + (size_t)sp * plane + i);
+  *reinterpret_cast<u32x2*>(p.dq + i) = __builtin_bit_cast(u32x2, __builtin_convertvector(s, bf16x4));
+}
+
 // ---------------------------------------------------------------- dQ
 template <int D, int NW, int P, int BN>
 struct BwdQCfg {
@@ -427,9 +442,13 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
+  // heaviest pair blocks first (causal: the last rows see every key), kv
+  // heads fastest, then the key-range splits of one pair block
   const int bid = blockIdx.x;
   const int head_wg = bid % p.n_heads_wg;
-  const int pb = p.n_pair_blocks - 1 - bid / p.n_heads_wg;  // heaviest first
+  const int rest = bid / p.n_heads_wg;
+  const int qsplit = rest % p.n_q_splits;
+  const int pb = p.n_pair_blocks - 1 - rest / p.n_q_splits;
   const int g = head_wg % p.H_kv;
   const int b = head_wg / p.H_kv;
   const int G = p.G;
@@ -442,6 +461,10 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const int wg_row_end = min(P0 + PPW - 1, last_pair) / G + 1;
   const int kv_end = p.causal ? min(wg_row_end + off, N_kv) : N_kv;
   const int n_tiles = (kv_end + BN - 1) / BN;
+  // this workgroup's contiguous range of those key tiles
+  const int t_lo = (int)(((int64_t)n_tiles * qsplit) / p.n_q_splits);
+  const int t_hi = (int)(((int64_t)n_tiles * (qsplit + 1)) / p.n_q_splits);
+  const int n_mine = t_hi - t_lo;
 
   // this lane's pair: Q and dO fragments (B operands), L2 and Dl
   const int pair = wp0 + col;
@@ -544,19 +567,32 @@ void attn_bwd_dq_kernel(BwdParams p) {
       }
   };
 
-  if (n_tiles > 0) {
+  // load ring over the range: its i-th tile goes to slot i % P
+  if (n_mine > 0) {
 #pragma unroll
-    for (int j = 0; j < P - 1; ++j) issue(min(j, n_tiles - 1), j);
-    for (int t = 0; t < n_tiles; ++t) {
+    for (int j = 0; j < P - 1; ++j) issue(t_lo + min(j, n_mine - 1), j);
+    for (int i = 0; i < n_mine; ++i) {
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 2) * C::GROUP_LOADS) : "memory");
       __syncthreads();
-      issue(min(t + P - 1, n_tiles - 1), (t + P - 1) % P);
-      compute(t, t % P);
+      issue(t_lo + min(i + P - 1, n_mine - 1), (i + P - 1) % P);
+      compute(t_lo + i, i % P);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
-  if (valid) {
+  // a split writes its fp32 partial (a range with no tile writes zeros)
+  if (valid && p.n_q_splits > 1) {
+    float* dqr = p.q_part + ((size_t)qsplit * (size_t)p.rows + bhr) * D;
+    const float gs = p.grad_scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * half;
+        *reinterpret_cast<f32x4*>(dqr + d0) =
+            f32x4{dqT[db][4 * g4] * gs, dqT[db][4 * g4 + 1] * gs, dqT[db][4 * g4 + 2] * gs, dqT[db][4 * g4 + 3] * gs};
+      }
+  } else if (valid) {
     uint16_t* dqr = p.dq + bhr * D;
     const float gs = p.grad_scale;
 #pragma unroll

@@ -184,14 +184,20 @@ size_t attn_splitkv_workspace_size(int64_t B, int64_t H_q, int64_t N_q, int64_t 
  *                 each, whose fp32 partial dk and dv are summed in range order
  *                 by one more kernel (a range may be empty)
  *   workspace     device scratch of at least attn_bwd_workspace_size(B, H_q,
- *                 H_kv, N_q, N_kv, D, n_splits') bytes, 16-byte aligned, where
- *                 n_splits' is the split count used (1 when N_q = 0): per row
- *                 L log2 e and Dl, then the partial sums; contents undefined
- *                 on entry and after; calls that overlap on one workspace race
+ *                 H_kv, N_q, N_kv, D, is_causal, n_splits') bytes, 16-byte
+ *                 aligned, where n_splits' is the split count used (unused
+ *                 when N_q = 0): per row L log2 e and Dl, then the partial
+ *                 sums of the dK/dV splits, then those of the dQ kernel's
+ *                 key-range splits, which the library chooses itself (by the
+ *                 rule of attn_bwd_num_splits applied to the dQ kernel's pair
+ *                 blocks: more than one only when they are few or unbalanced);
+ *                 contents undefined on entry and after; calls that overlap
+ *                 on one workspace race
  * All buffers are contiguous device memory of the current device.  Three
- * kernels are enqueued on `stream` (four with splits); the call never
- * synchronises.  The result is deterministic (no atomics) for a given split
- * count; different split counts round differently.
+ * kernels are enqueued on `stream`, and one more for each of the two split
+ * kinds in use; the call never synchronises.  The result is deterministic
+ * (no atomics) for given split counts; different split counts round
+ * differently.
  *
  * Errors, checked in this order; nothing is enqueued on failure:
  *   NEGATIVE_SIZE (any size or n_splits < 0), HEAD_RATIO, HEAD_DIM,
@@ -212,23 +218,28 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
  * attn_bwd_num_splits -- the split count attn_bwd uses for n_splits = 0 on
  * the current device: enough ranges that the heaviest key block's share is
  * no longer than an even share of all row tiles per CU (at least 4 tiles per
- * range), at most 64 and at most 1 GiB of partial sums; 1 when the key blocks
- * are already many and balanced.  Returns -1 when the
- * sizes fail attn_bwd's size checks (NEGATIVE_SIZE .. SIZE_OVERFLOW), 1 for
- * empty work.  Queries the current device's CU count; enqueues nothing.
+ * range), at most 64 and at most 1 GiB of partial sums, kept only when a cost
+ * model (about 2 us per tile saved against the partial sums' traffic at about
+ * 5 TB/s and one more launch) says the split pays; 1 when the key blocks are
+ * already many and balanced.  Returns -1 when the sizes fail attn_bwd's size
+ * checks (NEGATIVE_SIZE .. SIZE_OVERFLOW), 1 for empty work.  Queries the
+ * current device's CU count; enqueues nothing.
  */
 int64_t attn_bwd_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t D,
                             int is_causal);
 
 /*
  * attn_bwd_workspace_size -- bytes of workspace attn_bwd needs with n_splits
- * ranges: B * H_q * N_q * 8 when n_splits <= 1; otherwise that rounded up to
- * a multiple of 256, plus n_splits * 2 * B * H_kv * N_kv * D * 4 (fp32 partial
- * dk, then dv, per range).  0 for negative or too large sizes and for
- * n_splits > 64.
+ * dK/dV ranges on the current device: B * H_q * N_q * 8 (per-row statistics),
+ * then, each region starting at a multiple of 256 bytes, n_splits * 2 * B *
+ * H_kv * N_kv * D * 4 when n_splits > 1 (fp32 partial dk, then dv, per range)
+ * and q_splits * B * H_q * N_q * D * 4 when the library's dQ split count
+ * q_splits is above 1 (fp32 partial dq per range).  0 when the sizes fail
+ * attn_bwd's size checks (NEGATIVE_SIZE .. SIZE_OVERFLOW, n_splits included)
+ * and when N_q or N_kv is 0.  Queries the current device's CU count.
  */
 size_t attn_bwd_workspace_size(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t D,
-                               int64_t n_splits);
+                               int is_causal, int64_t n_splits);
 
 /*
  * Multi-head latent attention (MLA) decode, absorbed form.  Page "Attention
@@ -301,8 +312,9 @@ int mla_up_project(const void* out_lat, const void* w_uv, void* out, int64_t B, 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);
 
-/* Library ABI version, currently 5 (1: attn_fwd; 2: + split-KV; 3: + backward;
- * 4: + MLA decode; 5: backward row-range splits, attn_bwd_num_splits). */
+/* Library ABI version, currently 6 (1: attn_fwd; 2: + split-KV; 3: + backward;
+ * 4: + MLA decode; 5: backward row-range splits, attn_bwd_num_splits; 6:
+ * backward dQ key-range splits, is_causal in attn_bwd_workspace_size). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 5
+    assert lib.attn_abi_version() == 6
 
 
 def test_status_strings_distinct(lib):
@@ -267,14 +267,21 @@ def test_bwd_no_query_rows_needs_only_key_buffers(lib):
 
 
 def test_bwd_workspace_size():
+    # large balanced grids: only the per-row statistics
     assert ea.attn_bwd_workspace_size(2, 32, 8, 1024, 1024, 128) == 2 * 32 * 1024 * 8
-    assert ea.attn_bwd_workspace_size(2, 32, 8, 1024, 1024, 128, 1) == 2 * 32 * 1024 * 8
+    assert ea.attn_bwd_workspace_size(2, 32, 8, 1024, 1024, 128, False, 1) == 2 * 32 * 1024 * 8
     assert ea.attn_bwd_workspace_size(1, 4, 4, 0, 10, 64) == 0
     assert ea.attn_bwd_workspace_size(-1, 4, 4, 4, 4, 64) == 0
-    assert ea.attn_bwd_workspace_size(1, 4, 1, 4, 4, 64, 65) == 0
-    # row statistics rounded up to 256 bytes, then fp32 dK and dV partials per range
-    assert ea.attn_bwd_workspace_size(1, 3, 1, 5, 70, 64, 3) == 256 + 3 * 2 * 70 * 64 * 4
-    assert ea.attn_bwd_workspace_size(1, 16, 1, 512, 512, 128, 32) == 65536 + 32 * 2 * 512 * 128 * 4
+    assert ea.attn_bwd_workspace_size(1, 4, 1, 4, 4, 64, False, 65) == 0
+    assert ea.attn_bwd_workspace_size(1, 4, 4, 10, 5, 64, True) == 0    # causal with N_q > N_kv
+    # statistics rounded up to 256 bytes, then fp32 dK and dV partials per range
+    assert ea.attn_bwd_workspace_size(1, 3, 1, 5, 70, 64, False, 3) == 256 + 3 * 2 * 70 * 64 * 4
+    # (the cases below assume 256 CUs: this CPU run sees no device)
+    # one dQ workgroup over 128 key tiles: 32 dQ splits of fp32 partial dQ
+    assert ea.attn_bwd_workspace_size(1, 4, 1, 64, 8192, 128, False, 1) == 2048 + 32 * 4 * 64 * 128 * 4
+    # MQA N=512: 32 dK/dV ranges; two dQ ranges would save 4 tiles of the
+    # heaviest workgroup, less than their partial sums and launch cost
+    assert ea.attn_bwd_workspace_size(1, 16, 1, 512, 512, 128, False, 32) == 65536 + 32 * 2 * 512 * 128 * 4
 
 
 def test_bwd_num_splits():

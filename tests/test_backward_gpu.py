@@ -84,7 +84,7 @@ def _run_bwd(ea, q, k, v, o, dO, lse, causal, scale, poison=True, n_splits=0):
     B, H_q, N_q, D = q.shape
     H_kv, N_kv = k.shape[1], k.shape[2]
     ns = n_splits if n_splits > 0 else max(ea.attn_bwd_num_splits(B, H_q, H_kv, N_q, N_kv, D, causal), 1)
-    nbytes = ea.attn_bwd_workspace_size(B, H_q, H_kv, N_q, N_kv, D, ns)
+    nbytes = ea.attn_bwd_workspace_size(B, H_q, H_kv, N_q, N_kv, D, causal, ns)
     ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device=dev)
     ea.attn_bwd(t[0], t[1], t[2], t[3], t[4], lsed, dq, dk, dv, is_causal=causal, sm_scale=scale,
                 n_splits=n_splits, workspace=ws)
@@ -245,7 +245,7 @@ def test_backward_deterministic_and_no_overrun(ea):
     for _ in range(2):
         bufs = [torch.full((x.numel() + 4096,), 7.0, dtype=torch.bfloat16, device=dev) for x in (q, k, v)]
         dq, dk, dv = (b[:x.numel()].view(x.shape) for b, x in zip(bufs, (q, k, v)))
-        need = ea.attn_bwd_workspace_size(1, 8, 2, 333, 333, 128, 5)
+        need = ea.attn_bwd_workspace_size(1, 8, 2, 333, 333, 128, True, 5)
         wb = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device=dev)
         ea.attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, is_causal=True, n_splits=5, workspace=wb[:need])
         torch.cuda.synchronize()
