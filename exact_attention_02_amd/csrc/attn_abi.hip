@@ -64,14 +64,9 @@ hipError_t launch_fwd(bool narrow, const FwdParams& p, int grid, hipStream_t str
 template <int D>
 hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
   constexpr int tpr = D / 4;
-  const dim3 grid(static_cast<unsigned>(m.rows));
-  if (m.n_splits <= ea02::kMergeBatch * (64 / tpr))
-    hipLaunchKernelGGL((ea02::attn_merge_kernel<D, 64>), grid, dim3(64), 0, stream, m);
-  else if (m.n_splits <= ea02::kMergeBatch * (256 / tpr))
-    hipLaunchKernelGGL((ea02::attn_merge_kernel<D, 256>), grid, dim3(256), 0, stream, m);
-  else
-    hipLaunchKernelGGL((ea02::attn_merge_kernel<D, 1024>), grid, dim3(1024), 0, stream, m);
-  return hipGetLastError();
+  if (m.n_splits <= ea02::kMergeBatch * (64 / tpr)) return ea02::launch_merge_rows<D, 64>(m, stream);
+  if (m.n_splits <= ea02::kMergeBatch * (256 / tpr)) return ea02::launch_merge_rows<D, 256>(m, stream);
+  return ea02::launch_merge_rows<D, 1024>(m, stream);
 }
 
 // Arguments shared by both entry points, after validation.

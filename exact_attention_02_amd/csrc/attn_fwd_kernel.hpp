@@ -679,4 +679,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT))) void attn_merge_
   if (c == 0) p.lse[row] = tot > 0.f ? (M + __log2f(tot)) * kLn2 : -INFINITY;
 }
 
+// Launches the merge over every row, one block per row, in launches of at
+// most 2^31 work-items each (a dispatch counts its work-items in 32 bits).
+// Each launch takes a contiguous run of rows through offset pointers; m.rows
+// stays the stride between splits.
+template <int D, int NT>
+hipError_t launch_merge_rows(const MergeParams& m, hipStream_t stream) {
+  constexpr int64_t kRowsPerLaunch = (int64_t(1) << 31) / NT;
+  for (int64_t r0 = 0; r0 < m.rows; r0 += kRowsPerLaunch) {
+    const int64_t n = m.rows - r0 < kRowsPerLaunch ? m.rows - r0 : kRowsPerLaunch;
+    MergeParams c = m;
+    c.o_part = m.o_part + r0 * D;
+    c.lse_part = m.lse_part + r0;
+    c.o = m.o + r0 * D;
+    c.lse = m.lse + r0;
+    hipLaunchKernelGGL((attn_merge_kernel<D, NT>), dim3(static_cast<unsigned>(n)), dim3(NT), 0, stream, c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace ea02

@@ -138,14 +138,14 @@ extern "C" int attn_mla_decode(const void* q_lat, const void* kv, void* out_lat,
     m.lse = p.lse;
     m.rows = rows;
     m.n_splits = p.n_splits;
-    // 128 threads per row (4 of the 512 values each) times 2 or 8 split lanes
-    if (m.n_splits <= ea02::kMergeBatch * 2)
-      hipLaunchKernelGGL((ea02::attn_merge_kernel<ea02::kMlaDc, 256>), dim3(static_cast<unsigned>(rows)), dim3(256),
-                         0, s, m);
-    else
-      hipLaunchKernelGGL((ea02::attn_merge_kernel<ea02::kMlaDc, 1024>), dim3(static_cast<unsigned>(rows)),
-                         dim3(1024), 0, s, m);
-    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
+    // 128 threads per row (4 of the 512 values each) times 2 or 8 split
+    // lanes.  (Slicing a row over several blocks, to spread a decode step's
+    // few rows over more CUs, measured no faster: the merge is bound by the
+    // bytes of fp32 partials it reads, and many-row steps got slower.)
+    const hipError_t e = m.n_splits <= ea02::kMergeBatch * 2
+                             ? ea02::launch_merge_rows<ea02::kMlaDc, 256>(m, s)
+                             : ea02::launch_merge_rows<ea02::kMlaDc, 1024>(m, s);
+    if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;
 }

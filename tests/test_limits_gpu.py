@@ -14,6 +14,12 @@ oracle's attention over each chunk, combined with the oracle's split-T merge
 definition, evaluated piecewise; each chunk is converted once and serves every
 head and row.  Tolerances are the forward's: O within 2e-2 + 2e-2 |ref|, LSE
 within 1e-3.
+
+The last test forces a 33-way key split over 17 x 131072 = 2228224 output
+rows: more than 2^21 rows, so the merge (1024-thread blocks at that split
+count) runs as two launches of at most 2^31 work-items.  Sampled rows on both
+sides of the launch boundary go to the oracle; every row must also agree with
+the unsplit pass of the library within the same tolerance.
 """
 from __future__ import annotations
 
@@ -134,3 +140,42 @@ def test_causal_suffix_at_max_keys(ea, kv):
         out, lse = ea.fwd_splitkv(q.to(dev), k, v, is_causal=True, sm_scale=scale, n_splits=ns)
         torch.cuda.synchronize()
         _check(out, lse, O, L, f"attn_fwd_splitkv n_splits={ns}")
+
+
+def test_split_merge_over_many_rows(ea):
+    """2228224 rows, 33 forced key splits: the merge's second launch (rows
+    from 2^21 on) must cover its rows exactly like the first."""
+    B, H, N_q, N_kv = 1, 17, 131072, 33 * 64
+    dev = torch.device("cuda", 0)
+    scale = 1.0 / math.sqrt(D)
+    g = torch.Generator(device=dev)
+    g.manual_seed(SEED + 3)
+    q = torch.randn((B, H, N_q, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((B, H, N_kv, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((B, H, N_kv, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    print(f"[limits] split merge rows={B * H * N_q} n_splits=33", flush=True)
+    out, lse = ea.fwd_splitkv(q, k, v, is_causal=False, sm_scale=scale, n_splits=33)
+    torch.cuda.synchronize()
+    out1, lse1 = ea.fwd_splitkv(q, k, v, is_causal=False, sm_scale=scale, n_splits=1)
+    torch.cuda.synchronize()
+    # flattened row r = h * N_q + i; the second merge launch starts at r = 2^21
+    boundary = 1 << 21
+    rows = sorted({0, boundary - 1, boundary, boundary + 1, B * H * N_q - 1,
+                   *range(boundary - 64, boundary + 64, 5),
+                   *np.random.default_rng(SEED + 4).integers(0, B * H * N_q, 48).tolist()})
+    k_cpu, v_cpu, q_cpu = k.cpu(), v.cpu(), q.cpu()
+    o_g = out.cpu().to(torch.float64).numpy()[0]
+    l_g = lse.cpu().to(torch.float64).numpy()[0]
+    for h in sorted({r // N_q for r in rows}):
+        idx = [r % N_q for r in rows if r // N_q == h]
+        O, L = oracle.attention_forward(workloads.to_float64(q_cpu[:, h:h + 1, idx]),
+                                        workloads.to_float64(k_cpu[:, h:h + 1]),
+                                        workloads.to_float64(v_cpu[:, h:h + 1]),
+                                        is_causal=False, sm_scale=scale)
+        _check(torch.from_numpy(o_g[h:h + 1, idx])[None], torch.from_numpy(l_g[h:h + 1, idx])[None],
+               O[0], L[0], f"n_splits=33 head {h} rows {idx[:3]}...")
+    # every row against the unsplit pass
+    err = (out.float() - out1.float()).abs()
+    bad = err > 2e-2 + 2e-2 * out1.float().abs()
+    assert not bool(bad.any()), f"{int(bad.sum())} elements differ from the unsplit pass"
+    assert float((lse - lse1).abs().max()) <= 1e-3
