@@ -8,7 +8,9 @@ causal GQA-4, B=1, H_q=32, H_kv=8, N=32768, D=128, bf16 i.i.d. N(0,1).
 Prints ONE JSON line with the throughput in attention TFLOP/s
 (4*B*H_q*N^2*D, halved for causal), the roofline of the kernel (MFMA-bound:
 achieved TFLOP/s per launch from HIP events on the launch stream, against the
-2.5 PFLOP/s dense bf16 peak), a CPU baseline (the float64 oracle on a bounded
+2.5 PFLOP/s dense bf16 peak, and against the same MFMA rate at the shader
+clock measured during the kernel when a counter summary for the current
+sources is committed), a CPU baseline (the float64 oracle on a bounded
 sample of the same workload, on the host's cores) and a sampled-row parity
 check of the timed output against the oracle.
 
@@ -36,6 +38,7 @@ import workloads  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
+MFMA_FLOP_PER_CLK = 256 * 4096  # dense bf16 MFMA, whole chip (2.5 PFLOP/s at 2.4 GHz)
 METRIC = "attention fwd TFLOPS and % of MI355X bf16 MFMA peak (GQA causal, N=1K–32K)"
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_02_amd", "csrc", f)
                   for f in ("attn_fwd_kernel.hpp", "attn_abi.hip")]
@@ -65,6 +68,20 @@ def read_traffic(workload: str):
     if not m_hash or not m_b or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_b.group(1))
+
+
+def read_clock(workload: str):
+    """Shader clock (GHz) during the kernel from the committed rocprofv3
+    GRBM_COUNT summary, or None when missing or taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_clock.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_f = re.search(r"shader_clock_ghz:\s*([0-9.]+)", txt)
+    if not m_hash or not m_f or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_f.group(1))
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -401,6 +418,13 @@ def main():
     if flops / nbytes >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+        clock = read_clock(w.name)
+        if clock is not None:
+            # the same dense bf16 MFMA rate (4096 flop per clock per CU, 256
+            # CUs) at the clock the chip held during this kernel
+            peak_clk = MFMA_FLOP_PER_CLK * clock * 1e9 / 1e12
+            roofline.update({"clock_ghz": clock, "peak_at_clock": round(peak_clk, 1),
+                             "frac_at_clock": round(achieved / peak_clk, 4)})
     else:
         # below the ridge (decode): bytes moved, not FLOPs, bound the kernel
         gbs = nbytes / (avg_ms * 1e-3) / 1e9
