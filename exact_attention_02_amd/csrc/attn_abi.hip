@@ -19,12 +19,16 @@ using ea02::MergeParams;
 
 // Kernel shapes.  Wide: eight waves of 32 (row, head) pairs share each K/V
 // tile (256 pairs per workgroup, 64-key tiles, four LDS stages, 128 KiB LDS,
-// one workgroup per CU).  Narrow: one wave of 32 pairs (32-key tiles, two
-// stages, 32 KiB LDS at D=128) for kv heads with at most kNarrowPairs pairs,
-// e.g. a decode step, where the wide shape would leave most waves without a
-// query; five (D=128) or eight (D=64, register-bound) fit on a CU, which keeps
-// enough loads in flight for such HBM-bound work.
+// one workgroup per CU).  Mid: four such waves (128 pairs, two stages, 64 KiB
+// LDS, two workgroups per CU: the same eight waves per CU in workgroups half
+// as long), for small grids (pick_shape).  Narrow:
+// one wave of 32 pairs (32-key tiles, two stages, 32 KiB LDS at D=128) for kv
+// heads with at most kNarrowPairs pairs, e.g. a decode step, where the wide
+// shape would leave most waves without a query; five (D=128) or eight (D=64,
+// register-bound) fit on a CU, which keeps enough loads in flight for such
+// HBM-bound work.
 constexpr int kWideNW = 8, kWideP = 4, kWideBN = 64;
+constexpr int kMidNW = 4, kMidP = 2, kMidBN = 64;
 constexpr int kNarrowNW = 1, kNarrowP = 2, kNarrowBN = 32;
 constexpr int kNarrowPairs = 64;
 constexpr int kMaxSplits = 256;
@@ -35,23 +39,69 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+
+enum class Kind { kWide, kMid, kNarrow };
+
 struct Shape {
-  bool narrow;
+  Kind kind;
   int pairs_per_wg;
   int bn;
   int wg_per_cu;
 };
 
-Shape pick_shape(int64_t n_pairs, int64_t D) {
-  if (n_pairs <= kNarrowPairs) return {true, 32 * kNarrowNW, kNarrowBN, D == 128 ? 5 : 8};
-  return {false, 32 * kWideNW, kWideBN, 1};
+constexpr Shape kWideShape{Kind::kWide, 32 * kWideNW, kWideBN, 1};
+constexpr Shape kMidShape{Kind::kMid, 32 * kMidNW, kMidBN, 2};
+
+// Key splits for a grid of wgs workgroups of shape sh over n_kv keys: none
+// while the unsplit grid already fills every workgroup slot of the device;
+// otherwise enough splits for about two workgroups per CU, or one for the
+// wide shape (one fits a CU: a second round of workgroups measured slower
+// than fewer, longer splits), each split keeping at least 8 key tiles.
+int64_t splits_for(const Shape& sh, int64_t wgs, int64_t n_kv) {
+  const int64_t cus = device_cus();
+  if (wgs <= 0 || wgs >= cus * sh.wg_per_cu) return 1;
+  const int64_t tiles = (n_kv + sh.bn - 1) / sh.bn;
+  const int64_t target = std::min<int64_t>(2, sh.wg_per_cu) * cus;
+  int64_t n = (target + wgs - 1) / wgs;
+  n = std::min<int64_t>(n, tiles / 8);
+  n = std::min<int64_t>(n, kMaxSplits);
+  return n < 1 ? 1 : n;
+}
+
+// Shape of a problem with n_pairs (row, head) pairs per kv head and n_heads =
+// B * H_kv kv heads.  The mid shape replaces the wide one in two cases, both
+// measured: (1) a causal grid whose row blocks differ widely in length (N_q >
+// N_kv / 2, so the first blocks see few keys and the last ones all of them)
+// and that the wide shape covers in less than two rounds of the device: half
+// as long workgroups balance the CUs (causal GQA-4 B=2 N=1024: 40.0 -> 34.7
+// us); (2) a grid that fills less than one round even with the wide shape's
+// key splits (more, shorter workgroups).  Grids of even rows (non-causal, or
+// a short causal chunk against a long cache) at one round or more, and
+// larger grids, run 1-3 % faster with the wide shape's deeper ring.
+Shape pick_shape(int64_t n_pairs, int64_t D, int64_t n_heads, int64_t N_q, int64_t N_kv, bool causal) {
+  if (n_pairs <= kNarrowPairs) return {Kind::kNarrow, 32 * kNarrowNW, kNarrowBN, D == 128 ? 5 : 8};
+  const int64_t cus = device_cus();
+  const int64_t wide_wgs = (n_pairs + kWideShape.pairs_per_wg - 1) / kWideShape.pairs_per_wg * n_heads;
+  if (causal && 2 * N_q > N_kv && wide_wgs < 2 * cus) return kMidShape;
+  if (wide_wgs * splits_for(kWideShape, wide_wgs, N_kv) < cus) return kMidShape;
+  return kWideShape;
 }
 
 template <int D, bool SPLIT>
-hipError_t launch_fwd(bool narrow, const FwdParams& p, int grid, hipStream_t stream) {
-  if (narrow)
+hipError_t launch_fwd(Kind kind, const FwdParams& p, int grid, hipStream_t stream) {
+  if (kind == Kind::kNarrow)
     hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kNarrowNW, kNarrowP, 1, kNarrowBN, SPLIT>), dim3(grid),
                        dim3(kNarrowNW * 64), 0, stream, p);
+  else if (kind == Kind::kMid)
+    hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kMidNW, kMidP, 1, kMidBN, SPLIT>), dim3(grid),
+                       dim3(kMidNW * 64), 0, stream, p);
   else
     hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kWideNW, kWideP, 1, kWideBN, SPLIT>), dim3(grid),
                        dim3(kWideNW * 64), 0, stream, p);
@@ -79,6 +129,10 @@ struct Problem {
   int is_causal;
 };
 
+Shape problem_shape(const Problem& a) {
+  return pick_shape(a.N_q * (a.H_q / a.H_kv), a.D, a.B * a.H_kv, a.N_q, a.N_kv, a.is_causal != 0);
+}
+
 // Checks common to both entry points, in the documented order, up to and
 // including the empty-work test (*empty set when there is nothing to do).
 int check_sizes(const Problem& a, int64_t n_splits, bool* empty) {
@@ -98,7 +152,7 @@ int check_sizes(const Problem& a, int64_t n_splits, bool* empty) {
     return ATTN_ERR_SIZE_OVERFLOW;
   const int64_t n_pairs = a.N_q * (a.H_q / a.H_kv);
   if (n_pairs > (int64_t(1) << 30)) return ATTN_ERR_SIZE_OVERFLOW;
-  const Shape sh = pick_shape(n_pairs, a.D);
+  const Shape sh = problem_shape(a);
   const int64_t grid = ((n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg) * a.B * a.H_kv *
                        (n_splits > 1 ? n_splits : 1);
   if (grid > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
@@ -137,31 +191,11 @@ size_t workspace_bytes(int64_t B, int64_t H_q, int64_t N_q, int64_t D, int64_t n
   return size_t(n_splits) * size_t(B * H_q * N_q) * size_t(D + 1) * 4;
 }
 
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return 256;
-  return cus;
-}
-
-// Number of key splits the library picks: none while the unsplit grid already
-// fills every workgroup slot of the device; otherwise enough splits for about
-// two workgroups per CU, or one for the eight-wave shape (one fits a CU: a
-// second round of workgroups measured slower than fewer, longer splits), each
-// split keeping at least 8 key tiles.
+// Number of key splits the library picks (splits_for on the problem's shape).
 int64_t choose_splits(const Problem& a) {
   const int64_t n_pairs = a.N_q * (a.H_q / a.H_kv);
-  const Shape sh = pick_shape(n_pairs, a.D);
-  const int64_t wgs = ((n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg) * a.B * a.H_kv;
-  const int64_t cus = device_cus();
-  if (wgs <= 0 || wgs >= cus * sh.wg_per_cu) return 1;
-  const int64_t tiles = (a.N_kv + sh.bn - 1) / sh.bn;
-  const int64_t target = std::min<int64_t>(2, sh.wg_per_cu) * cus;
-  int64_t n = (target + wgs - 1) / wgs;
-  n = std::min<int64_t>(n, tiles / 8);
-  n = std::min<int64_t>(n, kMaxSplits);
-  return n < 1 ? 1 : n;
+  const Shape sh = problem_shape(a);
+  return splits_for(sh, ((n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg) * a.B * a.H_kv, a.N_kv);
 }
 
 // Launch after every check passed: one pass when n_splits <= 1, else the split
@@ -169,7 +203,7 @@ int64_t choose_splits(const Problem& a) {
 int run(const Problem& a, int64_t n_splits, void* ws, void* stream) {
   const int G = static_cast<int>(a.H_q / a.H_kv);
   const int64_t n_pairs = a.N_q * G;
-  const Shape sh = pick_shape(n_pairs, a.D);
+  const Shape sh = problem_shape(a);
   const int64_t n_pair_blocks = (n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg;
   const bool split = n_splits > 1;
   const int64_t grid = n_pair_blocks * a.B * a.H_kv * (split ? n_splits : 1);
@@ -205,9 +239,9 @@ int run(const Problem& a, int64_t n_splits, void* ws, void* stream) {
   const int g32 = static_cast<int>(grid);
   hipError_t err;
   if (!split)
-    err = (a.D == 128) ? launch_fwd<128, false>(sh.narrow, p, g32, s) : launch_fwd<64, false>(sh.narrow, p, g32, s);
+    err = (a.D == 128) ? launch_fwd<128, false>(sh.kind, p, g32, s) : launch_fwd<64, false>(sh.kind, p, g32, s);
   else
-    err = (a.D == 128) ? launch_fwd<128, true>(sh.narrow, p, g32, s) : launch_fwd<64, true>(sh.narrow, p, g32, s);
+    err = (a.D == 128) ? launch_fwd<128, true>(sh.kind, p, g32, s) : launch_fwd<64, true>(sh.kind, p, g32, s);
   if (err != hipSuccess) return ATTN_ERR_LAUNCH;
   if (split) {
     MergeParams m;

@@ -148,6 +148,24 @@ def test_ragged_lengths(ea, N, D, causal):
     _full_case(ea, 1, 4, 2, N, D, causal, seed=7000 + N + D)
 
 
+@pytest.mark.parametrize("H,D,causal", [(64, 128, False), (128, 64, True), (128, 128, True)])
+def test_ragged_wide_grid(ea, H, D, causal):
+    """N = 1000 over enough heads that the grid fills the 256 CUs (one round
+    of eight-wave workgroups non-causal, two causal): the library takes the
+    wide shape here, while the small cases above run the four-wave shape.
+    Also through attn_fwd_splitkv with three forced key splits."""
+    q, k, v = workloads.make_inputs(1, H, H, 1000, D, seed=7500 + H + D)
+    scale = 1.0 / math.sqrt(D)
+    O_ref, L_ref = oracle.attention_forward(workloads.to_float64(q), workloads.to_float64(k),
+                                            workloads.to_float64(v), is_causal=causal, sm_scale=scale)
+    o, l = _run(ea, q, k, v, causal, scale)
+    _check(o, l, O_ref, L_ref, what=f"wide H{H} D{D} c{int(causal)}")
+    dev = torch.device("cuda", 0)
+    o, l = ea.fwd_splitkv(q.to(dev), k.to(dev), v.to(dev), is_causal=causal, sm_scale=scale, n_splits=3)
+    torch.cuda.synchronize()
+    _check(o.cpu(), l.cpu(), O_ref, L_ref, what=f"wide split3 H{H} D{D} c{int(causal)}")
+
+
 @pytest.mark.parametrize("H_q,H_kv", [(3, 3), (6, 2), (6, 1), (8, 4), (16, 2), (32, 2), (12, 3)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_head_groupings(ea, H_q, H_kv, causal):
