@@ -107,6 +107,16 @@ def _oracle_unit_shared(args):
     return _oracle_unit((q, k, v) + tuple(args))
 
 
+def _blas_name():
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                if i.get("user_api") == "blas"]
+        return ", ".join(libs) or None
+    except Exception:  # reporting only
+        return None
+
+
 def cpu_baseline(w, q64, k64, v64, budget_s=15.0):
     """Time the oracle on random 512-row blocks of random heads until about
     budget_s of wall time is used, over a process pool of one worker per core."""
@@ -154,6 +164,8 @@ def cpu_baseline(w, q64, k64, v64, budget_s=15.0):
         "value": round(flops / wall / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": cores,
+        "numpy": np.__version__,
+        "blas": _blas_name(),
         "kind": "oracle",
         "sample": (f"{done} blocks of {blk} query rows at random (b, h, row offset) of the "
                    f"{w.name} workload, float64 NumPy oracle, {cores} worker processes with "
@@ -293,7 +305,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -438,6 +450,7 @@ def main():
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     kernel = "attn_fwd_kernel" if res["n_splits"] == 1 else "attn_fwd_kernel split pass + attn_merge_kernel"
     roofline.update({"traffic": traffic, "kernel": kernel, "avg_launch_ms": round(avg_ms, 4),
+                     "median_launch_ms": round(float(np.median(ev)), 4), "min_launch_ms": round(min(ev), 4),
                      "n_splits": res["n_splits"],
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes})
     line = {
