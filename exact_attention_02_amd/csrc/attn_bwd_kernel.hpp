@@ -425,12 +425,13 @@ struct BwdQCfg {
   static_assert((P - 1) * GROUP_LOADS <= 63, "loads in flight fit the 6-bit vmcnt");
 };
 
-// Eight waves share one workgroup's LDS ring at two waves per SIMD: one wave's
-// exponentials and dS run while the other's MFMAs issue (the register budget,
-// 256 per wave, still holds the 32-pair accumulators without spilling).
+// Two waves per SIMD: eight waves share one workgroup's LDS ring, or four
+// waves with two stages leave room for a second workgroup on the CU; one
+// wave's exponentials and dS run while the other's MFMAs issue (the register
+// budget, 256 per wave, still holds the 32-pair accumulators without spilling).
 template <int D, int NW, int P, int BN>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
-                          amdgpu_waves_per_eu(NW >= 8 ? 2 : 1, NW >= 8 ? 2 : 1)))
+                          amdgpu_waves_per_eu((NW >= 8 || P <= 2) ? 2 : 1, (NW >= 8 || P <= 2) ? 2 : 1)))
 void attn_bwd_dq_kernel(BwdParams p) {
   using C = BwdQCfg<D, NW, P, BN>;
   constexpr int PPW = 32 * NW;  // (row, head) pairs per workgroup
