@@ -60,6 +60,26 @@ struct MlaParams {
 // rows r and r+2 in different 4-chunk halves.
 __device__ __forceinline__ int mla_swz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
 
+// acc *= alpha on an accumulator the MFMAs keep in AGPRs, each element read,
+// scaled and written back by inline asm.  Written as plain VALU code, this
+// rare rescale makes the compiler keep VGPR copies of all 128 accumulator
+// registers and copy them on every tile, whether or not the rescale runs.
+// The compiler does not see into the asm for MFMA hazards: the last MFMA
+// that wrote acc (the previous tile's P V) is followed by the barrier and the
+// whole score chain before this runs, and the two wait states after each
+// write cover an MFMA reading it next.
+__device__ __forceinline__ void scale_agpr(f32x16& acc, float alpha) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = acc[r];
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1\n\ts_nop 1"
+                 : "+a"(x), "=&v"(tmp)
+                 : "v"(alpha));
+    acc[r] = x;
+  }
+}
+
 template <int P, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void attn_mla_kernel(MlaParams p) {
@@ -176,15 +196,17 @@ void attn_mla_kernel(MlaParams p) {
       const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + col * kMlaRowBytes + (chunk << 4)));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[i], s, 0, 0, 0);
     }
+    // partials as [r4][wave][lane] float4: a wave's 64 lanes store and load
+    // 1 KiB contiguous per access (no bank conflicts)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
-      *reinterpret_cast<f32x4*>(part + ((wave * 64 + lane) * 16 + 4 * r4)) =
+      *reinterpret_cast<f32x4*>(part + ((r4 * NW + wave) * 64 + lane) * 4) =
           f32x4{s[4 * r4], s[4 * r4 + 1], s[4 * r4 + 2], s[4 * r4 + 3]};
     __syncthreads();
     const int other = wave ^ 2;  // same pair block, other half
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(part + ((other * 64 + lane) * 16 + 4 * r4));
+      const f32x4 x = *reinterpret_cast<const f32x4*>(part + ((r4 * NW + other) * 64 + lane) * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[4 * r4 + e] += x[e];
     }
@@ -204,7 +226,7 @@ void attn_mla_kernel(MlaParams p) {
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      for (int db = 0; db < NDB; ++db) scale_agpr(acc[db], alpha);
       m_used = m_new;
     }
     const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;

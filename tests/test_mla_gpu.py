@@ -108,6 +108,32 @@ def test_latent_core_heads_and_tokens(ea, H, S, T, n_splits):
         _check_attn(o, l, O, L, f"H{H} S{S} T{T} c{int(causal)}")
 
 
+@pytest.mark.parametrize("n_splits", [1, 2])
+def test_latent_core_growing_scores(ea, n_splits):
+    """Cache rows whose norm grows along T: the running max of a row rises
+    by more than the lazy-rescale slack (8 in log2 units) on many tiles, so
+    the accumulators are rescaled again and again.  The inputs are checked
+    on the CPU to force at least 4 such rises for every row (the max over a
+    32-key tile against the largest max so far plus 8, in fp64)."""
+    B, H, S, T = 1, 64, 1, 1024
+    q_lat, kv = _latent_inputs(B, H, S, T, seed=13300)
+    ramp = torch.linspace(0.1, 6.0, T).view(1, T, 1)
+    kv = (kv.float() * ramp).to(torch.bfloat16)
+    sc = 0.3
+    s2 = np.einsum("bhsd,btd->bhst", _f64(q_lat), _f64(kv)) * sc / math.log(2)
+    tile_max = s2.reshape(B, H, S, T // 32, 32).max(-1)
+    rises = np.zeros((B, H, S), dtype=np.int64)
+    m_used = tile_max[..., 0]
+    for t in range(1, T // 32):
+        up = tile_max[..., t] > m_used + 8
+        rises += up
+        m_used = np.where(up, tile_max[..., t], m_used)
+    assert rises.min() >= 4, f"inputs force too few rescales: min {rises.min()}"
+    o, l = _run_core(ea, q_lat, kv, sc, False, n_splits)
+    O, L = oracle.mla_latent_attention(_f64(q_lat), _f64(kv), 512, is_causal=False, sm_scale=sc)
+    _check_attn(o, l, O, L, f"growing scores s{n_splits}")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.05, 0.3])
 def test_latent_core_scales(ea, scale):
     q_lat, kv = _latent_inputs(1, 32, 1, 500, seed=13200)
