@@ -17,7 +17,10 @@
  * keeps no state between calls and never allocates device memory.
  * Kernel shapes (not part of the contract): kv heads with more than 64
  * (query row, query head) pairs run on eight-wave workgroups with 64-key
- * tiles, smaller ones (decode) on one-wave workgroups with 32-key tiles.
+ * tiles, or on four-wave ones when that grid is small (uneven causal rows
+ * covering less than two rounds of the device, or less than one round even
+ * after key splits); smaller kv heads (decode) on one-wave workgroups with
+ * 32-key tiles.
  */
 #ifndef EA02_ATTN_H
 #define EA02_ATTN_H
@@ -140,9 +143,9 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, flo
  * attn_splitkv_num_splits -- the split count attn_fwd_splitkv uses for
  * n_splits = 0 on the current device: 1 when the unsplit launch already fills
  * every workgroup slot, otherwise enough splits for about two workgroups per
- * CU (one per CU for the eight-wave shape of more than 64 (row, head) pairs
- * per kv head, which fits one workgroup per CU), with at least eight key
- * tiles per split and at most 256.  Returns -1 when the
+ * CU (one per CU for the eight-wave shape, which fits one workgroup per CU),
+ * with at least eight key tiles per split and at most 256.  The shape is
+ * chosen first, from the unsplit grid.  Returns -1 when the
  * sizes fail attn_fwd_splitkv's size checks (NEGATIVE_SIZE .. SIZE_OVERFLOW).
  * Queries the current device's CU count; enqueues nothing.
  */
