@@ -153,11 +153,10 @@ extern "C" int attn_mla_decode(const void* q_lat, const void* kv, void* out_lat,
 extern "C" int mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_uk, void* q_lat, int64_t B,
                             int64_t H, int64_t S, int64_t d_nope, int64_t d_c, int64_t d_r, void* stream) {
   if (B < 0 || H < 0 || S < 0 || d_nope < 0 || d_c < 0 || d_r < 0) return ATTN_ERR_NEGATIVE_SIZE;
-  if (d_c != ea02::kMlaDc || d_r != ea02::kMlaDr || d_nope < 1 || d_nope > 256) return ATTN_ERR_HEAD_DIM;
+  if (d_c != ea02::kMlaDc || d_r != ea02::kMlaDr || d_nope < 1 || d_nope > ea02::kAbsorbMaxK) return ATTN_ERR_HEAD_DIM;
   if (B > (1 << 24) || H > (1 << 16) || S > (1 << 24) || B * S > INT32_MAX / 2 || B * H * S > INT32_MAX)
     return ATTN_ERR_SIZE_OVERFLOW;
-  const int64_t groups = (B * S + ea02::kProjRows - 1) / ea02::kProjRows;
-  if (groups * H > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
+  if (H * (ea02::kMlaDc / ea02::kAbsorbSlice) > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
   if (B == 0 || H == 0 || S == 0) return ATTN_OK;
   if (!q_nope || !q_pe || !w_uk || !q_lat) return ATTN_ERR_NULL_POINTER;
   if ((reinterpret_cast<uintptr_t>(q_nope) & 1u) || mis16(q_pe) || mis16(w_uk) || mis16(q_lat))
@@ -177,30 +176,11 @@ extern "C" int mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_
   p.d_n = static_cast<int>(d_nope);
   p.rows_per_head = static_cast<int>(B * S);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // passes of kProjRows rows of every head, then one pass over the remaining rows
-  const int64_t rows = B * S;
-  const int64_t full = rows / ea02::kProjRows;
-  const int rem = static_cast<int>(rows - full * ea02::kProjRows);
-  if (full > 0) {
-    p.row_base = 0;
-    hipLaunchKernelGGL(ea02::mla_absorb_kernel<ea02::kProjRows>, dim3(static_cast<unsigned>(full * H)), dim3(256),
-                       0, s, p);
-    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
-  }
-  if (rem > 0) {
-    p.row_base = static_cast<int>(full * ea02::kProjRows);
-    const dim3 g(static_cast<unsigned>(H));
-    switch (rem) {
-      case 1: hipLaunchKernelGGL(ea02::mla_absorb_kernel<1>, g, dim3(256), 0, s, p); break;
-      case 2: hipLaunchKernelGGL(ea02::mla_absorb_kernel<2>, g, dim3(256), 0, s, p); break;
-      case 3: hipLaunchKernelGGL(ea02::mla_absorb_kernel<3>, g, dim3(256), 0, s, p); break;
-      case 4: hipLaunchKernelGGL(ea02::mla_absorb_kernel<4>, g, dim3(256), 0, s, p); break;
-      case 5: hipLaunchKernelGGL(ea02::mla_absorb_kernel<5>, g, dim3(256), 0, s, p); break;
-      case 6: hipLaunchKernelGGL(ea02::mla_absorb_kernel<6>, g, dim3(256), 0, s, p); break;
-      default: hipLaunchKernelGGL(ea02::mla_absorb_kernel<7>, g, dim3(256), 0, s, p); break;
-    }
-    if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
-  }
+  // one block per (head, 128-column slice), every row of the head in it
+  const int kp = static_cast<int>((d_nope + 15) & ~int64_t(15));
+  hipLaunchKernelGGL(ea02::mla_absorb_kernel, dim3(static_cast<unsigned>(H * (ea02::kMlaDc / ea02::kAbsorbSlice))),
+                     dim3(256), ea02::absorb_lds_bytes(kp), s, p);
+  if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
   return ATTN_OK;
 }
 
@@ -228,7 +208,6 @@ extern "C" int mla_up_project(const void* out_lat, const void* w_uv, void* out, 
   p.S = static_cast<int>(S);
   p.d_n = static_cast<int>(d_v);
   p.rows_per_head = static_cast<int>(B * S);
-  p.row_base = 0;
   hipLaunchKernelGGL(ea02::mla_up_kernel, dim3(static_cast<unsigned>(blocks)), dim3(64), 0,
                      static_cast<hipStream_t>(stream), p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;

@@ -305,89 +305,128 @@ struct MlaProjParams {
   uint16_t* y;          // absorb: q_lat [B, H, S, 576];   up: out [B, H, S, d_v]
   int B, H, S, d_n;     // d_n: d_nope (absorb) or d_v (up)
   int rows_per_head;    // B * S
-  int row_base;         // absorb: first row of this launch's passes
 };
 
-constexpr int kProjRows = 8;       // query rows per absorb pass
-constexpr int kAbsorbDG = 4;       // d-groups per absorb block
-constexpr int kAbsorbUnroll = 8;   // weight rows in flight per thread
+constexpr int kAbsorbSlice = 128;   // output columns per absorb block
+constexpr int kAbsorbMaxK = 256;    // largest d_nope
 
-// q_lat[r, c] = sum_d q_nope[r, d] W_uk[h, d, c] for up to 8 rows r of head h,
-// q_lat[r, 512 + e] = q_pe[r, e].  A block of 256 threads covers one head and
-// one group of rows: thread t owns columns 8 (t % 64) .. +8 and every 4th
-// weight row d = t / 64 + 4 i, reading 16 bytes of W_uk per row with 8 rows
-// in flight (the weights are read once and streamed), and the four d-groups
-// are added through LDS.  R is the number of rows of the pass (1..8).
-template <int R>
+// LDS of one absorb block for kp = d_nope rounded up to 16: the W_uk slice
+// (kp rows of 256 bytes), then 32 staged query rows of kp + 8 values (16
+// bytes of padding per row).
+__host__ __device__ constexpr int absorb_lds_bytes(int kp) { return kp * 256 + 32 * (kp + 8) * 2; }
+
+// 16-byte chunk swizzle of the staged W_uk slice (rows of 128 values): a
+// bijection on 16 rows for 16-byte row access, and the transpose read (4 rows
+// x 4 chunks per 16 lanes) lands on 16 different chunk positions.
+__device__ __forceinline__ int absorb_swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+
+// q_lat[r, c] = sum_d q_nope[r, d] W_uk[h, d, c], q_lat[r, 512 + e] = q_pe[r, e].
+// A block of four waves owns head h and 128 output columns: it stages that
+// slice of W_uk[h] (d_nope rows, zero-padded to a multiple of 16) in LDS once
+// and runs every query row of the head past it in blocks of 32.  Wave w
+// computes the 32 x 32 block Y^T = W^T X^T for columns 32 w .. +32 with MFMA:
+// A = W^T from the LDS transpose read, B = the matching 8 values of d of a
+// query row staged in LDS (q_nope rows are only 2-byte aligned).  W_uk is
+// read from memory exactly once.  Dynamic LDS: absorb_lds_bytes(kp).
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void mla_absorb_kernel(MlaProjParams p) {
-  __shared__ float xs[kProjRows][256];
-  __shared__ f32x4 red[kAbsorbDG - 1][64][R][2];
-  const int h = blockIdx.x % p.H;
-  const int r0 = p.row_base + (blockIdx.x / p.H) * kProjRows;
-  const int t = threadIdx.x;
-  const int cg = t % 64, dg = t / 64;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t absorb_lds[];
+  constexpr int n_cs = kMlaDc / kAbsorbSlice;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int h = blockIdx.x / n_cs;
+  const int cs = blockIdx.x % n_cs;
+  const int dn = p.d_n;
+  const int kp = (dn + 15) & ~15;
+  const int xstride = kp + 8;
+  uint8_t* wsl = absorb_lds;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(absorb_lds + kp * 256);
   // row r of head h is (b, s) = (r / S, r % S)
-  auto row_index = [&](int r) {
-    const int rr = r0 + r;
-    return ((size_t)(rr / p.S) * p.H + h) * p.S + (rr % p.S);
-  };
-  for (int i = t; i < R * p.d_n; i += 256) {
-    const int r = i / p.d_n, d = i - r * p.d_n;
-    xs[r][d] = (float)__builtin_bit_cast(__bf16, p.x[row_index(r) * p.d_n + d]);
-  }
-  __syncthreads();
-  f32x4 acc[R][2];
+  auto row_index = [&](int r) { return ((size_t)(r / p.S) * p.H + h) * p.S + (r % p.S); };
+
+  // W_uk[h, d, 128 cs .. +128] -> wsl row d, chunk j at (j ^ swz(d)); at most
+  // 16 chunks per thread, all loads issued before the stores
+  const uint16_t* wh = p.w + (size_t)h * dn * kMlaDc + cs * kAbsorbSlice;
+  {
+    u32x4 v[kAbsorbMaxK * 16 / 256];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* wh = p.w + (size_t)h * p.d_n * kMlaDc + 8 * cg;
-  for (int d0 = dg; d0 < p.d_n; d0 += kAbsorbDG * kAbsorbUnroll) {
-    u32x4 wv[kAbsorbUnroll];
-#pragma unroll
-    for (int u = 0; u < kAbsorbUnroll; ++u) {
-      const int d = min(d0 + kAbsorbDG * u, p.d_n - 1);
-      wv[u] = *reinterpret_cast<const u32x4*>(wh + (size_t)d * kMlaDc);
+    for (int i = 0; i < kAbsorbMaxK * 16 / 256; ++i) {
+      const int e = tid + 256 * i, d = e >> 4, j = e & 15;
+      v[i] = d < dn ? *reinterpret_cast<const u32x4*>(wh + (size_t)d * kMlaDc + 8 * j) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < kAbsorbUnroll; ++u) {
-      const int d = d0 + kAbsorbDG * u;
-      if (d < p.d_n) {
-        const bf16x8 wb = as_bf16x8(wv[u]);
-        f32x4 w0 = {(float)wb[0], (float)wb[1], (float)wb[2], (float)wb[3]};
-        f32x4 w1 = {(float)wb[4], (float)wb[5], (float)wb[6], (float)wb[7]};
+    for (int i = 0; i < kAbsorbMaxK * 16 / 256; ++i) {
+      const int e = tid + 256 * i, d = e >> 4, j = e & 15;
+      if (d < kp) *reinterpret_cast<u32x4*>(wsl + d * 256 + ((j ^ absorb_swz(d)) << 4)) = v[i];
+    }
+  }
+  // transpose-read offsets: d rows 4 half + L/4 (+8 for the second read) of a
+  // 16-row step, columns 32 wave + 16 (G16 & 1) + 4 (L & 3)
+  const int L16 = lane & 15;
+  int tr_off[2];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float xv = xs[r][d];
-          acc[r][0] += xv * w0;
-          acc[r][1] += xv * w1;
-        }
+  for (int hi = 0; hi < 2; ++hi) {
+    const int row = 4 * half + (L16 >> 2) + 8 * hi;
+    const int c = wave * 32 + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
+    tr_off[hi] = row * 256 + (((c >> 3) ^ absorb_swz(row)) << 4) + (c & 7) * 2;
+  }
+
+  for (int r0 = 0; r0 < p.rows_per_head; r0 += 32) {
+    __syncthreads();  // the W slice is staged; the previous rows are read
+    // 32 query rows, zero past d_nope and past the last row; thread t takes
+    // row t / 8 and every 8th value of it
+    {
+      const int r = tid >> 3, d0 = tid & 7;
+      const int rr = r0 + r;
+      const bool live = rr < p.rows_per_head;
+      const uint16_t* xr = p.x + (live ? row_index(rr) * dn : 0);
+      uint16_t xv[kAbsorbMaxK / 8];
+#pragma unroll
+      for (int i = 0; i < kAbsorbMaxK / 8; ++i) {
+        const int d = d0 + 8 * i;
+        xv[i] = (live && d < dn) ? xr[d] : uint16_t(0);
+      }
+#pragma unroll
+      for (int i = 0; i < kAbsorbMaxK / 8; ++i) {
+        const int d = d0 + 8 * i;
+        if (d < kp) xs[r * xstride + d] = xv[i];
       }
     }
-  }
-  if (dg > 0) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      red[dg - 1][cg][r][0] = acc[r][0];
-      red[dg - 1][cg][r][1] = acc[r][1];
+    __syncthreads();
+    f32x16 acc = f32x16{};
+    for (int ks = 0; ks < kp / 16; ++ks) {
+      const uint8_t* a = wsl + (16 * ks) * 256;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[1]));
+      const bf16x8 wT = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      // the transpose read returns the k-step's rows 4 half .. +4 and 8 + 4
+      // half .. +4 (the order of an MFMA accumulator), so B takes the same d
+      const u32x2 x0 = *reinterpret_cast<const u32x2*>(xs + col * xstride + 16 * ks + 4 * half);
+      const u32x2 x1 = *reinterpret_cast<const u32x2*>(xs + col * xstride + 16 * ks + 8 + 4 * half);
+      const bf16x8 xf = as_bf16x8(u32x4{x0[0], x0[1], x1[0], x1[1]});
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wT, xf, acc, 0, 0, 0);
     }
-  }
-  __syncthreads();
-  if (dg != 0) return;
+    // element k holds column 32 wave + 8 (k/4) + 4 half + k%4 of row r0 + col
+    const int rr = r0 + col;
+    if (rr < p.rows_per_head) {
+      const size_t row = row_index(rr);
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-#pragma unroll
-    for (int g = 0; g < kAbsorbDG - 1; ++g) {
-      acc[r][0] += red[g][cg][r][0];
-      acc[r][1] += red[g][cg][r][1];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c = cs * kAbsorbSlice + wave * 32 + 8 * g4 + 4 * half;
+        const f32x4 f = {acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
+        *reinterpret_cast<u32x2*>(p.y + row * kMlaDqk + c) = __builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4));
+      }
     }
-    const size_t row = row_index(r);
-    const bf16x4 lo = __builtin_convertvector(acc[r][0], bf16x4);
-    const bf16x4 hi = __builtin_convertvector(acc[r][1], bf16x4);
-    *reinterpret_cast<u32x4*>(p.y + row * kMlaDqk + 8 * cg) =
-        u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-              __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-    if (cg < kMlaDr / 8)
-      *reinterpret_cast<u32x4*>(p.y + row * kMlaDqk + kMlaDc + 8 * cg) =
-          *reinterpret_cast<const u32x4*>(p.x2 + row * kMlaDr + 8 * cg);
+    // the rotary part is copied by the first column slice: 32 rows x 8 chunks
+    if (cs == 0) {
+      const int r = tid >> 3, j = tid & 7;
+      if (r0 + r < p.rows_per_head) {
+        const size_t row = row_index(r0 + r);
+        *reinterpret_cast<u32x4*>(p.y + row * kMlaDqk + kMlaDc + 8 * j) =
+            *reinterpret_cast<const u32x4*>(p.x2 + row * kMlaDr + 8 * j);
+      }
+    }
   }
 }
 

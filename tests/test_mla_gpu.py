@@ -159,6 +159,30 @@ def test_projections(ea):
     _check_scaled(y.cpu(), oracle.mla_up_project(_f64(x), _f64(W_uv)), "up")
 
 
+@pytest.mark.parametrize("d_nope,B,H,S", [(128, 1, 128, 1), (128, 32, 128, 1), (1, 2, 3, 1), (17, 5, 4, 7),
+                                           (64, 3, 8, 12), (100, 1, 6, 70), (192, 2, 4, 33),
+                                           (256, 4, 5, 9)])
+def test_absorb_shapes(ea, d_nope, B, H, S):
+    """mla_absorb_q over d_nope 1..256 (zero-padded to whole k-steps inside),
+    row counts spanning several 32-row blocks with a ragged last one, and a
+    q_nope that starts 2 bytes past a 16-byte boundary."""
+    dev = _dev()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(13400 + d_nope + B * H * S)
+    q_nope = torch.randn((B, H, S, d_nope), generator=g).to(torch.bfloat16)
+    q_pe = torch.randn((B, H, S, 64), generator=g).to(torch.bfloat16)
+    W_uk = (torch.randn((H, d_nope, 512), generator=g) / math.sqrt(d_nope)).to(torch.bfloat16)
+    buf = torch.empty(q_nope.numel() + 1, dtype=torch.bfloat16, device=dev)
+    qn = buf[1:].view(q_nope.shape)
+    qn.copy_(q_nope.to(dev))
+    q_lat = torch.full((B, H, S, 576), float("nan"), dtype=torch.bfloat16, device=dev)
+    ea.mla_absorb_q(qn, q_pe.to(dev), W_uk.to(dev), q_lat)
+    torch.cuda.synchronize()
+    ref = oracle.mla_absorb_q(_f64(q_nope), _f64(q_pe), _f64(W_uk))
+    _check_scaled(q_lat.cpu()[..., :512], ref[..., :512], f"absorb d{d_nope}")
+    assert torch.equal(q_lat.cpu()[..., 512:].view(torch.int16), q_pe.view(torch.int16)), "q_pe copy"
+
+
 @pytest.mark.parametrize("B,H,S,T,causal", [(2, 16, 1, 200, True), (1, 128, 1, 300, True),
                                             (1, 8, 3, 50, True), (33, 4, 1, 40, False)])
 def test_pipeline_against_naive(ea, B, H, S, T, causal):
