@@ -307,7 +307,9 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_OK: return "success";
     case ATTN_ERR_NEGATIVE_SIZE: return "a size argument is negative";
     case ATTN_ERR_HEAD_RATIO: return "H_kv must be >= 1 and divide H_q";
-    case ATTN_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
+    case ATTN_ERR_HEAD_DIM:
+      return "unsupported head dimension (D 64 or 128; MLA: d_c 512, d_R 64, d_nope 1..256, d_v a multiple of 32 "
+             "up to 1024)";
     case ATTN_ERR_CAUSAL_FLAG: return "is_causal must be 0 or 1";
     case ATTN_ERR_SCALE: return "sm_scale must be finite";
     case ATTN_ERR_SIZE_OVERFLOW:
@@ -318,7 +320,7 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_CAUSAL_SHAPE: return "is_causal needs N_q <= N_kv";
     case ATTN_ERR_NO_KEYS: return "N_kv is 0 while there are query rows";
-    case ATTN_ERR_SPLITS: return "n_splits must be in [0, 256]";
+    case ATTN_ERR_SPLITS: return "n_splits must be in [0, 256] (attn_bwd: [0, 64])";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL, too small or not 16-byte aligned";
     default: return "unknown status";
   }

@@ -38,7 +38,7 @@ enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NEGATIVE_SIZE = 1,  /* B, H_q, H_kv, N or D below zero              */
   ATTN_ERR_HEAD_RATIO = 2,     /* H_kv < 1 or H_q not a multiple of H_kv       */
-  ATTN_ERR_HEAD_DIM = 3,       /* D is neither 64 nor 128                      */
+  ATTN_ERR_HEAD_DIM = 3,       /* D not 64 or 128 (MLA: its fixed dimensions) */
   ATTN_ERR_CAUSAL_FLAG = 4,    /* is_causal is neither 0 nor 1                 */
   ATTN_ERR_SCALE = 5,          /* sm_scale is NaN or infinite                  */
   ATTN_ERR_SIZE_OVERFLOW = 6,  /* N > 2^24, N*D*2 > 2^31 (one kv head's K rows
