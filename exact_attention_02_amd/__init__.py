@@ -1,8 +1,9 @@
-"""MI355X (gfx950) fused attention forward: thin Python binding of libea02_attn.so.
+"""MI355X (gfx950) exact attention: thin Python binding of libea02_attn.so.
 
-The binding only marshals arguments: every step of the attention forward runs
-in the library's HIP kernels.  PyTorch supplies device memory and the stream.
-If the library is not built, every call raises; there is no fallback path.
+The fused forward, its split-KV and decode form, the backward and absorbed
+MLA decode.  The binding only marshals arguments: every step runs in the
+library's HIP kernels.  PyTorch supplies device memory and the stream.  If
+the library is not built, every call raises; there is no fallback path.
 
     out, lse = fwd(q, k, v, is_causal=True)          # allocates out and lse
     attn_fwd(q, k, v, out, lse, is_causal=True)      # caller-provided buffers
@@ -40,9 +41,12 @@ _lib = None
 
 
 class AttnError(RuntimeError):
-    def __init__(self, status: int, message: str):
-        super().__init__(f"attn_fwd failed with status {status}: {message}")
+    """A library entry point returned a nonzero status (see include/attn.h)."""
+
+    def __init__(self, status: int, message: str, call: str = "libea02_attn"):
+        super().__init__(f"{call} failed with status {status}: {message}")
         self.status = status
+        self.call = call
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
@@ -146,7 +150,7 @@ def attn_fwd(q, k, v, out, lse, is_causal: bool = False, sm_scale: float | None 
         st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           B, H_q, H_kv, N, D, float(sm_scale), int(bool(is_causal)), handle)
     if st != 0:
-        raise AttnError(st, attn_status_string(st))
+        raise AttnError(st, attn_status_string(st), "attn_fwd")
 
 
 def fwd(q, k, v, is_causal: bool = False, sm_scale: float | None = None, stream=None):
@@ -206,7 +210,7 @@ def attn_fwd_splitkv(q, k, v, out, lse, is_causal: bool = False, sm_scale: float
                                   lse.data_ptr(), B, H_q, H_kv, N_q, N_kv, D, float(sm_scale),
                                   int(bool(is_causal)), int(n_splits), ws_ptr, ws_bytes, handle)
     if st != 0:
-        raise AttnError(st, attn_status_string(st))
+        raise AttnError(st, attn_status_string(st), "attn_fwd_splitkv")
 
 
 def fwd_splitkv(q, k, v, is_causal: bool = False, sm_scale: float | None = None,
@@ -283,7 +287,7 @@ def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, is_causal: bool = False,
                           B, H_q, H_kv, N_q, N_kv, D, float(sm_scale), int(bool(is_causal)),
                           int(n_splits), ws_ptr, ws_bytes, handle)
     if st != 0:
-        raise AttnError(st, attn_status_string(st))
+        raise AttnError(st, attn_status_string(st), "attn_bwd")
 
 
 def bwd(q, k, v, out, dout, lse, is_causal: bool = False, sm_scale: float | None = None,
@@ -345,7 +349,7 @@ def attn_mla_decode(q_lat, kv, out_lat, lse, sm_scale: float, is_causal: bool = 
                                             float(sm_scale), int(bool(is_causal)), int(n_splits),
                                             ws_ptr, ws_bytes, handle)
     if st != 0:
-        raise AttnError(st, attn_status_string(st))
+        raise AttnError(st, attn_status_string(st), "attn_mla_decode")
 
 
 def mla_absorb_q(q_nope, q_pe, w_uk, q_lat, stream=None) -> None:
@@ -361,7 +365,7 @@ def mla_absorb_q(q_nope, q_pe, w_uk, q_lat, stream=None) -> None:
         st = load_library().mla_absorb_q(q_nope.data_ptr(), q_pe.data_ptr(), w_uk.data_ptr(),
                                          q_lat.data_ptr(), B, H, S, dn, MLA_DC, MLA_DR, handle)
     if st != 0:
-        raise AttnError(st, attn_status_string(st))
+        raise AttnError(st, attn_status_string(st), "mla_absorb_q")
 
 
 def mla_up_project(out_lat, w_uv, out, stream=None) -> None:
@@ -377,7 +381,7 @@ def mla_up_project(out_lat, w_uv, out, stream=None) -> None:
         st = load_library().mla_up_project(out_lat.data_ptr(), w_uv.data_ptr(), out.data_ptr(),
                                            B, H, S, MLA_DC, d_v, handle)
     if st != 0:
-        raise AttnError(st, attn_status_string(st))
+        raise AttnError(st, attn_status_string(st), "mla_up_project")
 
 
 def mla_decode(q_nope, q_pe, kv, w_uk, w_uv, sm_scale: float | None = None,

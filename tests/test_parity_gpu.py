@@ -278,3 +278,4 @@ def test_status_error_raises(ea):
     with pytest.raises(ea.AttnError) as e:
         ea.fwd(q, q, q)
     assert e.value.status == 3
+    assert e.value.call == "attn_fwd" and "attn_fwd failed with status 3" in str(e.value)

@@ -254,4 +254,4 @@ def test_split_errors_raise(ea):
     lse = torch.empty((1, 4, 8), dtype=torch.float32, device=dev)
     with pytest.raises(ea.AttnError) as e:
         ea.attn_fwd_splitkv(q, k, k, out, lse, n_splits=4, workspace=None)
-    assert e.value.status == 14
+    assert e.value.status == 14 and e.value.call == "attn_fwd_splitkv"
