@@ -272,6 +272,45 @@ def test_side_stream(ea):
     assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)) and torch.equal(l, ref_l)
 
 
+def test_concurrent_host_threads(ea):
+    """Two host threads enqueue forwards (single pass and key splits) on
+    their own streams at the same time; every result equals, bit for bit,
+    the same call made alone.  The library keeps no state between calls."""
+    import threading
+    dev = torch.device("cuda", 0)
+    cases = []
+    for i, (H_q, H_kv, N, n_splits) in enumerate([(8, 2, 700, 1), (4, 4, 513, 3)]):
+        q, k, v = workloads.make_inputs(1, H_q, H_kv, N, 128, seed=60 + i)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        ref = ea.fwd_splitkv(qd, kd, vd, is_causal=True, n_splits=n_splits)
+        cases.append((qd, kd, vd, n_splits, ref))
+    torch.cuda.synchronize()
+    results = [[None] * 10 for _ in cases]
+    errors = []
+
+    def worker(j):
+        try:
+            qd, kd, vd, n_splits, _ = cases[j]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for it in range(10):
+                    results[j][it] = ea.fwd_splitkv(qd, kd, vd, is_causal=True, n_splits=n_splits)
+            s.synchronize()
+        except Exception as exc:  # reported below, in the test's thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=worker, args=(j,)) for j in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (_, _, _, _, (ro, rl)), res in zip(cases, results):
+        for o, l in res:
+            assert torch.equal(o.view(torch.int16), ro.view(torch.int16)) and torch.equal(l, rl)
+
+
 def test_status_error_raises(ea):
     dev = torch.device("cuda", 0)
     q = torch.zeros((1, 4, 16, 96), dtype=torch.bfloat16, device=dev)
