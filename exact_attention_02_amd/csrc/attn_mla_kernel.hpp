@@ -449,12 +449,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64, 64))) void mla_up_kern
   const size_t arow = ((size_t)(rr / p.S) * p.H + h) * p.S + (rr % p.S);
   const uint16_t* a = p.x + arow * kMlaDc + half * 8;
   const uint16_t* w = p.w + ((size_t)h * p.d_n + 32 * vb + col) * kMlaDc + half * 8;
+  // the 32 k-steps in two halves, each half's 32 loads issued before its
+  // MFMAs (about 5 % faster than loads interleaved with the MFMAs)
   f32x16 acc = f32x16{};
-#pragma unroll 8
-  for (int ks = 0; ks < kMlaDc / 16; ++ks) {
-    const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(a + ks * 16));
-    const bf16x8 bv = as_bf16x8(*reinterpret_cast<const u32x4*>(w + ks * 16));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    u32x4 av[16], bv[16];
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      av[ks] = *reinterpret_cast<const u32x4*>(a + (hb * 16 + ks) * 16);
+      bv[ks] = *reinterpret_cast<const u32x4*>(w + (hb * 16 + ks) * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[ks]), as_bf16x8(bv[ks]), acc, 0, 0, 0);
   }
   // element r holds row r0 + 8(r/4) + 4 half + r%4 and v = 32 vb + col
 #pragma unroll
