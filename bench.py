@@ -16,6 +16,8 @@ every row of the timed output against the oracle.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--sweep]
+    python bench.py --backward-sweep | --mla-sweep      (tables to stderr)
+    python bench.py --backward --workload NAME | --mla NAME [--steps K] [--warmup W]
 """
 from __future__ import annotations
 
@@ -301,6 +303,50 @@ def full_parity(w, q64, k64, v64, out, lse):
             "wall_s": round(time.perf_counter() - t0, 1)}
 
 
+def time_mla(ea, torch, name, mw, steps, warmup):
+    """MLA decode (absorbed): the three steps timed together, plus the latent
+    core alone; core FLOPs 2*(2*512+64) per visible (token, head, key).
+    steps/warmup None: time-based counts (auto_counts)."""
+    dev = torch.device("cuda", 0)
+    c_kv, k_pe, q_nope, q_pe, W_uk, W_uv = workloads.make_mla_inputs(mw.B, mw.H, mw.S, mw.T, mw.seed)
+    kv = torch.cat([c_kv, k_pe], -1).contiguous().to(dev)
+    qn, qp, wk, wv = q_nope.to(dev), q_pe.to(dev), W_uk.to(dev), W_uv.to(dev)
+    q_lat = torch.empty((mw.B, mw.H, mw.S, 576), dtype=torch.bfloat16, device=dev)
+    out_lat = torch.empty((mw.B, mw.H, mw.S, 512), dtype=torch.bfloat16, device=dev)
+    lse_m = torch.empty((mw.B, mw.H, mw.S), dtype=torch.float32, device=dev)
+    out_m = torch.empty((mw.B, mw.H, mw.S, mw.d_v), dtype=torch.bfloat16, device=dev)
+    ns = ea.attn_mla_num_splits(mw.B, mw.H, mw.S, mw.T, mw.causal)
+    nb = ea.attn_mla_workspace_size(mw.B, mw.H, mw.S, ns)
+    ws_m = torch.empty((max(nb, 1),), dtype=torch.uint8, device=dev)
+
+    def core():
+        ea.attn_mla_decode(q_lat, kv, out_lat, lse_m, mw.sm_scale, is_causal=mw.causal,
+                           n_splits=ns, workspace=ws_m)
+
+    def full():
+        ea.mla_absorb_q(qn, qp, wk, q_lat)
+        core()
+        ea.mla_up_project(out_lat, wv, out_m)
+    res_t = {}
+    for label, fn in (("core", core), ("full", full)):
+        n_steps, n_warm = auto_counts(torch, fn, steps, warmup)
+        for _ in range(n_warm):
+            fn()
+        ev = []
+        for _ in range(n_steps):
+            s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_.record()
+            fn()
+            e_.record()
+            ev.append((s_, e_))
+        torch.cuda.synchronize()
+        res_t[label] = float(np.median([a.elapsed_time(b_) for a, b_ in ev]))
+    t = res_t["core"]
+    log(f"[mla] {name:22s} splits {ns:3d}  core {t * 1e3:8.1f} us  "
+        f"{mw.core_bytes() / t / 1e6:7.0f} GB/s  {mw.core_flops() / t / 1e9:7.1f} TFLOP/s   "
+        f"absorb+core+up {res_t['full'] * 1e3:8.1f} us")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +361,10 @@ def main():
                     help="time the MLA decode workloads and print a table to stderr, then exit")
     ap.add_argument("--backward-sweep", action="store_true",
                     help="time attn_bwd on the square workloads and print a table to stderr, then exit")
+    ap.add_argument("--backward", action="store_true",
+                    help="time attn_bwd on --workload only (--steps, --warmup), print one line to stderr, exit")
+    ap.add_argument("--mla", default=None, choices=sorted(workloads.MLA_WORKLOADS),
+                    help="time one MLA decode workload (--steps, --warmup), print one line to stderr, exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 512 MiB three times "
                          "(reference for scaling HBM byte counters) and exit")
@@ -342,48 +392,21 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
         return
 
-    if args.mla_sweep:
-        # MLA decode (absorbed): the three steps timed together, plus the
-        # latent core alone; core FLOPs 2*(2*512+64) per visible (token, head, key)
-        dev = torch.device("cuda", 0)
+    if args.mla_sweep or args.mla:
         for name, mw in workloads.MLA_WORKLOADS.items():
-            c_kv, k_pe, q_nope, q_pe, W_uk, W_uv = workloads.make_mla_inputs(mw.B, mw.H, mw.S, mw.T, mw.seed)
-            kv = torch.cat([c_kv, k_pe], -1).contiguous().to(dev)
-            qn, qp, wk, wv = q_nope.to(dev), q_pe.to(dev), W_uk.to(dev), W_uv.to(dev)
-            q_lat = torch.empty((mw.B, mw.H, mw.S, 576), dtype=torch.bfloat16, device=dev)
-            out_lat = torch.empty((mw.B, mw.H, mw.S, 512), dtype=torch.bfloat16, device=dev)
-            lse_m = torch.empty((mw.B, mw.H, mw.S), dtype=torch.float32, device=dev)
-            out_m = torch.empty((mw.B, mw.H, mw.S, mw.d_v), dtype=torch.bfloat16, device=dev)
-            ns = ea.attn_mla_num_splits(mw.B, mw.H, mw.S, mw.T, mw.causal)
-            nb = ea.attn_mla_workspace_size(mw.B, mw.H, mw.S, ns)
-            ws_m = torch.empty((max(nb, 1),), dtype=torch.uint8, device=dev)
+            if args.mla_sweep or name == args.mla:
+                time_mla(ea, torch, name, mw, None if args.mla_sweep else args.steps,
+                         None if args.mla_sweep else args.warmup)
+        return
 
-            def core():
-                ea.attn_mla_decode(q_lat, kv, out_lat, lse_m, mw.sm_scale, is_causal=mw.causal,
-                                   n_splits=ns, workspace=ws_m)
-
-            def full():
-                ea.mla_absorb_q(qn, qp, wk, q_lat)
-                core()
-                ea.mla_up_project(out_lat, wv, out_m)
-            res_t = {}
-            for label, fn in (("core", core), ("full", full)):
-                steps, warmup = auto_counts(torch, fn, None, None)
-                for _ in range(warmup):
-                    fn()
-                ev = []
-                for _ in range(steps):
-                    s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    s_.record()
-                    fn()
-                    e_.record()
-                    ev.append((s_, e_))
-                torch.cuda.synchronize()
-                res_t[label] = float(np.median([a.elapsed_time(b_) for a, b_ in ev]))
-            t = res_t["core"]
-            log(f"[mla] {name:22s} splits {ns:3d}  core {t * 1e3:8.1f} us  "
-                f"{mw.core_bytes() / t / 1e6:7.0f} GB/s  {mw.core_flops() / t / 1e9:7.1f} TFLOP/s   "
-                f"absorb+core+up {res_t['full'] * 1e3:8.1f} us")
+    if args.backward:
+        # one workload's attn_bwd alone (counter runs: --steps 2 --warmup 1)
+        w = workloads.WORKLOADS[args.workload]
+        r = time_backward(ea, torch, w, args.steps, args.warmup)
+        e = float(np.median(r["event_ms"]))
+        log(f"[bwd] {w.name:24s} median {e:9.4f} ms  min {min(r['event_ms']):9.4f} ms  "
+            f"{2.5 * w.flops() / (e * 1e-3) / 1e12:8.1f} TFLOP/s  splits {r['n_splits']}  "
+            f"({len(r['event_ms'])} launches)")
         return
 
     if args.backward_sweep:

@@ -99,7 +99,7 @@ int check_sizes(const Shape& a, int64_t n_splits, float sm_scale, bool* empty) {
 // Row tiles (BP query rows of one head) that key block kb visits.
 int64_t kv_block_tiles(const Shape& a, int64_t kb) {
   const int64_t off = a.causal ? a.N_kv - a.N_q : 0;
-  const int64_t r_start = a.causal ? std::max<int64_t>(0, kb * 32 * kKvNW - off) : 0;
+  const int64_t r_start = a.causal ? std::max<int64_t>(0, kb * 32 * kKvNW - off) / kKvBP * kKvBP : 0;
   return (a.H_q / a.H_kv) * ((a.N_q - r_start + kKvBP - 1) / kKvBP);
 }
 

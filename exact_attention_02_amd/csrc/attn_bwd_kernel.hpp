@@ -15,8 +15,8 @@
 //  * attn_bwd_prep_kernel: Dl = rowsum(dO * O) and L2 = L log2(e) per row.
 //  * attn_bwd_dkdv_kernel: a workgroup owns 32 keys per wave of one kv head;
 //    K and V of those keys stay in registers while the query rows of every
-//    head of the group stream through LDS (head-major, so each tile is
-//    contiguous rows of one head).  When the key blocks alone are too few to
+//    head of the group stream through LDS (each tile is contiguous rows of
+//    one head; row tiles from the last down, the group's heads in turn).  When the key blocks alone are too few to
 //    fill the device (one kv head, short sequences), a key block's sequence
 //    of row tiles is cut into n_kv_splits contiguous ranges, one workgroup
 //    each, writing fp32 partial sums; attn_bwd_kv_reduce_kernel adds them in
@@ -173,8 +173,10 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   const int kw = k0 + 32 * wave;     // first key of this wave
   const int my_key = kw + col;
 
-  // rows before r_start see no key of this block; per head, row tiles of BP
-  const int r_start = p.causal ? max(0, k0 - off) : 0;
+  // rows before r_start see no key of this block; row tiles of BP (r_start
+  // aligned down to a tile, so every key block shares one tile grid; the
+  // rows it adds see none of the block's keys and are masked)
+  const int r_start = p.causal ? max(0, k0 - off) / BP * BP : 0;
   const int n_rt = (N_q - r_start + BP - 1) / BP;
   const int n_tiles = G * n_rt;
   // this workgroup's contiguous range of the G * n_rt (head, row tile) tiles
@@ -205,9 +207,15 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
   const int ld_row_in = lane / C::DC;
   const int ld_chunk = lane % C::DC;
+  // tile t of the sequence: row tiles from the last one down, the G heads of
+  // a row tile in turn.  Workgroups that run at the same time then read the
+  // same Q and dO rows at the same time and the L2 serves all but the first
+  // (walking up from each block's own first row spread them over thousands
+  // of rows: 36 % of the reads went past the L2 at causal N = 32768).
   auto tile_rows = [&](int t, int& hs, int& row0) {
-    hs = t / n_rt;
-    row0 = r_start + (t - hs * n_rt) * BP;
+    const int g = t / G;
+    hs = t - g * G;
+    row0 = r_start + (n_rt - 1 - g) * BP;
   };
   // one tile (Q, dO, and this wave's private copy of L2 and Dl) into stage slot
   auto issue = [&](int t, int slot) {
