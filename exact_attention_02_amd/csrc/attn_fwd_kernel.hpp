@@ -152,7 +152,7 @@ struct Cfg {
   static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
   static constexpr int LDS_BYTES = 2 * P * TILE_BYTES;    // K ring then V ring
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
-  static_assert(QB == 1 || QB == 2, "one or two query blocks per wave");
+  static_assert(QB == 1, "one 32-pair query block per wave (the only shape built and tested)");
   static_assert(BN == 32 || BN == 64, "key tiles of 32 or 64");
   static_assert(LOADS % NW == 0 && LOADS_PER_WAVE >= 1, "tile loads split evenly over waves");
   static_assert(P >= 2 && LDS_BYTES <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
@@ -175,9 +175,10 @@ __device__ __forceinline__ int v_swz(int row) {
   else return 4 * ((row >> 1) & 1);
 }
 
-// QB = 1: waves of 32 (row, head) pairs, two waves per SIMD (256 VGPRs each).
-// QB = 2: 64 pairs per wave, one wave per SIMD (512 registers): each K or V^T
-// fragment read from LDS feeds two MFMAs, halving LDS traffic per FLOP.
+// QB: 32-pair query blocks per wave.  The code is written over QB, but only
+// QB = 1 is built and tested: waves of 32 (row, head) pairs, two waves per
+// SIMD (256 VGPRs each).  Two blocks per wave (one wave per SIMD, each K or
+// V^T fragment feeding two MFMAs) measured slower and is not supported.
 // SPLIT: write the fp32 partial result of one key range instead of the final
 // bf16 output.
 template <int D, int NW, int P, int QB, int BN_, bool SPLIT>
