@@ -27,9 +27,9 @@ using ea02::MergeParams;
 // shape would leave most waves without a query; five (D=128) or eight (D=64,
 // register-bound) fit on a CU, which keeps enough loads in flight for such
 // HBM-bound work.
-constexpr int kWideNW = 8, kWideP = 4, kWideBN = 64;
-constexpr int kMidNW = 4, kMidP = 2, kMidBN = 64;
-constexpr int kNarrowNW = 1, kNarrowP = 2, kNarrowBN = 32;
+constexpr int kWideNW = 8, kWideP = 4, kWideBN = 64, kWideMN = 16;
+constexpr int kMidNW = 4, kMidP = 2, kMidBN = 64, kMidMN = 32;
+constexpr int kNarrowNW = 1, kNarrowP = 2, kNarrowBN = 32, kNarrowMN = 32;
 constexpr int kNarrowPairs = 64;
 constexpr int kMaxSplits = 256;
 
@@ -97,13 +97,13 @@ Shape pick_shape(int64_t n_pairs, int64_t D, int64_t n_heads, int64_t N_q, int64
 template <int D, bool SPLIT>
 hipError_t launch_fwd(Kind kind, const FwdParams& p, int grid, hipStream_t stream) {
   if (kind == Kind::kNarrow)
-    hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kNarrowNW, kNarrowP, 1, kNarrowBN, SPLIT>), dim3(grid),
+    hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kNarrowNW, kNarrowP, 1, kNarrowBN, kNarrowMN, SPLIT>), dim3(grid),
                        dim3(kNarrowNW * 64), 0, stream, p);
   else if (kind == Kind::kMid)
-    hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kMidNW, kMidP, 1, kMidBN, SPLIT>), dim3(grid),
+    hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kMidNW, kMidP, 1, kMidBN, kMidMN, SPLIT>), dim3(grid),
                        dim3(kMidNW * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kWideNW, kWideP, 1, kWideBN, SPLIT>), dim3(grid),
+    hipLaunchKernelGGL((ea02::attn_fwd_kernel<D, kWideNW, kWideP, 1, kWideBN, (SPLIT ? 32 : kWideMN), SPLIT>), dim3(grid),
                        dim3(kWideNW * 64), 0, stream, p);
   return hipGetLastError();
 }

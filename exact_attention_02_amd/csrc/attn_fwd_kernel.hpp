@@ -12,18 +12,27 @@
 //
 // MI355X mapping (not taken from the pages):
 //  * Transposed products.  Each wave computes S^T = K Q^T and O^T = V^T P^T
-//    with v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane
-//    holds one column and 16 rows, so a lane owns ONE query and 16 keys per
-//    32-key block: the row max and row sum are lane-local plus one exchange
-//    between the wave halves (v_permlane32_swap), and the rescale factor is a
-//    lane scalar.  The S^T accumulator rounded to bf16 is directly the B
-//    operand of the PV product.
+//    with bf16 MFMAs, so a lane owns queries (MFMA columns) and a few keys of
+//    each: the row max and row sum are lane-local plus an exchange between
+//    the lanes of one column (v_permlane32_swap, v_permlane16_swap), and the
+//    rescale factor is a lane scalar.  The S^T accumulator rounded to bf16 is
+//    directly the B operand of the PV product.
+//  * MFMA size per launch shape.  The wide single-pass shape uses
+//    v_mfma_f32_16x16x32_bf16 (a lane owns two queries and 4 keys per 16-key
+//    block): on random bf16 data the chip sustains about 12 % more FLOP/s
+//    with it than with the 32x32x16 form (a higher clock under the same power
+//    limit), and long launches are power-bound.  The other shapes use
+//    v_mfma_f32_32x32x16_bf16 (one query, 16 keys per 32-key block): their
+//    short, latency-bound launches run faster with it, and the split variant
+//    of the wide shape does not fit its registers in the 16x16 form.
 //  * Query fragments stay in VGPRs for the whole kernel (B operand of S^T).
 //  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 with the
-//    lds modifier on a buffer resource per kv head, no staging registers),
-//    each 16-byte chunk of a row XOR-swizzled by the row index.  K fragments are 128-bit LDS reads; V^T fragments come from the
-//    LDS transpose read ds_read_b64_tr_b16 on the untransposed V tile, two per
-//    MFMA, in the key order the S^T accumulator layout implies.
+//    lds modifier on a buffer resource per tile, no staging registers, lane
+//    offsets fixed for the whole loop), each 16-byte chunk of a row
+//    XOR-swizzled by the row index.  K fragments are 128-bit LDS reads; V^T
+//    fragments come from the LDS transpose read ds_read_b64_tr_b16 on the
+//    untransposed V tile, two per MFMA, in the key order the S^T accumulator
+//    layout implies.
 //  * A ring of P LDS stages for K and for V: after the barrier that opens tile
 //    t the loads of tile t+P are issued into the stage tile t-1 used, so P-1
 //    tiles are in flight while one is computed; one barrier per tile.
@@ -47,9 +56,10 @@
 //    an fp32 partial result (O normalised by its own l, and log2 l + m) that
 //    the merge kernel combines through the log-sum-exps (page "Attention
 //    Kernel 实现与正确性验证", section 2.4, split-T with a safe-softmax merge).
-//  * Pairs and keys past the ends are clamped to the last valid one on load
-//    (their scores are masked, their outputs not stored), so loads need no
-//    bounds branches.
+//  * Pairs past the end are clamped to the last valid one on load (their
+//    outputs are not stored).  Each K/V tile is read through a buffer
+//    resource that ends at the head's last key, so key rows past N_kv come
+//    back as zeros; their scores are masked.  Loads need no bounds branches.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -104,16 +114,49 @@ constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 for gfx9
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// v_permlane32_swap exchanges lanes 32..63 of the first operand with lanes
-// 0..31 of the second; with both operands x, the two results hold x of this
-// lane and of lane l^32.
-__device__ __forceinline__ float half_swap_max(float x) {
+// Reductions over the lanes that hold one MFMA column (lanes l, l^32 for
+// MN = 32; l, l^16, l^32, l^48 for MN = 16).  v_permlane32_swap exchanges
+// lanes 32..63 of its first operand with lanes 0..31 of its second,
+// v_permlane16_swap the odd 16-lane rows of the first with the even rows of
+// the second; with both operands x, the two results hold x of this lane and
+// of its partner.
+template <int MN>
+__device__ __forceinline__ float col_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  if constexpr (MN == 16) {
+    auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+  }
+  return x;
 }
-__device__ __forceinline__ float half_swap_sum(float x) {
+template <int MN>
+__device__ __forceinline__ float col_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  if constexpr (MN == 16) {
+    auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  }
+  return x;
+}
+
+// bf16 MFMA of size MN x MN x (512 / MN) with fp32 accumulators: one lane
+// holds MN * MN / 64 of them.
+template <int MN>
+struct MfmaAcc;
+template <>
+struct MfmaAcc<32> {
+  using type = f32x16;
+};
+template <>
+struct MfmaAcc<16> {
+  using type = f32x4;
+};
+template <int MN>
+__device__ __forceinline__ typename MfmaAcc<MN>::type mfma_bf16(bf16x8 a, bf16x8 b, typename MfmaAcc<MN>::type c) {
+  if constexpr (MN == 32) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Raw buffer resource: 48-bit base, no stride, num_records bytes.
@@ -159,42 +202,64 @@ struct Cfg {
   static_assert((P - 1) * 2 * LOADS_PER_WAVE <= 63, "loads in flight fit the 6-bit vmcnt");
 };
 
-// 16-byte chunk swizzles.  K: the 16 (D=128) or 8 (D=64) chunks of a row are
-// permuted so that the 16 keys read together by 16 lanes at one chunk index
-// hit 16 different bank groups.  V: chosen so that a transpose read (4 rows x
-// 4 chunks per 16 lanes, two such groups per half wave) spreads 8 rows over
-// all banks.
+// 16-byte chunk swizzles of K and V rows in LDS: stored chunk j of row r
+// holds chunk j ^ swz(r), so that the MFMA operand reads hit every bank
+// group.  K reads: 16 lanes read 16 consecutive keys at one chunk index, so
+// swz is a bijection on r mod 16 (within each row parity for D = 64, whose
+// rows are half the 64 banks).  V transpose reads: a half wave reads 4 rows x
+// 4 adjacent chunks (MN = 32) or 8 rows x 2 adjacent chunks (MN = 16) of
+// aligned rows.  For MN = 16 one swizzle serves both (its bits 1.. take 8
+// values over 8 aligned rows), so a K load and a V load share an offset.
 template <int D>
+__device__ __forceinline__ int kv16_swz(int row) {
+  if constexpr (D == 128) return 2 * (row & 7) + ((row >> 3) & 1);
+  else return 2 * ((row >> 1) & 3) + ((row >> 3) & 1);
+}
+template <int D, int MN>
 __device__ __forceinline__ int k_swz(int row) {
-  if constexpr (D == 128) return row & 15;
+  if constexpr (MN == 16) return kv16_swz<D>(row);
+  else if constexpr (D == 128) return row & 15;
   else return (row >> 1) & 7;
 }
-template <int D>
+template <int D, int MN>
 __device__ __forceinline__ int v_swz(int row) {
-  if constexpr (D == 128) return 4 * (row & 3);
+  if constexpr (MN == 16) return kv16_swz<D>(row);
+  else if constexpr (D == 128) return 4 * (row & 3);
   else return 4 * ((row >> 1) & 1);
 }
 
-// QB: 32-pair query blocks per wave.  The code is written over QB, but only
-// QB = 1 is built and tested: waves of 32 (row, head) pairs, two waves per
-// SIMD (256 VGPRs each).  Two blocks per wave (one wave per SIMD, each K or
-// V^T fragment feeding two MFMAs) measured slower and is not supported.
+// QB: 32-pair query blocks per wave.  Only QB = 1 is built and tested: waves
+// of 32 (row, head) pairs, two waves per SIMD (256 registers each).  Two
+// blocks per wave (one wave per SIMD, each K or V^T fragment feeding twice
+// the MFMAs) measured slower.
+// MN: MFMA size, 32 (v_mfma_f32_32x32x16_bf16: one 32-query column block per
+// wave) or 16 (v_mfma_f32_16x16x32_bf16: two 16-query column blocks).
 // SPLIT: write the fp32 partial result of one key range instead of the final
 // bf16 output.
-template <int D, int NW, int P, int QB, int BN_, bool SPLIT>
+template <int D, int NW, int P, int QB, int BN_, int MN, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void attn_fwd_kernel(FwdParams p) {
   using C = Cfg<D, NW, P, QB, BN_>;
   constexpr int BN = C::BN;
+  constexpr int KK = 512 / MN;        // contraction length of one MFMA
+  constexpr int ACC = MN * MN / 64;   // accumulator registers per lane and MFMA block
+  constexpr int QC = C::QW / MN;      // query column blocks per wave
+  constexpr int KB = BN / MN;         // key row blocks of S^T per tile
+  using AccT = typename MfmaAcc<MN>::type;
+  static_assert(MN == 16 || MN == 32, "MFMA 16x16x32 or 32x32x16");
   constexpr int PPW = C::QW * C::NW;  // (row, head) pairs per workgroup
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = lane >> 5;
-  const int col = lane & 31;
+  // MFMA operand and result layout: lane = MN kgrp + col.  An operand lane
+  // holds row (A) or column (B) `col` and contraction slots 8 kgrp .. 8 kgrp
+  // + 7; a result lane holds column `col` and rows (r / 4) (256 / MN) + 4 kgrp
+  // + r % 4 for its accumulator registers r.
+  const int kgrp = lane / MN;
+  const int col = lane % MN;
 
   // ---- work decomposition: heaviest pair blocks first (causal), then the
   //      key splits, kv heads fastest
@@ -227,166 +292,176 @@ void attn_fwd_kernel(FwdParams p) {
   }
 
   const size_t kv_base = ((size_t)b * p.H_kv + g) * (size_t)N_kv * D;
-  // K and V of this kv head as buffer resources (base in SGPRs, 32-bit offsets)
-  const uint32_t head_bytes = (uint32_t)N_kv * C::ROW_BYTES;
-  const u32x4 k_rsrc = make_rsrc(p.k + kv_base, head_bytes);
-  const u32x4 v_rsrc = make_rsrc(p.v + kv_base, head_bytes);
 
-  // ---- query fragments (B operands of S^T = K Q^T): in query block qb the
-  //      lane holds pair wp0 + 32 qb + col = (row, head g*G + j), d = 16*ks +
-  //      8*half .. +8.  Pairs past the end are clamped to the last one.
-  // (b * H_q + h) * N_q + row of query block qb's pair (recomputed where
+  // ---- query fragments (B operands of S^T = K Q^T): in column block qc the
+  //      lane holds pair wp0 + MN qc + col = (row, head g*G + j), d = KK*ks +
+  //      8*kgrp .. +8.  Pairs past the end are clamped to the last one.
+  // (b * H_q + h) * N_q + row of column block qc's pair (recomputed where
   // needed rather than kept live through the tile loop)
-  auto bhr_of = [&](int qb) {
-    const int pc = min(wp0 + 32 * qb + col, last_pair);
+  auto bhr_of = [&](int qc) {
+    const int pc = min(wp0 + MN * qc + col, last_pair);
     const int row = pc / G;
     const int h = g * G + (pc - row * G);
     return ((size_t)b * p.H_q + h) * (size_t)p.N_q + row;
   };
-  int my_row[QB];
-  bf16x8 qf[QB][D / 16];
+  // query row of column block qc's pair (recomputed on the masked tiles
+  // only: a register held across the tile loop costs more)
+  auto row_of = [&](int qc) { return min(wp0 + MN * qc + col, last_pair) / G; };
+  bf16x8 qf[QC][D / KK];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    my_row[qb] = min(wp0 + 32 * qb + col, last_pair) / G;
-    const size_t bhr = bhr_of(qb);
+  for (int qc = 0; qc < QC; ++qc) {
+    const size_t bhr = bhr_of(qc);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(p.q + bhr * D + ks * 16 + half * 8);
+    for (int ks = 0; ks < D / KK; ++ks) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(p.q + bhr * D + ks * KK + kgrp * 8);
       x ^= p.q_sign;
-      qf[qb][ks] = as_bf16x8(x);
+      qf[qc][ks] = as_bf16x8(x);
     }
   }
 
   // ---- direct HBM -> LDS tile loads.  Load instruction i of a tile fills
   //      bytes [1024 i, 1024 i + 1024): lane -> (row, stored chunk j), and it
   //      fetches global chunk j ^ swz(row).  LDS holds a ring of P K tiles
-  //      then a ring of P V tiles.
+  //      then a ring of P V tiles.  Each tile is read through a buffer
+  //      resource that starts at the tile's first key and ends at the last
+  //      key of the head, so the lane offsets are loop constants and rows
+  //      past the last key come back as zeros (their scores are masked).
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
-  const int ld_row_in = lane / C::DC;
-  const int ld_chunk = lane % C::DC;
-  // one tile of K (ring 0) or V (ring 1) into ring slot `slot`; tile numbers
-  // count from the split's first key; keys past the end are clamped to the last
-  auto issue_tile = [&](int tile, int slot, const u32x4& rsrc, int ring) {
+  int ld_off_k[C::LOADS_PER_WAVE], ld_off_v[C::LOADS_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
-      const int li = wave * C::LOADS_PER_WAVE + i;
-      const int r = li * C::ROWS_PER_LOAD + ld_row_in;
-      const int swz = ring == 0 ? k_swz<D>(r) : v_swz<D>(r);
-      const int byte = min(kbase + tile * BN + r, N_kv - 1) * C::ROW_BYTES + ((ld_chunk ^ swz) << 4);
-      dma_16B(rsrc, byte, lds_base + (ring * P + slot) * C::TILE_BYTES + li * 1024);
-    }
+  for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+    const int r = (wave * C::LOADS_PER_WAVE + i) * C::ROWS_PER_LOAD + lane / C::DC;
+    ld_off_k[i] = r * C::ROW_BYTES + (((lane % C::DC) ^ k_swz<D, MN>(r)) << 4);
+    ld_off_v[i] = r * C::ROW_BYTES + (((lane % C::DC) ^ v_swz<D, MN>(r)) << 4);
+  }
+  const uint16_t* k_head = p.k + kv_base;
+  const uint16_t* v_head = p.v + kv_base;
+  // one tile of K (ring 0) or V (ring 1) into ring slot `slot`; tile numbers
+  // count from the split's first key
+  auto issue_tile = [&](int tile, int slot, const uint16_t* head, int ring) {
+    const int row0 = kbase + tile * BN;
+    const u32x4 rsrc = make_rsrc(head + (size_t)row0 * D, (uint32_t)(N_kv - row0) * C::ROW_BYTES);
+#pragma unroll
+    for (int i = 0; i < C::LOADS_PER_WAVE; ++i)
+      dma_16B(rsrc, ring == 0 ? ld_off_k[i] : ld_off_v[i], lds_base + (ring * P + slot) * C::TILE_BYTES + (wave * C::LOADS_PER_WAVE + i) * 1024);
   };
 
   // per-lane LDS byte offsets of the MFMA operand reads (tile-relative)
-  // K (A operand of S^T): key c*32+col, chunk 2ks+half (swizzled)
-  // V^T (A operand of O^T, transpose read): 16-lane group G = lane>>4, L = lane&15
-  //   reads rows k0 + L/4 (k0 = 16 s + 4 half + 8 part), d = db*32 + 16(G&1) + 4(L&3)
+  // K (A operand of S^T, MN keys x KK d): key MN c + col, chunk (KK/8) ks + kgrp.
+  // V^T (A operand of O^T, MN d x KK keys): lane row d = MN db + col; its
+  //   contraction slots are the keys KK st + 4 kgrp + {0..3} (first transpose
+  //   read) and KK st + KK/2 + 4 kgrp + {0..3} (second): in the S^T
+  //   accumulator layout exactly the keys whose scores this lane holds in
+  //   the 8 consecutive accumulator registers that form P's B operand of
+  //   step st.  Each transpose read: lane L of a 16-lane group addresses row
+  //   4 kgrp + L/4 (+ KK st, + KK/2), d = d16 + 4 (L & 3) .. +4, and receives
+  //   d = d16 + L of the group's four rows (d16: the group's 16 d).
   const int L = lane & 15;
-  const int vt_row = 4 * half + (L >> 2);
-  int vt_off[D / 32];
+  const int vt_row = 4 * kgrp + (L >> 2);
+  int vt_off[D / MN];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    const int d = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
-    const int chunk = (d >> 3) ^ v_swz<D>(vt_row);
+  for (int db = 0; db < D / MN; ++db) {
+    const int d = db * MN + 16 * ((lane >> 4) % (MN / 16)) + 4 * (L & 3);
+    const int chunk = (d >> 3) ^ v_swz<D, MN>(vt_row);
     vt_off[db] = vt_row * C::ROW_BYTES + chunk * 16 + (d & 7) * 2;
   }
   auto k_read = [&](int tile, int i) {
     const uint8_t* kb = lds + (tile % P) * C::TILE_BYTES;
-    const int c = i % (BN / 32), ks = i / (BN / 32);  // consecutive reads alternate key blocks
-    const int key = c * 32 + col;
+    const int c = i % KB, ks = i / KB;  // consecutive reads alternate key blocks
+    const int key = c * MN + col;
     return *reinterpret_cast<const u32x4*>(kb + key * C::ROW_BYTES +
-                                           (((2 * ks + half) ^ k_swz<D>(key)) << 4));
+                                           ((((KK / 8) * ks + kgrp) ^ k_swz<D, MN>(key)) << 4));
   };
   auto v_read = [&](int tile, int i) {
     const uint8_t* vb = lds + (P + tile % P) * C::TILE_BYTES;
-    const int st = i / (D / 32), db = i % (D / 32);
-    const uint8_t* a0 = vb + vt_off[db] + (16 * st) * C::ROW_BYTES;
+    const int st = i / (D / MN), db = i % (D / MN);
+    const uint8_t* a0 = vb + vt_off[db] + (KK * st) * C::ROW_BYTES;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + 8 * C::ROW_BYTES));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0 + (KK / 2) * C::ROW_BYTES));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  constexpr int NS = (BN / 32) * (D / 16);  // K fragment reads per tile (each feeds QB MFMAs)
-  constexpr int NP = (BN / 16) * (D / 32);  // V^T fragment reads per tile (each feeds QB MFMAs)
-  constexpr int NV = BN / 2;                // scores per lane per query block per tile
-  constexpr int EPR = QB * NV / NS;         // exponentials per K fragment read
-  constexpr int MPR = QB * NV / NP;         // max operations per V^T fragment read
-  static_assert(EPR * NS == QB * NV && MPR * NP == QB * NV, "score work splits evenly");
-  constexpr int PF = QB == 1 ? 2 : 3;       // LDS operand prefetch distance
+  constexpr int NS = KB * (D / KK);         // K fragment reads per tile (each feeds QC MFMAs)
+  constexpr int NP = (BN / KK) * (D / MN);  // V^T fragment reads per tile (each feeds QC MFMAs)
+  constexpr int NV = KB * ACC;              // scores per lane per column block per tile
+  constexpr int EPR = QC * NV / NS;         // exponentials per K fragment read
+  static_assert(EPR * NS == QC * NV, "score work splits evenly");
+  constexpr int PF = 2;                     // LDS operand prefetch distance
 
-  // ---- running state: per query block, one query per lane
-  float m_used[QB], l_run[QB];
-  f32x16 acc[D / 32][QB];
+  // ---- running state: per column block, one query per lane
+  float m_used[QC], l_run[QC];
+  AccT acc[D / MN][QC];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_used[qb] = -INFINITY;  // max used in the exponent (log2-scaled units)
-    l_run[qb] = 0.f;         // this lane's partial sum of P over its keys
+  for (int qc = 0; qc < QC; ++qc) {
+    m_used[qc] = -INFINITY;  // max used in the exponent (log2-scaled units)
+    l_run[qc] = 0.f;         // this lane's partial sum of P over its keys
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) acc[i][qb] = f32x16{};
+    for (int i = 0; i < D / MN; ++i) acc[i][qc] = AccT{};
   }
   const float sl2 = p.scale_log2;
 
-  using Scores = f32x16[BN / 32][QB];
+  using Scores = AccT[KB][QC];
   // S^T = K Q^T of one tile with no other work interleaved (prologue only)
   auto s_tile = [&](int tile, Scores& s) {
 #pragma unroll
-    for (int c = 0; c < BN / 32; ++c)
+    for (int c = 0; c < KB; ++c)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[c][qb] = f32x16{};
+      for (int qc = 0; qc < QC; ++qc) s[c][qc] = AccT{};
     u32x4 kx[PF + 1];
 #pragma unroll
     for (int i = 0; i < PF; ++i) kx[i] = k_read(tile, i);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (i + PF < NS) kx[(i + PF) % (PF + 1)] = k_read(tile, i + PF);
-      const int c = i % (BN / 32), ks = i / (BN / 32);
+      const int c = i % KB, ks = i / KB;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        s[c][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx[i % (PF + 1)]), qf[qb][ks], s[c][qb], 0, 0, 0);
+      for (int qc = 0; qc < QC; ++qc)
+        s[c][qc] = mfma_bf16<MN>(as_bf16x8(kx[i % (PF + 1)]), qf[qc][ks], s[c][qc]);
     }
   };
-  // diagonal or ragged tile: element (c, r) holds key kbase + tile*BN +
-  // 4 half + [c*32 + 8(r/4) + r%4]; it is visible when the bracket is below
-  // lim.  Rows grow with the pair index, so the wave's first row decides.
+  // diagonal or ragged tile: element (c, qc, r) holds key kbase + tile*BN +
+  // MN c + (r/4)(256/MN) + 4 kgrp + r%4 of column block qc's query; it is
+  // visible when that offset minus 4 kgrp is below lim.  Rows grow with the
+  // pair index, so the wave's first row decides.
   auto needs_mask = [&](int tile) {
     const int key0 = kbase + tile * BN;
     return (p.causal && key0 + BN - 1 > wave_row0 + off) || key0 + BN > N_kv;
   };
   auto apply_mask = [&](int tile, Scores& s) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int lim = (p.causal ? min(my_row[qb] + off + 1, N_kv) : N_kv) - kbase - tile * BN - 4 * half;
+    for (int qc = 0; qc < QC; ++qc) {
+      const int lim = (p.causal ? min(row_of(qc) + off + 1, N_kv) : N_kv) - kbase - tile * BN - 4 * kgrp;
 #pragma unroll
-      for (int c = 0; c < BN / 32; ++c)
+      for (int c = 0; c < KB; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[c][qb][r] = (c * 32 + 8 * (r >> 2) + (r & 3) < lim) ? s[c][qb][r] : -INFINITY;
+        for (int r = 0; r < ACC; ++r)
+          s[c][qc][r] = (c * MN + (r >> 2) * (256 / MN) + (r & 3) < lim) ? s[c][qc][r] : -INFINITY;
     }
   };
   // raise the exponent's max when the tile max exceeds it by more than the
   // slack (wave-uniform branch; rare after the first tile)
   auto update_max = [&](const float* mx_lane) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mt = half_swap_max(mx_lane[qb]) * sl2;  // sl2 > 0: a masked row stays -inf
-      if (__builtin_amdgcn_ballot_w64(mt > m_used[qb] + kRescaleSlack)) {
-        const float m_new = fmaxf(m_used[qb], mt);
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used[qb] - m_new);
-        l_run[qb] *= alpha;
+    for (int qc = 0; qc < QC; ++qc) {
+      const float mt = col_max<MN>(mx_lane[qc]) * sl2;  // sl2 > 0: a masked row stays -inf
+      if (__builtin_amdgcn_ballot_w64(mt > m_used[qc] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_used[qc], mt);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used[qc] - m_new);
+        l_run[qc] *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db][qb] *= alpha;
-        m_used[qb] = m_new;
+        for (int db = 0; db < D / MN; ++db) acc[db][qc] *= alpha;
+        m_used[qc] = m_new;
       }
     }
   };
   auto lane_max = [&](const Scores& s, float* mx) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float m = s[0][qb][0];
+    for (int qc = 0; qc < QC; ++qc) {
+      float m = s[0][qc][0];
 #pragma unroll
-      for (int c = 0; c < BN / 32; ++c)
+      for (int c = 0; c < KB; ++c)
 #pragma unroll
-        for (int r = (c == 0 ? 1 : 0); r < 16; ++r) m = fmaxf(m, s[c][qb][r]);
-      mx[qb] = m;
+        for (int r = (c == 0 ? 1 : 0); r < ACC; ++r) m = fmaxf(m, s[c][qc][r]);
+      mx[qc] = m;
     }
   };
 
@@ -394,48 +469,50 @@ void attn_fwd_kernel(FwdParams p) {
   // applied), in two phases: P(t) = 2^(S(t) sl2 - m) interleaved with
   // S(t+1) = K(t+1) Q^T into sn (when HAS_NEXT), then O += V(t) P(t).  P(t)
   // passes between them in pbf, declared outside both (fewer registers live
-  // across the step than a local of one lambda).
-  bf16x8 pbf[QB][BN / 16];
+  // across the step than a local of one lambda).  pbf[qc][st] is the B
+  // operand of the KK keys of step st: accumulator registers 8 st .. 8 st + 7
+  // of the lane's scores in key-block-major order.
+  bf16x8 pbf[QC][BN / KK];
   auto phase_x = [&](int t, Scores& sc, Scores& sn, auto has_next_tag) {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
-    float m_sub[QB], l_t[QB];
+    float m_sub[QC], l_t[QC];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      m_sub[qb] = (m_used[qb] == -INFINITY) ? 0.f : m_used[qb];
-      l_t[qb] = 0.f;
+    for (int qc = 0; qc < QC; ++qc) {
+      m_sub[qc] = (m_used[qc] == -INFINITY) ? 0.f : m_used[qc];
+      l_t[qc] = 0.f;
     }
-    f32x8 pf[QB];
-    // exponential number j of this tile: query block j / NV, element j % NV,
-    // taken against the max in use (no max of this tile is computed here)
+    f32x8 pf[QC];
+    // exponential number j of this tile: column block j / NV, element e =
+    // j % NV (key block e / ACC, register e % ACC), taken against the max in
+    // use (no max of this tile is computed here)
     auto p_elem = [&](int j) {
-      const int qb = j / NV, e = j % NV;
-      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 4][qb][e & 15], sl2, -m_sub[qb]));
-      pf[qb][e & 7] = pe;
-      l_t[qb] += pe;
-      if ((e & 7) == 7) pbf[qb][e >> 3] = __builtin_convertvector(pf[qb], bf16x8);
+      const int qc = j / NV, e = j % NV;
+      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e / ACC][qc][e % ACC], sl2, -m_sub[qc]));
+      pf[qc][e & 7] = pe;
+      l_t[qc] += pe;
+      if ((e & 7) == 7) pbf[qc][e >> 3] = __builtin_convertvector(pf[qc], bf16x8);
     };
     if constexpr (HAS_NEXT) {
 #pragma unroll
-      for (int c = 0; c < BN / 32; ++c)
+      for (int c = 0; c < KB; ++c)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sn[c][qb] = f32x16{};
+        for (int qc = 0; qc < QC; ++qc) sn[c][qc] = AccT{};
       u32x4 kx[PF + 1];
 #pragma unroll
       for (int i = 0; i < PF; ++i) kx[i] = k_read(t + 1, i);
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         if (i + PF < NS) kx[(i + PF) % (PF + 1)] = k_read(t + 1, i + PF);
-        const int c = i % (BN / 32), ks = i / (BN / 32);
+        const int c = i % KB, ks = i / KB;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sn[c][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kx[i % (PF + 1)]), qf[qb][ks],
-                                                              sn[c][qb], 0, 0, 0);
+        for (int qc = 0; qc < QC; ++qc)
+          sn[c][qc] = mfma_bf16<MN>(as_bf16x8(kx[i % (PF + 1)]), qf[qc][ks], sn[c][qc]);
 #pragma unroll
         for (int e = 0; e < EPR; ++e) p_elem(i * EPR + e);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < QB * NV; ++j) p_elem(j);
+      for (int j = 0; j < QC * NV; ++j) p_elem(j);
     }
     // A tile sum above 2^24 means some score exceeds the max in use by more
     // than 24 (log2 units), or overflowed: take this tile's true max, rescale
@@ -443,44 +520,44 @@ void attn_fwd_kernel(FwdParams p) {
     // sets the max, and scores rarely climb that far above it).
     bool big = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) big |= !(l_t[qb] <= kOverflowSum);
+    for (int qc = 0; qc < QC; ++qc) big |= !(l_t[qc] <= kOverflowSum);
     if (__builtin_amdgcn_ballot_w64(big)) {
-      float mx[QB];
+      float mx[QC];
       lane_max(sc, mx);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float mt = half_swap_max(mx[qb]) * sl2;
-        const float m_new = fmaxf(m_used[qb], mt);
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used[qb] - m_new);
-        l_run[qb] *= alpha;
+      for (int qc = 0; qc < QC; ++qc) {
+        const float mt = col_max<MN>(mx[qc]) * sl2;
+        const float m_new = fmaxf(m_used[qc], mt);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used[qc] - m_new);
+        l_run[qc] *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db][qb] *= alpha;
-        m_used[qb] = m_new;
-        m_sub[qb] = (m_new == -INFINITY) ? 0.f : m_new;
-        l_t[qb] = 0.f;
+        for (int db = 0; db < D / MN; ++db) acc[db][qc] *= alpha;
+        m_used[qc] = m_new;
+        m_sub[qc] = (m_new == -INFINITY) ? 0.f : m_new;
+        l_t[qc] = 0.f;
       }
 #pragma unroll
-      for (int j = 0; j < QB * NV; ++j) p_elem(j);
+      for (int j = 0; j < QC * NV; ++j) p_elem(j);
     }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l_run[qb] += l_t[qb];
+    for (int qc = 0; qc < QC; ++qc) l_run[qc] += l_t[qc];
     // a diagonal or ragged next tile is masked before its exponentials
     if constexpr (HAS_NEXT) {
       if (needs_mask(t + 1)) apply_mask(t + 1, sn);
     }
   };
   auto phase_y = [&](int t) {
-    // O^T += V^T P^T; k-step st covers keys 16 st .. 16 st + 15
+    // O^T += V^T P^T; step st covers keys KK st .. KK st + KK - 1
     bf16x8 vx[PF + 1];
 #pragma unroll
     for (int i = 0; i < PF; ++i) vx[i] = v_read(t, i);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       if (i + PF < NP) vx[(i + PF) % (PF + 1)] = v_read(t, i + PF);
-      const int st = i / (D / 32), db = i % (D / 32);
+      const int st = i / (D / MN), db = i % (D / MN);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx[i % (PF + 1)], pbf[qb][st], acc[db][qb], 0, 0, 0);
+      for (int qc = 0; qc < QC; ++qc)
+        acc[db][qc] = mfma_bf16<MN>(vx[i % (PF + 1)], pbf[qc][st], acc[db][qc]);
     }
   };
   auto step = [&](int t, Scores& sc, Scores& sn, auto has_next_tag) {
@@ -496,8 +573,8 @@ void attn_fwd_kernel(FwdParams p) {
   // clamped, valid tile into its (free) slots, so every group is the same
   // number of loads and each wait below is one constant vmcnt.
   auto issue_group = [&](int j) {
-    issue_tile(min(j, n_tiles - 1), j % P, k_rsrc, 0);
-    issue_tile(max(min(j - 1, n_tiles - 1), 0), (j + P - 1) % P, v_rsrc, 1);
+    issue_tile(min(j, n_tiles - 1), j % P, k_head, 0);
+    issue_tile(max(min(j - 1, n_tiles - 1), 0), (j + P - 1) % P, v_head, 1);
   };
   constexpr int GROUP_LOADS = 2 * C::LOADS_PER_WAVE;
   auto sync_prologue = [&]() {
@@ -517,7 +594,7 @@ void attn_fwd_kernel(FwdParams p) {
     s_tile(0, sa);
     if (needs_mask(0)) apply_mask(0, sa);
     {
-      float mx[QB];
+      float mx[QC];
       lane_max(sa, mx);
       update_max(mx);
     }
@@ -549,41 +626,41 @@ void attn_fwd_kernel(FwdParams p) {
   // ---- epilogue.  Single pass: O = acc / l (bf16, round to nearest even),
   //      LSE in natural log.  Split pass: fp32 O = acc / l and log2-unit
   //      m + log2 l of this key range; a range with no visible key (l = 0)
-  //      gives O = 0 and -inf, the neutral element of the merge.
+  //      gives O = 0 and -inf, the neutral element of the merge.  A lane
+  //      holds d = MN db + g4 (256/MN) + 4 kgrp .. +4 of its query in
+  //      registers 4 g4 .. 4 g4 + 3 of acc[db].
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = half_swap_sum(l_run[qb]);
-    if (wp0 + 32 * qb + col > last_pair) continue;
-    const size_t bhr = bhr_of(qb);
+  for (int qc = 0; qc < QC; ++qc) {
+    const float l_tot = col_sum<MN>(l_run[qc]);
+    if (wp0 + MN * qc + col > last_pair) continue;
+    const size_t bhr = bhr_of(qc);
     if constexpr (!SPLIT) {
       const float inv = 1.f / l_tot;
       uint16_t* orow = p.o + bhr * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / MN; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = db * 32 + 8 * g4 + 4 * half;
-          f32x4 f = {acc[db][qb][4 * g4 + 0] * inv, acc[db][qb][4 * g4 + 1] * inv,
-                     acc[db][qb][4 * g4 + 2] * inv, acc[db][qb][4 * g4 + 3] * inv};
+        for (int g4 = 0; g4 < ACC / 4; ++g4) {
+          const f32x4 f = {acc[db][qc][4 * g4 + 0] * inv, acc[db][qc][4 * g4 + 1] * inv,
+                           acc[db][qc][4 * g4 + 2] * inv, acc[db][qc][4 * g4 + 3] * inv};
           const bf16x4 bv = __builtin_convertvector(f, bf16x4);
-          *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, bv);
+          *reinterpret_cast<u32x2*>(orow + db * MN + g4 * (256 / MN) + 4 * kgrp) = __builtin_bit_cast(u32x2, bv);
         }
-      if (half == 0) p.lse[bhr] = (m_used[qb] + __log2f(l_tot)) * kLn2;
+      if (kgrp == 0) p.lse[bhr] = (m_used[qc] + __log2f(l_tot)) * kLn2;
     } else {
       const bool seen = l_tot > 0.f;
       const float inv = seen ? 1.f / l_tot : 0.f;
       const size_t slot = (size_t)split * ((size_t)p.B * p.H_q * p.N_q) + bhr;
       float* orow = p.o_part + slot * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / MN; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = db * 32 + 8 * g4 + 4 * half;
-          f32x4 f = {acc[db][qb][4 * g4 + 0] * inv, acc[db][qb][4 * g4 + 1] * inv,
-                     acc[db][qb][4 * g4 + 2] * inv, acc[db][qb][4 * g4 + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + d0) = f;
+        for (int g4 = 0; g4 < ACC / 4; ++g4) {
+          const f32x4 f = {acc[db][qc][4 * g4 + 0] * inv, acc[db][qc][4 * g4 + 1] * inv,
+                           acc[db][qc][4 * g4 + 2] * inv, acc[db][qc][4 * g4 + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + db * MN + g4 * (256 / MN) + 4 * kgrp) = f;
         }
-      if (half == 0) p.lse_part[slot] = seen ? m_used[qb] + __log2f(l_tot) : -INFINITY;
+      if (kgrp == 0) p.lse_part[slot] = seen ? m_used[qc] + __log2f(l_tot) : -INFINITY;
     }
   }
 }

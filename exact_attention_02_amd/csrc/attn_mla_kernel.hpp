@@ -220,7 +220,7 @@ void attn_mla_kernel(MlaParams p) {
     float mx = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    const float mt = half_swap_max(mx) * sl2;
+    const float mt = col_max<32>(mx) * sl2;
     if (__builtin_amdgcn_ballot_w64(mt > m_used + kRescaleSlack)) {
       const float m_new = fmaxf(m_used, mt);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used - m_new);
@@ -264,7 +264,7 @@ void attn_mla_kernel(MlaParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
-  const float l_tot = half_swap_sum(l_run);
+  const float l_tot = col_sum<32>(l_run);
   if (!valid) return;
   const int dbase = kh * (kMlaDc / 2);
   if constexpr (!SPLIT) {
