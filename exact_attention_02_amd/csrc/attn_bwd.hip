@@ -223,9 +223,9 @@ hipError_t launch_all(const BwdParams& p, int q_nw, hipStream_t s) {
   if (p.rows > 0) {
     const dim3 grid(static_cast<unsigned>(p.n_heads_wg * p.n_pair_blocks * p.n_q_splits));
     if (q_nw == kQMidNW)
-      hipLaunchKernelGGL((ea02::attn_bwd_dq_kernel<D, kQMidNW, kQMidP, kQBN>), grid, dim3(kQMidNW * 64), 0, s, p);
+      hipLaunchKernelGGL((ea02::attn_bwd_dq_kernel<D, kQMidNW, kQMidP, kQBN, 32>), grid, dim3(kQMidNW * 64), 0, s, p);
     else
-      hipLaunchKernelGGL((ea02::attn_bwd_dq_kernel<D, kQNW, kQP, kQBN>), grid, dim3(kQNW * 64), 0, s, p);
+      hipLaunchKernelGGL((ea02::attn_bwd_dq_kernel<D, kQNW, kQP, kQBN, 16>), grid, dim3(kQNW * 64), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.n_q_splits > 1) {
       const int64_t quads = p.rows * D / 4;

@@ -437,19 +437,35 @@ struct BwdQCfg {
 // waves with two stages leave room for a second workgroup on the CU; one
 // wave's exponentials and dS run while the other's MFMAs issue (the register
 // budget, 256 per wave, still holds the 32-pair accumulators without spilling).
-template <int D, int NW, int P, int BN>
+// MN: MFMA size as in the forward, 16 (v_mfma_f32_16x16x32_bf16: a lane owns
+// two pairs, the long power-bound launches) or 32 (v_mfma_f32_32x32x16_bf16).
+// K and V rows use the forward's swizzle for MN = 16 (its 16x16 transpose
+// reads cover 8 rows x 2 chunks) and bwd_swz for MN = 32.
+template <int D, int MN>
+__device__ __forceinline__ int dq_swz(int row) {
+  if constexpr (MN == 16) return kv16_swz<D>(row);
+  else return bwd_swz<D>(row);
+}
+template <int D, int NW, int P, int BN, int MN>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu((NW >= 8 || P <= 2) ? 2 : 1, (NW >= 8 || P <= 2) ? 2 : 1)))
 void attn_bwd_dq_kernel(BwdParams p) {
   using C = BwdQCfg<D, NW, P, BN>;
-  constexpr int PPW = 32 * NW;  // (row, head) pairs per workgroup
+  constexpr int PPW = 32 * NW;        // (row, head) pairs per workgroup
+  constexpr int KK = 512 / MN;        // contraction length of one MFMA
+  constexpr int ACC = MN * MN / 64;   // accumulator registers per lane and MFMA block
+  constexpr int QC = 32 / MN;         // pair column blocks per wave
+  using AccT = typename MfmaAcc<MN>::type;
+  static_assert(MN == 16 || MN == 32, "MFMA 16x16x32 or 32x32x16");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = lane >> 5;
-  const int col = lane & 31;
+  // lane = MN kgrp + col: operand row/column col, contraction slots 8 kgrp ..
+  // +7; result column col, rows (r / 4)(256 / MN) + 4 kgrp + r % 4
+  const int kgrp = lane / MN;
+  const int col = lane % MN;
 
   // heaviest pair blocks first (causal: the last rows see every key), kv
   // heads fastest, then the key-range splits of one pair block
@@ -475,23 +491,30 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const int t_hi = (int)(((int64_t)n_tiles * (qsplit + 1)) / p.n_q_splits);
   const int n_mine = t_hi - t_lo;
 
-  // this lane's pair: Q and dO fragments (B operands), L2 and Dl
-  const int pair = wp0 + col;
-  const bool valid = pair <= last_pair;
-  const int pc = min(pair, last_pair);
-  const int my_row = pc / G;
-  const int h = g * G + (pc - my_row * G);
-  const size_t bhr = ((size_t)b * p.H_q + h) * (size_t)p.N_q + my_row;
-  bf16x8 qf[D / 16], df[D / 16];
+  // this lane's pairs (one per column block): Q and dO fragments (B
+  // operands), L2 and Dl
+  auto bhr_of = [&](int qc) {
+    const int pc = min(wp0 + MN * qc + col, last_pair);
+    const int row = pc / G;
+    const int h = g * G + (pc - row * G);
+    return ((size_t)b * p.H_q + h) * (size_t)p.N_q + row;
+  };
+  auto row_of = [&](int qc) { return min(wp0 + MN * qc + col, last_pair) / G; };
+  bf16x8 qf[QC][D / KK], df[QC][D / KK];
+  float l2[QC], dl[QC];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 x = *reinterpret_cast<const u32x4*>(p.q + bhr * D + ks * 16 + half * 8);
-    x ^= p.q_sign;
-    qf[ks] = as_bf16x8(x);
-    df[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.dout + bhr * D + ks * 16 + half * 8));
+  for (int qc = 0; qc < QC; ++qc) {
+    const size_t bhr = bhr_of(qc);
+#pragma unroll
+    for (int ks = 0; ks < D / KK; ++ks) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(p.q + bhr * D + ks * KK + kgrp * 8);
+      x ^= p.q_sign;
+      qf[qc][ks] = as_bf16x8(x);
+      df[qc][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.dout + bhr * D + ks * KK + kgrp * 8));
+    }
+    l2[qc] = p.lse2[bhr];
+    dl[qc] = p.delta[bhr];
   }
-  const float l2 = p.lse2[bhr];
-  const float dl = p.delta[bhr];
 
   const size_t kv_base = ((size_t)b * p.H_kv + g) * (size_t)N_kv * D;
   const uint32_t head_bytes = (uint32_t)N_kv * C::ROW_BYTES;
@@ -506,26 +529,33 @@ void attn_bwd_dq_kernel(BwdParams p) {
     for (int i = 0; i < C::LPW; ++i) {
       const int li = wave * C::LPW + i;
       const int r = li * C::RPL + ld_row_in;
-      const int byte = min(t * BN + r, N_kv - 1) * C::ROW_BYTES + ((ld_chunk ^ bwd_swz<D>(r)) << 4);
+      const int byte = min(t * BN + r, N_kv - 1) * C::ROW_BYTES + ((ld_chunk ^ dq_swz<D, MN>(r)) << 4);
       dma_16B(k_rsrc, byte, st + li * 1024);
       dma_16B(v_rsrc, byte, st + C::TILE_BYTES + li * 1024);
     }
   };
 
+  // K^T (A operand of dQ^T, MN d x KK keys) from the transpose read: lane
+  // row d = MN db + col; contraction slots are the keys KK st + 4 kgrp +
+  // {0..3} (first read) and + KK/2 (second), the keys whose dS this lane
+  // holds in 8 consecutive accumulator registers.  Lane L of a 16-lane group
+  // addresses row 4 kgrp + L/4, d = d16 + 4 (L & 3) .. +4.
   const int L16 = lane & 15;
-  int tr_off[2][D / 32];
+  int tr_off[2][D / MN];
 #pragma unroll
   for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int row = 4 * half + (L16 >> 2) + 8 * hi;
-      const int d = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
-      tr_off[hi][db] = row * C::ROW_BYTES + (((d >> 3) ^ bwd_swz<D>(row)) << 4) + (d & 7) * 2;
+    for (int db = 0; db < D / MN; ++db) {
+      const int row = 4 * kgrp + (L16 >> 2) + (KK / 2) * hi;
+      const int d = db * MN + 16 * ((lane >> 4) % (MN / 16)) + 4 * (L16 & 3);
+      tr_off[hi][db] = row * C::ROW_BYTES + (((d >> 3) ^ dq_swz<D, MN>(row)) << 4) + (d & 7) * 2;
     }
 
-  f32x16 dqT[D / 32];
+  AccT dqT[D / MN][QC];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) dqT[db] = f32x16{};
+  for (int db = 0; db < D / MN; ++db)
+#pragma unroll
+    for (int qc = 0; qc < QC; ++qc) dqT[db][qc] = AccT{};
   const float sl2 = p.scale_log2;
 
   auto compute = [&](int t, int slot) {
@@ -533,46 +563,58 @@ void attn_bwd_dq_kernel(BwdParams p) {
     const uint8_t* vt = kt + C::TILE_BYTES;
     const int key0 = t * BN;
     const bool masked = (p.causal && key0 + BN - 1 > wave_row0 + off) || key0 + BN > N_kv;
-    // element (c, r) holds key key0 + c*32 + 8(r/4) + 4 half + r%4; visible below lim
-    const int lim = (p.causal ? min(my_row + off + 1, N_kv) : N_kv) - key0 - 4 * half;
-    bf16x8 dsb[BN / 16];
+    // dS of the tile in bf16, 8 consecutive accumulator registers per entry
+    // (key-block-major), the B operands of dQ^T
+    bf16x8 dsb[QC][BN / KK];
+    f32x8 sf[QC];
 #pragma unroll
-    for (int c = 0; c < BN / 32; ++c) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const int key = c * 32 + col;
+    for (int c = 0; c < BN / MN; ++c) {
+      AccT s[QC], dp[QC];
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const int chunk = ((2 * ks + half) ^ bwd_swz<D>(key)) << 4;
+      for (int qc = 0; qc < QC; ++qc) s[qc] = dp[qc] = AccT{};
+      const int key = c * MN + col;
+#pragma unroll
+      for (int ks = 0; ks < D / KK; ++ks) {
+        const int chunk = (((KK / 8) * ks + kgrp) ^ dq_swz<D, MN>(key)) << 4;
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + key * C::ROW_BYTES + chunk));
         const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + key * C::ROW_BYTES + chunk));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
-      }
-      // masked tiles only (a wave-uniform branch): invisible scores become
-      // -inf, so their dS is 0 with no per-element test below
-      if (masked) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (c * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
+        for (int qc = 0; qc < QC; ++qc) {
+          s[qc] = mfma_bf16<MN>(ka, qf[qc][ks], s[qc]);
+          dp[qc] = mfma_bf16<MN>(va, df[qc][ks], dp[qc]);
+        }
       }
-      f32x8 sf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l2));
-        sf[r & 7] = pe * (dp[r] - dl);
-        if ((r & 7) == 7) dsb[2 * c + (r >> 3)] = __builtin_convertvector(sf, bf16x8);
+      for (int qc = 0; qc < QC; ++qc) {
+        // masked tiles only (a wave-uniform branch): invisible scores become
+        // -inf, so their dS is 0 with no per-element test below.  Element r
+        // holds key key0 + MN c + (r/4)(256/MN) + 4 kgrp + r%4.
+        if (masked) {
+          const int lim = (p.causal ? min(row_of(qc) + off + 1, N_kv) : N_kv) - key0 - 4 * kgrp;
+#pragma unroll
+          for (int r = 0; r < ACC; ++r)
+            if (c * MN + (r >> 2) * (256 / MN) + (r & 3) >= lim) s[qc][r] = -INFINITY;
+        }
+#pragma unroll
+        for (int r = 0; r < ACC; ++r) {
+          const int e = c * ACC + r;
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qc][r], sl2, -l2[qc]));
+          sf[qc][e & 7] = pe * (dp[qc][r] - dl[qc]);
+          if ((e & 7) == 7) dsb[qc][e >> 3] = __builtin_convertvector(sf[qc], bf16x8);
+        }
       }
     }
-    // dQ^T += K^T dS^T; k-step st covers keys 16 st .. 16 st + 15
+    // dQ^T += K^T dS^T; step st covers keys KK st .. KK st + KK - 1
 #pragma unroll
-    for (int st = 0; st < BN / 16; ++st)
+    for (int st = 0; st < BN / KK; ++st)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint8_t* a = kt + (16 * st) * C::ROW_BYTES;
+      for (int db = 0; db < D / MN; ++db) {
+        const uint8_t* a = kt + (KK * st) * C::ROW_BYTES;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[0][db]));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[1][db]));
         const bf16x8 kT = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsb[st], dqT[db], 0, 0, 0);
+#pragma unroll
+        for (int qc = 0; qc < QC; ++qc) dqT[db][qc] = mfma_bf16<MN>(kT, dsb[qc][st], dqT[db][qc]);
       }
   };
 
@@ -589,28 +631,24 @@ void attn_bwd_dq_kernel(BwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
-  // a split writes its fp32 partial (a range with no tile writes zeros)
-  if (valid && p.n_q_splits > 1) {
-    float* dqr = p.q_part + ((size_t)qsplit * (size_t)p.rows + bhr) * D;
-    const float gs = p.grad_scale;
+  // a split writes its fp32 partial (a range with no tile writes zeros);
+  // register 4 g4 + j of dqT[db] holds d = MN db + g4 (256/MN) + 4 kgrp + j
+  const float gs = p.grad_scale;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qc = 0; qc < QC; ++qc) {
+    if (wp0 + MN * qc + col > last_pair) continue;
+    const size_t bhr = bhr_of(qc);
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * half;
-        *reinterpret_cast<f32x4*>(dqr + d0) =
-            f32x4{dqT[db][4 * g4] * gs, dqT[db][4 * g4 + 1] * gs, dqT[db][4 * g4 + 2] * gs, dqT[db][4 * g4 + 3] * gs};
-      }
-  } else if (valid) {
-    uint16_t* dqr = p.dq + bhr * D;
-    const float gs = p.grad_scale;
+    for (int db = 0; db < D / MN; ++db)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * half;
-        f32x4 f = {dqT[db][4 * g4] * gs, dqT[db][4 * g4 + 1] * gs, dqT[db][4 * g4 + 2] * gs, dqT[db][4 * g4 + 3] * gs};
-        *reinterpret_cast<u32x2*>(dqr + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4));
+      for (int g4 = 0; g4 < ACC / 4; ++g4) {
+        const int d0 = db * MN + g4 * (256 / MN) + 4 * kgrp;
+        const f32x4 f = {dqT[db][qc][4 * g4] * gs, dqT[db][qc][4 * g4 + 1] * gs, dqT[db][qc][4 * g4 + 2] * gs,
+                         dqT[db][qc][4 * g4 + 3] * gs};
+        if (p.n_q_splits > 1)
+          *reinterpret_cast<f32x4*>(p.q_part + ((size_t)qsplit * (size_t)p.rows + bhr) * D + d0) = f;
+        else
+          *reinterpret_cast<u32x2*>(p.dq + bhr * D + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4));
       }
   }
 }
