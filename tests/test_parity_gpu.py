@@ -192,6 +192,25 @@ def test_ragged_wide_grid(ea, H, D, causal):
     _check(o.cpu(), l.cpu(), O_ref, L_ref, what=f"wide split3 H{H} D{D} c{int(causal)}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_wide_grid_last_tile_one_key(ea, D):
+    """N = 65 over 256 kv heads, non-causal: one round of eight-wave
+    workgroups, so the library takes the wide shape, whose last 64-key tile
+    holds one key and 63 rows past the end.  Those rows come back from the
+    tile's buffer range as zeros and must contribute nothing.  Also through
+    attn_fwd_splitkv with three forced key splits."""
+    q, k, v = workloads.make_inputs(1, 256, 256, 65, D, seed=7700 + D)
+    scale = 1.0 / math.sqrt(D)
+    O_ref, L_ref = oracle.attention_forward(workloads.to_float64(q), workloads.to_float64(k),
+                                            workloads.to_float64(v), is_causal=False, sm_scale=scale)
+    o, l = _run(ea, q, k, v, False, scale)
+    _check(o, l, O_ref, L_ref, what=f"wide N65 D{D}")
+    dev = torch.device("cuda", 0)
+    o, l = ea.fwd_splitkv(q.to(dev), k.to(dev), v.to(dev), is_causal=False, sm_scale=scale, n_splits=3)
+    torch.cuda.synchronize()
+    _check(o.cpu(), l.cpu(), O_ref, L_ref, what=f"wide N65 split3 D{D}")
+
+
 @pytest.mark.parametrize("H_q,H_kv", [(3, 3), (6, 2), (6, 1), (8, 4), (16, 2), (32, 2), (12, 3)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_head_groupings(ea, H_q, H_kv, causal):
