@@ -144,6 +144,19 @@ def test_backward_rectangular(ea, N_q, N_kv, causal):
     _case(ea, 1, 8, 2, N_q, N_kv, 128, causal, seed=12200 + N_q + N_kv)
 
 
+@pytest.mark.parametrize("B,H_q,H_kv,N_q,N_kv,D,causal", [
+    (2, 128, 128, 100, 100, 128, False),   # 256 dQ workgroups: one round of eight waves
+    (2, 256, 128, 90, 90, 64, False),      # GQA-2, two pairs per head row
+    (2, 256, 256, 100, 100, 128, True),    # causal: 512 workgroups, two rounds
+    (2, 128, 128, 60, 300, 128, True),     # causal chunk, N_q < N_kv / 2
+])
+def test_backward_eight_wave_dq(ea, B, H_q, H_kv, N_q, N_kv, D, causal):
+    """Grids large enough for the eight-wave dQ kernel (16x16x32 MFMAs, two
+    pairs per lane) at sizes the oracle checks element by element; the
+    smaller cases above run the four-wave kernel."""
+    _case(ea, B, H_q, H_kv, N_q, N_kv, D, causal, seed=8100 + H_q + N_q)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
 def test_backward_scale_values(ea, scale):
     _case(ea, 1, 4, 2, 150, 150, 128, True, seed=12300, scale=scale)
