@@ -211,6 +211,17 @@ def test_wide_grid_last_tile_one_key(ea, D):
     _check(o.cpu(), l.cpu(), O_ref, L_ref, what=f"wide N65 split3 D{D}")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.088, 1.0])
+def test_wide_grid_scale_values(ea, scale):
+    """Zero, negative (Q negated on load) and large scales on a grid that
+    takes the wide shape (GQA-2, 128 kv heads, N = 200, non-causal)."""
+    q, k, v = workloads.make_inputs(1, 256, 128, 200, 128, seed=7800)
+    O_ref, L_ref = oracle.attention_forward(workloads.to_float64(q), workloads.to_float64(k),
+                                            workloads.to_float64(v), is_causal=False, sm_scale=scale)
+    o, l = _run(ea, q, k, v, False, scale)
+    _check(o, l, O_ref, L_ref, what=f"wide scale {scale}")
+
+
 @pytest.mark.parametrize("H_q,H_kv", [(3, 3), (6, 2), (6, 1), (8, 4), (16, 2), (32, 2), (12, 3)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_head_groupings(ea, H_q, H_kv, causal):
