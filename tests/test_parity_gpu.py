@@ -242,13 +242,48 @@ def test_identical_keys(ea):
 
 
 def test_growing_scores_force_rescaling(ea):
-    """Keys whose norm grows along the sequence push the running max up on
-    every tile, so each tile rescales the accumulator."""
+    """Key norms ramp from 0.2 to 12 along the sequence, so later scores climb
+    far past the max the first tile sets and the tile-sum check (a sum of P
+    above 2^24) takes its rescale branch on a small grid (the four-wave
+    shape).  The premise is checked on the CPU: over 30 % of the rows past
+    the first tile have a later score more than 24 (log2 units) above their
+    first tile's max.  (A ramp to 3 climbs at most 17.4: P stays below 2^18
+    and no tile rescales.)"""
     def ramp(q, k, v):
-        g = torch.linspace(0.2, 3.0, k.shape[2]).view(1, 1, -1, 1)
+        g = torch.linspace(0.2, 12.0, k.shape[2]).view(1, 1, -1, 1)
         return q, (k.float() * g).to(torch.bfloat16), v
+    q, k, v = workloads.make_inputs(1, 4, 4, 700, 128, 43)
+    _, k, _ = ramp(q, k, v)
+    s = np.einsum("bhnd,bhmd->bhnm", workloads.to_float64(q), workloads.to_float64(k)) / math.sqrt(128) / math.log(2.0)
+    first = s[:, :, 64:, :64].max(axis=-1)
+    later = s[:, :, 64:, 64:].max(axis=-1)
+    assert np.mean(later - first > 24.0) > 0.3
     for causal in (False, True):
         _full_case(ea, 1, 4, 4, 700, 128, causal, seed=43, mutate=ramp)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_grid_forced_rescaling(ea, causal):
+    """Key norms ramp from 0.1 to 25 along the sequence, so later scores
+    climb far past the max the first tile sets: the tile-sum check (a sum of
+    P above 2^24) must take its rescale branch.  The grid takes the wide
+    shape (B=2, 128 kv heads, GQA-2, N = 200).  The premise is checked on the
+    CPU: over 30 % of the rows past the first tile have a later score more
+    than 24 (log2 units) above their first tile's max."""
+    B, H_q, H_kv, N, D = 2, 256, 128, 200, 128
+    q, k, v = workloads.make_inputs(B, H_q, H_kv, N, D, seed=7900 + int(causal))
+    ramp = torch.linspace(0.1, 25.0, N).view(1, 1, -1, 1)
+    k = (k.float() * ramp).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    q64, k64, v64 = (workloads.to_float64(x) for x in (q, k, v))
+    s = np.einsum("bhnd,bhmd->bhnm", q64, np.repeat(k64, H_q // H_kv, axis=1)) * scale / math.log(2.0)
+    rows = np.arange(64, N)   # rows that see keys past the first tile (causal or not)
+    first = s[:, :, rows, :64].max(axis=-1)
+    later = np.where(np.arange(N)[None, None, None, :] <= rows[None, None, :, None], s[:, :, rows, :], -np.inf)[..., 64:].max(axis=-1)
+    assert np.mean(later - first > 24.0) > 0.3
+    O_ref, L_ref = oracle.attention_forward(q64, k64, v64, is_causal=causal, sm_scale=scale)
+    o, l = _run(ea, q, k, v, causal, scale)
+    _check(o, l, O_ref, L_ref, what=f"wide rescale c{int(causal)}")
 
 
 def test_uniform_inputs_d64(ea):
