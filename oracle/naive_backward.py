@@ -36,7 +36,9 @@ Implementation shape: per (b, h) the full score matrix is materialised (so
 inputs are limited to a few thousand rows and keys), in float64, with no
 blocking.  `backward_rows` and `backward_keys` compute the same quantities for
 chosen query rows (dQ) or chosen keys (dK, dV) of one head, taking query rows
-in blocks of ROW_BLOCK, for inputs too large for the full matrix.
+in blocks of ROW_BLOCK, for inputs too large for the full matrix;
+`backward_keys` can also sum over a subset of the query rows, so that a
+caller may split the sum over rows across processes.
 """
 from __future__ import annotations
 
@@ -107,19 +109,22 @@ def backward_rows(q, k, v, dout, b: int, h: int, rows, *, is_causal: bool, sm_sc
 
 
 def backward_keys(q, k, v, dout, b: int, g: int, keys, *, is_causal: bool, sm_scale: float,
-                  out=None):
+                  out=None, rows=None):
     """(dK[b, g, keys], dV[b, g, keys]) ([len(keys), D] each, float64), summed
     over the query heads of kv head g and all their rows; out as in
-    attention_backward."""
+    attention_backward.  rows (optional): sum over these query rows only (of
+    every head of the group), the part of the sum they contribute; the
+    default is every row."""
     B, H_q, H_kv, N_q, N_kv, D = _check(q, k, v)
     off = N_kv - N_q if is_causal else 0
     keys = np.asarray(keys, dtype=np.int64)
+    rows = np.arange(N_q) if rows is None else np.asarray(rows, dtype=np.int64)
     dK = np.zeros((keys.size, D))
     dV = np.zeros((keys.size, D))
     heads = [h for h in range(H_q) if kv_head(h, H_q, H_kv) == g]
     for h in heads:
-        for s in range(0, N_q, ROW_BLOCK):
-            r = np.arange(s, min(s + ROW_BLOCK, N_q))
+        for s in range(0, rows.size, ROW_BLOCK):
+            r = rows[s:s + ROW_BLOCK]
             P = _probs(q, k, b, h, g, r, is_causal=is_causal, sm_scale=sm_scale, off=off)
             dO = dout[b, h, r]
             O = P @ v[b, g] if out is None else out[b, h, r]

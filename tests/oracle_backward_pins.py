@@ -17,7 +17,10 @@ Pins used:
     invariant to a common shift of all keys);
   * head map: GQA gradients equal MHA gradients on repeated K/V, summed back;
   * the forward output as an input: the exact output changes nothing, and a
-    perturbed one moves dQ by the closed-form amount and leaves dV unchanged.
+    perturbed one moves dQ by the closed-form amount and leaves dV unchanged;
+  * key gradients over a subset of query rows: the parts over a partition of
+    the rows sum to the key gradients of attention_backward, and the part of
+    a single row is the outer-product formula written out for that row.
 """
 from __future__ import annotations
 
@@ -191,8 +194,41 @@ def pin_bwd_supplied_exact_output(ora):
         _close(bk, dK2[0, 1, keys], what="keys with out")
 
 
+def pin_bwd_keys_row_partition(ora):
+    """dK, dV of chosen keys summed over a partition of the query rows equal
+    the full gradients; one row's part is its own rank-one term, written out
+    per element: dV_j = sum_h P_hj dO_h, dK_j = scale sum_h P_hj (dP_hj - Dl_h) q_h."""
+    q, k, v, dO = _inputs(1, 4, 2, 9, 13, 5, 91)
+    keys = np.array([0, 4, 12])
+    for causal in (False, True):
+        _, dK, dV = ora.attention_backward(q, k, v, dO, is_causal=causal, sm_scale=0.7)
+        parts = [np.array([0, 3, 8]), np.array([1, 2]), np.array([4, 5, 6, 7])]
+        got = [ora.backward_keys(q, k, v, dO, 0, 1, keys, is_causal=causal, sm_scale=0.7, rows=r)
+               for r in parts]
+        _close(sum(g_[0] for g_ in got), dK[0, 1, keys], what="row partition dK")
+        _close(sum(g_[1] for g_ in got), dV[0, 1, keys], what="row partition dV")
+        i = 6
+        bk, bv = ora.backward_keys(q, k, v, dO, 0, 1, keys, is_causal=causal, sm_scale=0.7,
+                                   rows=np.array([i]))
+        off = 13 - 9 if causal else 0
+        ek, ev = np.zeros_like(bk), np.zeros_like(bv)
+        for h in (2, 3):  # the query heads of kv head 1
+            s_ = [0.7 * sum(q[0, h, i, d] * k[0, 1, j, d] for d in range(5)) for j in range(13)]
+            vis = [j for j in range(13) if not causal or j <= i + off]
+            m = max(s_[j] for j in vis)
+            z = sum(math.exp(s_[j] - m) for j in vis)
+            p = [math.exp(s_[j] - m) / z if j in vis else 0.0 for j in range(13)]
+            dp = [sum(dO[0, h, i, d] * v[0, 1, j, d] for d in range(5)) for j in range(13)]
+            dl = sum(p[j] * dp[j] for j in range(13))
+            for n, j in enumerate(keys):
+                ev[n] += p[j] * dO[0, h, i]
+                ek[n] += 0.7 * p[j] * (dp[j] - dl) * q[0, h, i]
+        _close(bk, ek, what="one row's dK part")
+        _close(bv, ev, what="one row's dV part")
+
+
 PINS_BWD = [
     pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_single_key, pin_bwd_zero_scale,
     pin_bwd_identical_keys, pin_bwd_key_grads_sum_to_zero, pin_bwd_gqa_equals_repeated,
-    pin_bwd_supplied_exact_output,
+    pin_bwd_supplied_exact_output, pin_bwd_keys_row_partition,
 ]

@@ -56,6 +56,9 @@ MUTATIONS = {
     "keys_dv_scaled": ("dV += Pk.T @ dO", "dV += sm_scale * (Pk.T @ dO)"),
     "dv_scaled": ("dV[b, g] += P.T @ dO", "dV[b, g] += sm_scale * (P.T @ dO)"),
     "head_map_modulo": ("g = kv_head(h, H_q, H_kv)", "g = h % H_kv"),
+    "keys_row_subset_ignored": ("rows = np.arange(N_q) if rows is None else np.asarray(rows, dtype=np.int64)",
+                                "rows = np.arange(N_q)"),
+    "keys_row_blocks_skip_first": ("r = rows[s:s + ROW_BLOCK]", "r = rows[s + 1:s + ROW_BLOCK]"),
     "supplied_output_ignored": ("O = P @ v[b, g] if out is None else out[b, h]", "O = P @ v[b, g]"),
 }
 
