@@ -42,48 +42,52 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 MFMA_FLOP_PER_CLK = 256 * 4096  # dense bf16 MFMA, whole chip (2.5 PFLOP/s at 2.4 GHz)
 METRIC = "attention fwd TFLOPS and % of MI355X bf16 MFMA peak (GQA causal, N=1K–32K)"
-KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_02_amd", "csrc", f)
-                  for f in ("attn_fwd_kernel.hpp", "attn_abi.hip")]
+CSRC = os.path.join(ROOT, "exact_attention_02_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("attn_fwd_kernel.hpp", "attn_abi.hip")]
+BWD_SOURCES = [os.path.join(CSRC, f) for f in ("attn_bwd_kernel.hpp", "attn_bwd.hip")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (sources or KERNEL_SOURCES):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when it is missing or was taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.md")
+def read_profile(name: str, key: str, sources=None):
+    """A figure (`key: value`) from a committed rocprofv3 summary under
+    profiles/, or None when the file is missing or its kernel-source hash
+    differs from the current sources (a figure of other kernels)."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
-    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_hash or not m_b or m_hash.group(1) != kernel_source_hash():
+    m_v = re.search(re.escape(key) + r":\s*([0-9.eE+-]+)", txt)
+    if not m_hash or not m_v or m_hash.group(1) != kernel_source_hash(sources):
         return None
-    return float(m_b.group(1))
+    return float(m_v.group(1))
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary (or None)."""
+    return read_profile(f"attn_fwd_{workload}_hbm_traffic.md", "hbm_bytes_per_launch")
 
 
 def read_clock(workload: str):
-    """Shader clock (GHz) during the kernel from the committed rocprofv3
-    GRBM_COUNT summary, or None when missing or taken on other sources."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_clock.md")
-    if not os.path.exists(path):
-        return None
-    txt = open(path).read()
-    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
-    m_f = re.search(r"shader_clock_ghz:\s*([0-9.]+)", txt)
-    if not m_hash or not m_f or m_hash.group(1) != kernel_source_hash():
-        return None
-    return float(m_f.group(1))
+    """Shader clock (GHz) during the kernel from the committed GRBM_COUNT summary (or None)."""
+    return read_profile(f"attn_fwd_{workload}_clock.md", "shader_clock_ghz")
+
+
+def read_mfma_busy(workload: str):
+    """Fraction of SIMD cycles with the MFMA pipe busy during the kernel, from
+    the committed SQ_VALU_MFMA_BUSY_CYCLES summary (or None)."""
+    return read_profile(f"attn_fwd_{workload}_mfma_busy.md", "mfma_busy_frac")
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -262,8 +266,79 @@ def time_backward(ea, torch, w, steps, warmup):
         ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return {"wall_ms_per_step": wall * 1e3 / steps, "n_splits": ns,
-            "event_ms": [s_.elapsed_time(e) for s_, e in zip(starts, ends)]}
+    return ({"wall_ms_per_step": wall * 1e3 / steps, "n_splits": ns,
+             "event_ms": [s_.elapsed_time(e) for s_, e in zip(starts, ends)]},
+            (q, k, v, dO, out.cpu(), dq.cpu(), dk.cpu(), dv.cpu()))
+
+
+def _bwd_init(q64, k64, v64, d64, o64):
+    _G["bwd"] = (q64, k64, v64, d64, o64)
+
+
+def _bwd_task(args):
+    from threadpoolctl import threadpool_limits
+    import oracle
+    kind, idx, sel, rows, causal, scale = args
+    q64, k64, v64, d64, o64 = _G["bwd"]
+    with threadpool_limits(1):
+        if kind == "rows":
+            return kind, idx, oracle.backward_rows(q64, k64, v64, d64, 0, idx, sel, is_causal=causal,
+                                                   sm_scale=scale, out=o64)
+        return kind, idx, oracle.backward_keys(q64, k64, v64, d64, 0, idx, sel, is_causal=causal,
+                                               sm_scale=scale, out=o64, rows=rows)
+
+
+def backward_parity(w, tensors):
+    """Part of the CPU-baseline leg of --backward: dQ of sampled rows of every
+    head of the first and last kv groups, and dK/dV of sampled keys of those
+    groups summed over every query row, against the oracle's row and key
+    entry points (key sums split over a process pool in 512-row blocks).
+    Tolerance as the backward parity tests: |g - r| <= 2e-2 s + 2e-2 |r|, s the
+    larger of the reference row's RMS, the sampled tensor's RMS and 1e-4."""
+    q, k, v, dO, o, dq, dk, dv = tensors
+    q64, k64, v64, d64, o64 = (workloads.to_float64(x) for x in (q, k, v, dO, o))
+    N, G = w.N, w.H_q // w.H_kv
+    rng = np.random.default_rng(w.seed + 1)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, N // 2 - 1, N // 2, N - 129, N - 128,
+                                      N - 65, N - 64, N - 2, N - 1], rng.choice(N, 6, replace=False)]))
+    rows = rows[rows < w.Nq]
+    keys = np.unique(np.concatenate([[0, 1, 127, 128, N // 2, N - 2, N - 1], rng.choice(N, 5, replace=False)]))
+    groups = (0, w.H_kv - 1)
+    tasks = [("rows", g * G + j, rows, None, w.causal, w.sm_scale) for g in groups for j in range(G)]
+    tasks += [("keys", g, keys, np.arange(r0, min(r0 + 512, w.Nq)), w.causal, w.sm_scale)
+              for g in groups for r0 in range(0, w.Nq, 512)]
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    t0 = time.perf_counter()
+    ref_k = {g: np.zeros((keys.size, w.D)) for g in groups}
+    ref_v = {g: np.zeros((keys.size, w.D)) for g in groups}
+    worst = {"dQ": 0.0, "dK": 0.0, "dV": 0.0}
+    ok = True
+
+    def check(name, got, ref):
+        nonlocal ok
+        g_ = got.double().numpy()
+        rms = float(np.sqrt(np.mean(ref * ref)))
+        sc = np.maximum(np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True)), max(rms, 1e-4))
+        err = np.abs(g_ - ref)
+        ok = ok and bool(np.isfinite(g_).all()) and bool(np.all(err <= 2e-2 * sc + 2e-2 * np.abs(ref)))
+        worst[name] = max(worst[name], float((err / (sc + np.abs(ref))).max()))
+
+    ctx = __import__("multiprocessing").get_context("fork")
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx, initializer=_bwd_init,
+                                initargs=(q64, k64, v64, d64, o64)) as ex:
+        for kind, idx, r in ex.map(_bwd_task, tasks):
+            if kind == "rows":
+                check("dQ", dq[0, idx, rows], r)
+            else:
+                ref_k[idx] += r[0]
+                ref_v[idx] += r[1]
+    for g in groups:
+        check("dK", dk[0, g, keys], ref_k[g])
+        check("dV", dv[0, g, keys], ref_v[g])
+    return {"sampled_pass": ok, "dq_rows": int(rows.size) * len(groups) * G,
+            "dkdv_keys": int(keys.size) * len(groups),
+            "max_scaled_err": {k_: round(v_, 5) for k_, v_ in worst.items()},
+            "wall_s": round(time.perf_counter() - t0, 1)}
 
 
 def _parity_init(q, k, v, o, l):
@@ -400,13 +475,37 @@ def main():
         return
 
     if args.backward:
-        # one workload's attn_bwd alone (counter runs: --steps 2 --warmup 1)
+        # one workload's attn_bwd alone, one JSON line (counter runs: --steps 2
+        # --warmup 1 --no-cpu-baseline)
         w = workloads.WORKLOADS[args.workload]
-        r = time_backward(ea, torch, w, args.steps, args.warmup)
-        e = float(np.median(r["event_ms"]))
-        log(f"[bwd] {w.name:24s} median {e:9.4f} ms  min {min(r['event_ms']):9.4f} ms  "
-            f"{2.5 * w.flops() / (e * 1e-3) / 1e12:8.1f} TFLOP/s  splits {r['n_splits']}  "
-            f"({len(r['event_ms'])} launches)")
+        r, tensors = time_backward(ea, torch, w, args.steps, args.warmup)
+        ev = r["event_ms"]
+        avg = float(np.mean(ev))
+        flops = 2.5 * w.flops()   # five products of 2*D per visible (query, key) pair
+        nbytes = w.bwd_algorithmic_bytes()
+        log(f"[bwd] {w.name:24s} median {float(np.median(ev)):9.4f} ms  min {min(ev):9.4f} ms  "
+            f"{flops / (avg * 1e-3) / 1e12:8.1f} TFLOP/s  splits {r['n_splits']}  ({len(ev)} launches)")
+        parity = None
+        if not args.no_cpu_baseline:
+            log("[bwd] oracle: sampled dQ rows and dK/dV keys")
+            parity = backward_parity(w, tensors)
+            log(f"[bwd] parity {parity}")
+        achieved = flops / (avg * 1e-3) / 1e12
+        traffic = read_profile(f"attn_bwd_{w.name}_hbm_traffic.md", "hbm_bytes_per_launch", BWD_SOURCES)
+        print(json.dumps({
+            "metric": "attention bwd TFLOPS (dQ, dK, dV; 2.5x the forward FLOPs) and % of MI355X bf16 MFMA peak",
+            "value": round(flops / (r["wall_ms_per_step"] * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": len(ev), "ms_per_step": round(r["wall_ms_per_step"], 4),
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "N": w.N,
+                       "N_q": w.Nq, "D": w.D, "causal": w.causal, "seed": w.seed},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic, "kernel": "attn_bwd (prep, dK/dV and dQ kernels)",
+                         "avg_launch_ms": round(avg, 4), "median_launch_ms": round(float(np.median(ev)), 4),
+                         "n_splits": r["n_splits"], "algorithmic_flops_per_launch": flops,
+                         "algorithmic_bytes_per_launch": nbytes},
+            "parity": parity}), flush=True)
         return
 
     if args.backward_sweep:
@@ -415,7 +514,7 @@ def main():
         for name, ww in workloads.WORKLOADS.items():
             if ww.N_q is not None and name != "chunk_gqa4_q512_n8192":
                 continue
-            r = time_backward(ea, torch, ww, None, None)
+            r, _ = time_backward(ea, torch, ww, None, None)
             e = float(np.median(r["event_ms"]))
             tf = 2.5 * ww.flops() / (e * 1e-3) / 1e12
             log(f"[bwd] {name:24s} median {e:9.4f} ms  min {min(r['event_ms']):9.4f} ms  "
@@ -466,6 +565,9 @@ def main():
             peak_clk = MFMA_FLOP_PER_CLK * clock * 1e9 / 1e12
             roofline.update({"clock_ghz": clock, "peak_at_clock": round(peak_clk, 1),
                              "frac_at_clock": round(achieved / peak_clk, 4)})
+        busy = read_mfma_busy(w.name)
+        if busy is not None:
+            roofline["mfma_busy"] = busy
     else:
         # below the ridge (decode): bytes moved, not FLOPs, bound the kernel
         gbs = nbytes / (avg_ms * 1e-3) / 1e9

@@ -75,6 +75,15 @@ enum attn_status {
  *   is_causal 0 or 1
  *   stream    a hipStream_t, or NULL for the default stream
  *
+ * Numeric range: the softmax runs in fp32 on scores in log2 units
+ * (s_ij * log2 e).  The result is specified while every such scaled score
+ * is below 2^31 in magnitude and the fp32 products q.k are finite; the
+ * rounding error of the largest score, times the scale, is then the exponent
+ * of its weight and stays representable.  Beyond that range the output is
+ * unspecified (it may be NaN).  The range depends on the data, so it is not
+ * checked; with sm_scale = 1/sqrt(D) it holds for any inputs whose dot
+ * products stay below about 2^30.
+ *
  * Ownership: the caller allocates and frees all five buffers; they must be
  * device memory of the current device.  out and lse must not overlap each
  * other or any input.
@@ -138,6 +147,7 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, flo
                      int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t D,
                      float sm_scale, int is_causal, int64_t n_splits, void* workspace,
                      size_t workspace_size, void* stream);
+
 
 /*
  * attn_splitkv_num_splits -- the split count attn_fwd_splitkv uses for

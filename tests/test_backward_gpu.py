@@ -268,3 +268,80 @@ def test_backward_deterministic_and_no_overrun(ea):
         res.append([t.clone() for t in (dq, dk, dv)])
     for a, b in zip(*res):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+_BW = {}
+
+
+def _bw_init(q64, k64, v64, d64, o64):
+    _BW["t"] = (q64, k64, v64, d64, o64)
+
+
+def _bw_keys_task(args):
+    """dK, dV of the sampled keys of kv head g, summed over one block of query
+    rows of every head of the group (the parent sums the blocks)."""
+    from threadpoolctl import threadpool_limits
+    g, keys, rows, scale = args
+    q64, k64, v64, d64, o64 = _BW["t"]
+    with threadpool_limits(1):
+        return g, oracle.backward_keys(q64, k64, v64, d64, 0, g, keys, is_causal=True, sm_scale=scale,
+                                       out=o64, rows=rows)
+
+
+def _bw_rows_task(args):
+    from threadpoolctl import threadpool_limits
+    h, rows, scale = args
+    q64, k64, v64, d64, o64 = _BW["t"]
+    with threadpool_limits(1):
+        return h, oracle.backward_rows(q64, k64, v64, d64, 0, h, rows, is_causal=True, sm_scale=scale,
+                                       out=o64)
+
+
+@pytest.mark.parametrize("name", ["gqa4_n8192_causal", "gqa4_n32768_causal"])
+def test_backward_timed_workloads_sampled(ea, name):
+    """The backward at the shapes its throughput is quoted on (causal GQA-4,
+    B=1, H_q=32, H_kv=8, D=128), in the library's default launch (the split
+    count attn_bwd_num_splits picks), fed this library's own forward output
+    and LSE.  dQ of sampled rows (first and last row tiles, both sides of
+    64- and 128-row boundaries, random rows) of every head of two kv groups,
+    and dK/dV of sampled keys (0, 127, 128, N-1, random) of the same two kv
+    groups summed over every query row, against the oracle's row and key
+    entry points.  The key sums run over a process pool in blocks of 512 rows
+    (about 200 CPU-seconds at N = 32768)."""
+    import concurrent.futures as cf
+    import multiprocessing
+    import os
+    w = workloads.WORKLOADS[name]
+    print(f"[bwd-timed] {name}", flush=True)
+    q, k, v, dO = _inputs(w.B, w.H_q, w.H_kv, w.N, w.N, w.D, w.seed)
+    dev = _dev()
+    o, lse = ea.fwd(q.to(dev), k.to(dev), v.to(dev), is_causal=True)
+    o, lse = o.cpu(), lse.cpu()
+    dq, dk, dv = _run_bwd(ea, q, k, v, o, dO, lse, True, w.sm_scale)
+    print(f"[bwd-timed] {name}: GPU done, oracle next", flush=True)
+    q64, k64, v64, d64, o64 = (workloads.to_float64(x) for x in (q, k, v, dO, o))
+    N, G = w.N, w.H_q // w.H_kv
+    rng = np.random.default_rng(w.seed + 1)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, N // 2 - 1, N // 2, N - 129, N - 128,
+                                      N - 65, N - 64, N - 2, N - 1], rng.choice(N, 6, replace=False)]))
+    keys = np.unique(np.concatenate([[0, 1, 127, 128, N // 2, N - 2, N - 1], rng.choice(N, 5, replace=False)]))
+    groups = (0, w.H_kv - 1)
+    heads = [g * G + j for g in groups for j in range(G)]
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    key_tasks = [(g, keys, np.arange(r0, min(r0 + 512, N)), w.sm_scale)
+                 for g in groups for r0 in range(0, N, 512)]
+    rk = {g: np.zeros((keys.size, w.D)) for g in groups}
+    rv = {g: np.zeros((keys.size, w.D)) for g in groups}
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=multiprocessing.get_context("fork"),
+                                initializer=_bw_init, initargs=(q64, k64, v64, d64, o64)) as ex:
+        row_res = list(ex.map(_bw_rows_task, [(h, rows, w.sm_scale) for h in heads]))
+        for g, (a, b_) in ex.map(_bw_keys_task, key_tasks):
+            rk[g] += a
+            rv[g] += b_
+    for h, r in row_res:
+        _check("dQ", dq[0, h, rows], r, f"{name} dQ h{h}")
+    for g in groups:
+        _check("dK", dk[0, g, keys], rk[g], f"{name} dK g{g}")
+        _check("dV", dv[0, g, keys], rv[g], f"{name} dV g{g}")
+    print(f"[bwd-timed] {name}: {len(heads)} heads x {rows.size} rows, {len(groups)} groups x "
+          f"{keys.size} keys pass", flush=True)

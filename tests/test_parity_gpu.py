@@ -286,6 +286,76 @@ def test_wide_grid_forced_rescaling(ea, causal):
     _check(o, l, O_ref, L_ref, what=f"wide rescale c{int(causal)}")
 
 
+@pytest.mark.parametrize("B,H_q,H_kv,N,causal", [
+    (1, 32, 8, 4096, True),    # wide shape (16x16x32 MFMAs) for both runs
+    (1, 32, 8, 4096, False),
+    (2, 32, 8, 1024, True),    # mid shape (32x32x16 MFMAs) for both runs
+    (1, 16, 1, 512, True),     # MQA: both runs split the keys, at different boundaries
+])
+def test_gqa_equals_own_mha_on_repeated_kv(ea, B, H_q, H_kv, N, causal):
+    """Grouped-query attention equals this library's own multi-head run on K
+    and V repeated to H_q heads (head h reads kv head h * H_kv / H_q; page
+    "Triton Cuda Attention", section 变体改法, GQA).  Where both runs take the
+    same kernel shape and no key split, every query sees the same K/V tiles
+    in the same order with the same arithmetic, and i.i.d. N(0,1) inputs never
+    take the rescale branch (a score 24 above the first tile's max), so the
+    outputs are bit-identical; with key splits (MQA) the split boundaries
+    differ and the two agree to the parity tolerance."""
+    dev = torch.device("cuda", 0)
+    q, k, v = workloads.make_inputs(B, H_q, H_kv, N, 128, seed=9100 + N + H_kv)
+    G = H_q // H_kv
+    kr, vr = (x.repeat_interleave(G, dim=1).contiguous() for x in (k, v))
+    o_g, l_g = _run(ea, q, k, v, causal, 1.0 / math.sqrt(128))
+    o_m, l_m = _run(ea, q, kr, vr, causal, 1.0 / math.sqrt(128))
+    splits_g = ea.attn_splitkv_num_splits(B, H_q, H_kv, N, N, 128, causal)
+    splits_m = ea.attn_splitkv_num_splits(B, H_q, H_q, N, N, 128, causal)
+    if splits_g == 1 and splits_m == 1:
+        assert torch.equal(o_g.view(torch.int16), o_m.view(torch.int16)), "GQA and MHA outputs differ"
+        assert torch.equal(l_g.view(torch.int32), l_m.view(torch.int32)), "GQA and MHA LSEs differ"
+    else:
+        assert splits_g > 1 and splits_m > 1
+        o64 = o_m.to(torch.float64).numpy()
+        _check(o_g, l_g, o64, l_m.to(torch.float64).numpy(), what="GQA vs own MHA")
+    O_ref, L_ref = oracle.attention_forward(workloads.to_float64(q), workloads.to_float64(k),
+                                            workloads.to_float64(v), is_causal=causal,
+                                            sm_scale=1.0 / math.sqrt(128))
+    _check(o_g, l_g, O_ref, L_ref, what="GQA vs oracle")
+
+
+@pytest.mark.parametrize("scale", [1e3, 1e6, -1e6])
+def test_large_scales_peaked_softmax(ea, scale):
+    """Scales far above 1/sqrt(D): each row's softmax is one-hot on its largest
+    score (the second largest is at least 1e-3 below it here, checked on the
+    CPU, so the weight of any other key is below e^-1), O is that key's V row
+    and the LSE is the largest scaled score, of order 1e7 at scale 1e6.  The
+    LSE bound is relative there: the fp32 score carries the rounding of its
+    128-term dot product, of order 2^-24 times the sum of |q_d k_d| (a few
+    times the score itself for N(0,1) data), and the scale multiplies it, so
+    the bound is 2^-20 of |LSE| on top of 1e-3.  Within the documented range
+    (scaled scores below 2^31 in log2 units) the kernel's exponent of the
+    largest score is the rounding error of that score times the scale, which
+    stays small."""
+    B, H_q, H_kv, N, D = 1, 4, 2, 300, 128
+    q, k, v = workloads.make_inputs(B, H_q, H_kv, N, D, seed=9300)
+    q64, k64, v64 = (workloads.to_float64(x) for x in (q, k, v))
+    for causal in (False, True):
+        s = scale * np.einsum("bhnd,bhmd->bhnm", q64, np.repeat(k64, 2, axis=1))
+        if causal:
+            s = np.where(np.arange(N)[None, None, None, :] > np.arange(N)[None, None, :, None], -np.inf, s)
+        srt = np.sort(s, axis=-1)
+        gap = (srt[..., -1] - srt[..., -2])[:, :, 1:]   # row 0 of causal sees one key
+        assert gap.min() > 1.0
+        assert np.abs(srt[..., -1]).max() / math.log(2.0) < 2.0 ** 31
+        O_ref, L_ref = oracle.attention_forward(q64, k64, v64, is_causal=causal, sm_scale=scale)
+        o, l = _run(ea, q, k, v, causal, scale)
+        o64, l64 = o.to(torch.float64).numpy(), l.to(torch.float64).numpy()
+        assert np.all(np.isfinite(o64)) and np.all(np.isfinite(l64))
+        assert np.all(np.abs(o64 - O_ref) <= O_ATOL + O_RTOL * np.abs(O_ref)), f"O at scale {scale}"
+        rel = float(np.max(np.abs(l64 - L_ref) / np.maximum(np.abs(L_ref), 1.0)))
+        assert np.all(np.abs(l64 - L_ref) <= LSE_ATOL + 2.0 ** -20 * np.abs(L_ref)), \
+            f"LSE at scale {scale}: max relative error {rel:.3e}"
+
+
 def test_uniform_inputs_d64(ea):
     _full_case(ea, 2, 8, 2, 300, 64, True, seed=44, dist="uniform")
 

@@ -64,6 +64,14 @@ class Workload:
         lse = self.B * self.H_q * self.Nq * 4
         return 2 * qo + 2 * kv + lse
 
+    def bwd_algorithmic_bytes(self) -> int:
+        """The backward's Q, K, V, O, dO (bf16) and LSE (fp32) read once and
+        dQ, dK, dV (bf16) written once."""
+        qo = self.B * self.H_q * self.Nq * self.D * 2
+        kv = self.B * self.H_kv * self.N * self.D * 2
+        lse = self.B * self.H_q * self.Nq * 4
+        return 4 * qo + 4 * kv + lse
+
 
 _W = [
     Workload("tiny_mha_n256_d64", 1, 4, 4, 256, 64, False, 101),
