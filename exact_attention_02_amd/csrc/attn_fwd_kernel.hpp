@@ -106,6 +106,15 @@ struct BoolTag {
   static constexpr bool value = V;
 };
 
+// An LDS ring slot known at compile time (the steady-state loop is unrolled
+// by the ring depth, so every operand read takes its slot's offset as an
+// immediate); the tail passes a plain int.
+template <int V>
+struct SlotC {
+  static constexpr int value = V;
+  __device__ constexpr operator int() const { return V; }
+};
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P stays <= 2^8
@@ -113,6 +122,14 @@ constexpr float kOverflowSum = 16777216.0f;  // 2^24: largest tile sum of P take
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 for gfx9 (untyped dword access)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// x in a VGPR whose value the compiler no longer knows: a constant folded
+// into it stays out of the LDS instructions' 16-bit offset field, which the
+// V ring's base (64 KiB and up in the deepest ring) would overflow.
+__device__ __forceinline__ int opaque_vgpr(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // Reductions over the lanes that hold one MFMA column (lanes l, l^32 for
 // MN = 32; l, l^16, l^32, l^48 for MN = 16).  v_permlane32_swap exchanges
@@ -358,22 +375,24 @@ void attn_fwd_kernel(FwdParams p) {
   //   d = d16 + L of the group's four rows (d16: the group's 16 d).
   const int L = lane & 15;
   const int vt_row = 4 * kgrp + (L >> 2);
+  // V ring base plus lane offset of each d block (the tile's slot and step
+  // are added as immediates)
   int vt_off[D / MN];
 #pragma unroll
   for (int db = 0; db < D / MN; ++db) {
     const int d = db * MN + 16 * ((lane >> 4) % (MN / 16)) + 4 * (L & 3);
     const int chunk = (d >> 3) ^ v_swz<D, MN>(vt_row);
-    vt_off[db] = vt_row * C::ROW_BYTES + chunk * 16 + (d & 7) * 2;
+    vt_off[db] = opaque_vgpr(P * C::TILE_BYTES + vt_row * C::ROW_BYTES + chunk * 16 + (d & 7) * 2);
   }
-  auto k_read = [&](int tile, int i) {
-    const uint8_t* kb = lds + (tile % P) * C::TILE_BYTES;
+  auto k_read = [&](auto slot, int i) {
+    const uint8_t* kb = lds + int(slot) * C::TILE_BYTES;
     const int c = i % KB, ks = i / KB;  // consecutive reads alternate key blocks
     const int key = c * MN + col;
     return *reinterpret_cast<const u32x4*>(kb + key * C::ROW_BYTES +
                                            ((((KK / 8) * ks + kgrp) ^ k_swz<D, MN>(key)) << 4));
   };
-  auto v_read = [&](int tile, int i) {
-    const uint8_t* vb = lds + (P + tile % P) * C::TILE_BYTES;
+  auto v_read = [&](auto slot, int i) {
+    const uint8_t* vb = lds + int(slot) * C::TILE_BYTES;
     const int st = i / (D / MN), db = i % (D / MN);
     const uint8_t* a0 = vb + vt_off[db] + (KK * st) * C::ROW_BYTES;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a0));
@@ -401,17 +420,17 @@ void attn_fwd_kernel(FwdParams p) {
 
   using Scores = AccT[KB][QC];
   // S^T = K Q^T of one tile with no other work interleaved (prologue only)
-  auto s_tile = [&](int tile, Scores& s) {
+  auto s_tile = [&](auto slot, Scores& s) {
 #pragma unroll
     for (int c = 0; c < KB; ++c)
 #pragma unroll
       for (int qc = 0; qc < QC; ++qc) s[c][qc] = AccT{};
     u32x4 kx[PF + 1];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) kx[i] = k_read(tile, i);
+    for (int i = 0; i < PF; ++i) kx[i] = k_read(slot, i);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      if (i + PF < NS) kx[(i + PF) % (PF + 1)] = k_read(tile, i + PF);
+      if (i + PF < NS) kx[(i + PF) % (PF + 1)] = k_read(slot, i + PF);
       const int c = i % KB, ks = i / KB;
 #pragma unroll
       for (int qc = 0; qc < QC; ++qc)
@@ -473,7 +492,8 @@ void attn_fwd_kernel(FwdParams p) {
   // operand of the KK keys of step st: accumulator registers 8 st .. 8 st + 7
   // of the lane's scores in key-block-major order.
   bf16x8 pbf[QC][BN / KK];
-  auto phase_x = [&](int t, Scores& sc, Scores& sn, auto has_next_tag) {
+  // ks_next: the ring slot of tile t + 1 (int, or SlotC in the unrolled loop)
+  auto phase_x = [&](int t, auto ks_next, Scores& sc, Scores& sn, auto has_next_tag) {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     float m_sub[QC], l_t[QC];
 #pragma unroll
@@ -499,10 +519,10 @@ void attn_fwd_kernel(FwdParams p) {
         for (int qc = 0; qc < QC; ++qc) sn[c][qc] = AccT{};
       u32x4 kx[PF + 1];
 #pragma unroll
-      for (int i = 0; i < PF; ++i) kx[i] = k_read(t + 1, i);
+      for (int i = 0; i < PF; ++i) kx[i] = k_read(ks_next, i);
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        if (i + PF < NS) kx[(i + PF) % (PF + 1)] = k_read(t + 1, i + PF);
+        if (i + PF < NS) kx[(i + PF) % (PF + 1)] = k_read(ks_next, i + PF);
         const int c = i % KB, ks = i / KB;
 #pragma unroll
         for (int qc = 0; qc < QC; ++qc)
@@ -546,23 +566,32 @@ void attn_fwd_kernel(FwdParams p) {
       if (needs_mask(t + 1)) apply_mask(t + 1, sn);
     }
   };
-  auto phase_y = [&](int t) {
+  // vs: the ring slot of tile t
+  auto phase_y = [&](auto vs) {
     // O^T += V^T P^T; step st covers keys KK st .. KK st + KK - 1
     bf16x8 vx[PF + 1];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) vx[i] = v_read(t, i);
+    for (int i = 0; i < PF; ++i) vx[i] = v_read(vs, i);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      if (i + PF < NP) vx[(i + PF) % (PF + 1)] = v_read(t, i + PF);
+      if (i + PF < NP) vx[(i + PF) % (PF + 1)] = v_read(vs, i + PF);
       const int st = i / (D / MN), db = i % (D / MN);
 #pragma unroll
       for (int qc = 0; qc < QC; ++qc)
         acc[db][qc] = mfma_bf16<MN>(vx[i % (PF + 1)], pbf[qc][st], acc[db][qc]);
     }
   };
+  // one tile with its ring slots computed at run time (prologue and tail)
   auto step = [&](int t, Scores& sc, Scores& sn, auto has_next_tag) {
-    phase_x(t, sc, sn, has_next_tag);
-    phase_y(t);
+    phase_x(t, (t + 1) % P, sc, sn, has_next_tag);
+    phase_y(t % P);
+  };
+  // tile t = t0 + J of the unrolled loop, t0 a multiple of P: both slots are
+  // compile-time constants
+  auto step_c = [&](int t0, auto j_tag, Scores& sc, Scores& sn) {
+    constexpr int J = decltype(j_tag)::value;
+    phase_x(t0 + J, SlotC<(J + 1) % P>{}, sc, sn, BoolTag<true>{});
+    phase_y(SlotC<J>{});
   };
 
   // Load schedule.  Group j loads K(j) into K slot j % P and V(j-1) into V
@@ -591,15 +620,34 @@ void attn_fwd_kernel(FwdParams p) {
     for (int j = 0; j < P; ++j) issue_group(j);
     sync_prologue();
     Scores sa, sb;
-    s_tile(0, sa);
+    s_tile(SlotC<0>{}, sa);
     if (needs_mask(0)) apply_mask(0, sa);
     {
       float mx[QC];
       lane_max(sa, mx);
       update_max(mx);
     }
-    // steady state, unrolled by two so the score buffers alternate without copies
+    // steady state, unrolled by the ring depth P (even: the score buffers
+    // alternate without copies, and every LDS offset is a constant), then
+    // by two with run-time slots for the last tiles
     int t = 0;
+    static_assert(P == 2 || P == 4, "ring depths of 2 or 4: even, so the score buffers stay in step");
+    for (; t + P < n_tiles; t += P) {
+      sync_steady();
+      issue_group(t + P);
+      step_c(t, SlotC<0>{}, sa, sb);
+      sync_steady();
+      issue_group(t + 1 + P);
+      step_c(t, SlotC<1>{}, sb, sa);
+      if constexpr (P >= 4) {
+        sync_steady();
+        issue_group(t + 2 + P);
+        step_c(t, SlotC<2>{}, sa, sb);
+        sync_steady();
+        issue_group(t + 3 + P);
+        step_c(t, SlotC<3>{}, sb, sa);
+      }
+    }
     for (; t + 2 < n_tiles; t += 2) {
       sync_steady();
       issue_group(t + P);
