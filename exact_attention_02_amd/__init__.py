@@ -24,6 +24,7 @@ import os
 from .build import LIB_PATH
 
 __all__ = ["attn_fwd", "fwd", "attn_fwd_splitkv", "fwd_splitkv", "attn_splitkv_num_splits",
+           "attn_fwd_splitkv_static", "attn_static_scratch_bytes",
            "attn_splitkv_workspace_size", "attn_bwd", "bwd", "attn_bwd_num_splits",
            "attn_bwd_workspace_size",
            "attn_mla_decode", "attn_mla_num_splits", "attn_mla_workspace_size", "mla_absorb_q",
@@ -32,6 +33,7 @@ __all__ = ["attn_fwd", "fwd", "attn_fwd_splitkv", "fwd_splitkv", "attn_splitkv_n
            "load_library", "AttnError", "EXPORTED_SYMBOLS"]
 
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splitkv", "attn_splitkv_num_splits",
+                    "attn_fwd_splitkv_static", "attn_static_scratch_bytes",
                     "attn_splitkv_workspace_size", "attn_bwd", "attn_bwd_num_splits",
                     "attn_bwd_workspace_size",
                     "attn_mla_decode", "attn_mla_num_splits", "attn_mla_workspace_size",
@@ -65,6 +67,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd_splitkv.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [
         ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t,
         ctypes.c_void_p]
+    lib.attn_fwd_splitkv_static.restype = ctypes.c_int
+    lib.attn_fwd_splitkv_static.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [
+        ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
+    lib.attn_static_scratch_bytes.restype = ctypes.c_size_t
+    lib.attn_static_scratch_bytes.argtypes = []
     lib.attn_splitkv_num_splits.restype = ctypes.c_int64
     lib.attn_splitkv_num_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int]
     lib.attn_splitkv_workspace_size.restype = ctypes.c_size_t
@@ -211,6 +218,41 @@ def attn_fwd_splitkv(q, k, v, out, lse, is_causal: bool = False, sm_scale: float
                                   int(bool(is_causal)), int(n_splits), ws_ptr, ws_bytes, handle)
     if st != 0:
         raise AttnError(st, attn_status_string(st), "attn_fwd_splitkv")
+
+
+def attn_static_scratch_bytes() -> int:
+    """Bytes of the library's static per-device scratch (attn_fwd_splitkv_static)."""
+    return int(load_library().attn_static_scratch_bytes())
+
+
+def attn_fwd_splitkv_static(q, k, v, out, lse, is_causal: bool = False,
+                            sm_scale: float | None = None, n_splits: int = 0, stream=None) -> None:
+    """attn_fwd_splitkv with its partial results in the library's static device
+    scratch instead of a caller workspace: the call allocates nothing.  Calls
+    that overlap on one GPU race on that scratch."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, D]")
+    B, H_q, N_q, D = q.shape
+    H_kv, N_kv = k.shape[1], k.shape[2]
+    _check_tensor(q, "q", (B, H_q, N_q, D), torch.bfloat16)
+    _check_tensor(k, "k", (B, H_kv, N_kv, D), torch.bfloat16)
+    _check_tensor(v, "v", (B, H_kv, N_kv, D), torch.bfloat16)
+    _check_tensor(out, "out", (B, H_q, N_q, D), torch.bfloat16)
+    _check_tensor(lse, "lse", (B, H_q, N_q), torch.float32)
+    for name, t in (("k", k), ("v", v), ("out", out), ("lse", lse)):
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_splitkv_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         lse.data_ptr(), B, H_q, H_kv, N_q, N_kv, D, float(sm_scale),
+                                         int(bool(is_causal)), int(n_splits), handle)
+    if st != 0:
+        raise AttnError(st, attn_status_string(st), "attn_fwd_splitkv_static")
 
 
 def fwd_splitkv(q, k, v, is_causal: bool = False, sm_scale: float | None = None,

@@ -1,6 +1,8 @@
 // C ABI of the fused attention forward (declared in include/attn.h):
 // argument validation, kernel-shape and split choice, and kernel launches.
-// The library allocates nothing, keeps no state and never synchronises.
+// The library allocates nothing and never synchronises; its only state is
+// the static scratch of attn_fwd_splitkv_static and that scratch's address
+// per device.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -8,6 +10,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "attn_fwd_kernel.hpp"
@@ -302,6 +305,63 @@ extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, voi
   return run(a, ns, workspace, stream);
 }
 
+// ---- the split forward without a caller workspace (for callers that cannot
+// allocate device memory: code under HIP graph capture, tight serving loops).
+// Its partial results live in this file-scope device array, one copy per GPU
+// the library runs on, held until the process ends.  Host code never passes
+// the array's name to a kernel (in host code it is a host-side stand-in):
+// the first call on a device looks up that device's address with
+// hipGetSymbolAddress and keeps it.
+static constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of this device's scratch (looked up once per device, with the
+// device current), or nullptr when the lookup fails.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" size_t attn_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+extern "C" int attn_fwd_splitkv_static(const void* q, const void* k, const void* v, void* out, float* lse,
+                                       int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv,
+                                       int64_t D, float sm_scale, int is_causal, int64_t n_splits,
+                                       void* stream) {
+  const Problem a{q, k, v, out, lse, B, H_q, H_kv, N_q, N_kv, D, sm_scale, is_causal};
+  bool empty = false;
+  int st = check_sizes(a, n_splits, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if ((st = check_buffers(a)) != ATTN_OK) return st;
+  int64_t ns = n_splits;
+  if (ns == 0) {
+    // the library's choice, lowered until its partials fit the static scratch
+    ns = choose_splits(a);
+    while (ns > 1 && workspace_bytes(B, H_q, N_q, D, ns) > kStaticScratchBytes) --ns;
+  } else if (workspace_bytes(B, H_q, N_q, D, ns) > kStaticScratchBytes) {
+    return ATTN_ERR_STATIC_SCRATCH;
+  }
+  if ((st = check_alias(a, nullptr, 0)) != ATTN_OK) return st;
+  void* ws = nullptr;
+  if (ns > 1 && !(ws = device_scratch())) return ATTN_ERR_LAUNCH;
+  return run(a, ns, ws, stream);
+}
+
 extern "C" const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "success";
@@ -322,8 +382,11 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_ERR_NO_KEYS: return "N_kv is 0 while there are query rows";
     case ATTN_ERR_SPLITS: return "n_splits must be in [0, 256] (attn_bwd: [0, 64])";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL, too small or not 16-byte aligned";
+    case ATTN_ERR_STATIC_SCRATCH:
+      return "the requested key splits need more partial-result memory than the library's static scratch "
+             "(attn_static_scratch_bytes) holds";
     default: return "unknown status";
   }
 }
 
-extern "C" int attn_abi_version(void) { return 6; }
+extern "C" int attn_abi_version(void) { return 7; }

@@ -51,7 +51,9 @@ enum attn_status {
   ATTN_ERR_CAUSAL_SHAPE = 11,  /* is_causal with more query rows than keys     */
   ATTN_ERR_NO_KEYS = 12,       /* N_kv = 0 while there are query rows          */
   ATTN_ERR_SPLITS = 13,        /* n_splits above the entry point's maximum   */
-  ATTN_ERR_WORKSPACE = 14      /* split workspace NULL, too small or misaligned */
+  ATTN_ERR_WORKSPACE = 14,     /* split workspace NULL, too small or misaligned */
+  ATTN_ERR_STATIC_SCRATCH = 15 /* attn_fwd_splitkv_static: the requested splits'
+                                  partials exceed the static scratch          */
 };
 
 /*
@@ -147,6 +149,33 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, flo
                      int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t D,
                      float sm_scale, int is_causal, int64_t n_splits, void* workspace,
                      size_t workspace_size, void* stream);
+
+/*
+ * attn_fwd_splitkv_static -- attn_fwd_splitkv for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The partial results of the key splits live in a
+ * static device array of the library (attn_static_scratch_bytes(), 16 MiB),
+ * one per GPU, held until the process ends; there is no workspace argument
+ * and the call allocates nothing (no hipMalloc, no allocating library call).
+ * The first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress) once.
+ *
+ * Semantics, arguments and check order as attn_fwd_splitkv without
+ * workspace/workspace_size; n_splits 0 takes the library's split count,
+ * lowered until its partials fit the scratch; an explicit n_splits whose
+ * partials (attn_splitkv_workspace_size) exceed the scratch returns
+ * ATTN_ERR_STATIC_SCRATCH before anything is enqueued.  Every call on one
+ * GPU shares that GPU's scratch: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and give undefined results; calls on
+ * one stream are ordered and safe.  The scratch needs no clearing: each call
+ * writes every partial it reads.
+ */
+int attn_fwd_splitkv_static(const void* q, const void* k, const void* v, void* out, float* lse,
+                            int64_t B, int64_t H_q, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t D,
+                            float sm_scale, int is_causal, int64_t n_splits, void* stream);
+
+/* Size in bytes of the static scratch attn_fwd_splitkv_static uses (per GPU). */
+size_t attn_static_scratch_bytes(void);
 
 
 /*

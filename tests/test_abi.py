@@ -38,7 +38,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 6
+    assert lib.attn_abi_version() == 7
 
 
 def test_status_strings_distinct(lib):
@@ -350,3 +350,42 @@ def test_mla_projection_arguments_rejected(lib):
     assert lib.mla_up_project(QL, WM, WM, 1, 4, 1, 512, 128, None) == STATUS["ATTN_ERR_ALIAS"]
     assert lib.mla_up_project(QL, WM, OL, -1, 4, 1, 512, 128, None) == STATUS["ATTN_ERR_NEGATIVE_SIZE"]
     assert ok
+
+
+# ------------------------------------------------------------ static-scratch split entry
+def call_static(lib, q=Q, k=K, v=V, o=O, l=L, B=1, H_q=4, H_kv=2, N_q=16, N_kv=40, D=64,
+                scale=0.125, causal=0, n_splits=4):
+    return lib.attn_fwd_splitkv_static(q, k, v, o, l, B, H_q, H_kv, N_q, N_kv, D, ctypes.c_float(scale),
+                                       causal, n_splits, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_splits=-1), "ATTN_ERR_NEGATIVE_SIZE"),
+    (dict(H_q=6, H_kv=4), "ATTN_ERR_HEAD_RATIO"),
+    (dict(scale=float("nan")), "ATTN_ERR_SCALE"),
+    (dict(n_splits=257), "ATTN_ERR_SPLITS"),
+    (dict(causal=1, N_q=41, N_kv=40), "ATTN_ERR_CAUSAL_SHAPE"),
+    (dict(N_kv=0), "ATTN_ERR_NO_KEYS"),
+    (dict(o=0), "ATTN_ERR_NULL_POINTER"),
+    (dict(k=K + 2), "ATTN_ERR_ALIGNMENT"),
+    # 256 splits of 160 rows at D=128: 21 MB of partials, above the 16 MiB scratch
+    (dict(N_q=40, D=128, n_splits=256), "ATTN_ERR_STATIC_SCRATCH"),
+    (dict(l=Q + 64), "ATTN_ERR_ALIAS"),
+])
+def test_static_invalid_arguments_rejected(lib, kw, code):
+    assert call_static(lib, **kw) == STATUS[code]
+
+
+def test_static_scratch_size_and_limit(lib):
+    assert ea.attn_static_scratch_bytes() == 16 << 20
+    # the largest request that fits is accepted up to the alias check
+    ns = 1
+    while ea.attn_splitkv_workspace_size(1, 4, 40, 128, ns + 1) <= ea.attn_static_scratch_bytes():
+        ns += 1
+    assert call_static(lib, N_q=40, D=128, n_splits=ns, o=Q) == STATUS["ATTN_ERR_ALIAS"]
+    assert call_static(lib, N_q=40, D=128, n_splits=ns + 1, o=Q) == STATUS["ATTN_ERR_STATIC_SCRATCH"]
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N_q=0)])
+def test_static_empty_work_is_success_without_pointers(lib, kw):
+    assert call_static(lib, q=0, k=0, v=0, o=0, l=0, **kw) == STATUS["ATTN_OK"]
