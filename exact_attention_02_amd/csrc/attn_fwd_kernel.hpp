@@ -484,17 +484,27 @@ void attn_fwd_kernel(FwdParams p) {
     }
   };
 
-  // One pipelined step over tile t (its scores already in sc, masked, max
-  // applied), in two phases: P(t) = 2^(S(t) sl2 - m) interleaved with
-  // S(t+1) = K(t+1) Q^T into sn (when HAS_NEXT), then O += V(t) P(t).  P(t)
-  // passes between them in pbf, declared outside both (fewer registers live
-  // across the step than a local of one lambda).  pbf[qc][st] is the B
-  // operand of the KK keys of step st: accumulator registers 8 st .. 8 st + 7
-  // of the lane's scores in key-block-major order.
-  bf16x8 pbf[QC][BN / KK];
-  // ks_next: the ring slot of tile t + 1 (int, or SlotC in the unrolled loop)
-  auto phase_x = [&](int t, auto ks_next, Scores& sc, Scores& sn, auto has_next_tag) {
+  // Software pipeline: one phase per tile t, entered with the scores S(t)
+  // computed, masked and the max applied:
+  //   O += V(t-1) P(t-1)          (HAS_PREV: 32 MFMAs on V^T operand reads)
+  //   P(t) = 2^(S(t) sl2 - m)      (the exponentials, spread over both halves)
+  //   S(t+1) = K(t+1) Q^T          (HAS_NEXT: 32 MFMAs on K operand reads)
+  // so the softmax VALU of a tile runs under the MFMAs of both neighbouring
+  // products instead of only the scores of the next tile.  P(t) goes to
+  // pcur while P(t-1) is read from pprev (two buffers, alternating by tile
+  // parity).  pcur[qc][st] is the B operand of the KK keys of step st:
+  // accumulator registers 8 st .. 8 st + 7 of the lane's scores in
+  // key-block-major order.
+  using PBuf = bf16x8[QC][BN / KK];
+  constexpr int NE = QC * NV;  // exponentials per lane and tile
+  auto phase = [&](int t, auto ks_next, auto vs_prev, Scores& sc, Scores& sn, PBuf& pcur, PBuf& pprev,
+                   auto has_prev_tag, auto has_next_tag) {
+    constexpr bool HAS_PREV = decltype(has_prev_tag)::value;
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    // exponentials under the PV half and under the score half
+    constexpr int EA = HAS_PREV ? (HAS_NEXT ? NE / 2 : NE) : 0;
+    constexpr int EB = HAS_NEXT ? NE - EA : 0;
+    static_assert(EA % NP == 0 && EB % NS == 0, "exponentials spread evenly over the operand reads");
     float m_sub[QC], l_t[QC];
 #pragma unroll
     for (int qc = 0; qc < QC; ++qc) {
@@ -510,8 +520,32 @@ void attn_fwd_kernel(FwdParams p) {
       const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e / ACC][qc][e % ACC], sl2, -m_sub[qc]));
       pf[qc][e & 7] = pe;
       l_t[qc] += pe;
-      if ((e & 7) == 7) pbf[qc][e >> 3] = __builtin_convertvector(pf[qc], bf16x8);
+      if ((e & 7) == 7) {
+        pcur[qc][e >> 3] = __builtin_convertvector(pf[qc], bf16x8);
+        // packed here: otherwise the compiler carries the eight fp32 values
+        // into the next phase and converts them there
+        asm volatile("" : "+v"(pcur[qc][e >> 3]));
+      }
     };
+    if constexpr (HAS_PREV) {
+      // O^T += V^T P^T of tile t-1; step st covers keys KK st .. KK st + KK - 1
+      bf16x8 vx[PF + 1];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) vx[i] = v_read(vs_prev, i);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        if (i + PF < NP) vx[(i + PF) % (PF + 1)] = v_read(vs_prev, i + PF);
+        const int st = i / (D / MN), db = i % (D / MN);
+#pragma unroll
+        for (int qc = 0; qc < QC; ++qc)
+          acc[db][qc] = mfma_bf16<MN>(vx[i % (PF + 1)], pprev[qc][st], acc[db][qc]);
+#pragma unroll
+        for (int e = 0; e < EA / NP; ++e) p_elem(i * (EA / NP) + e);
+      }
+    }
+    // keep the halves apart: interleaving them would hold the next tile's
+    // score accumulators and the previous tile's P at once
+    if constexpr (HAS_PREV && HAS_NEXT) __builtin_amdgcn_sched_barrier(0);
     if constexpr (HAS_NEXT) {
 #pragma unroll
       for (int c = 0; c < KB; ++c)
@@ -528,16 +562,18 @@ void attn_fwd_kernel(FwdParams p) {
         for (int qc = 0; qc < QC; ++qc)
           sn[c][qc] = mfma_bf16<MN>(as_bf16x8(kx[i % (PF + 1)]), qf[qc][ks], sn[c][qc]);
 #pragma unroll
-        for (int e = 0; e < EPR; ++e) p_elem(i * EPR + e);
+        for (int e = 0; e < EB / NS; ++e) p_elem(EA + i * (EB / NS) + e);
       }
-    } else {
+    }
+    if constexpr (!HAS_PREV && !HAS_NEXT) {
 #pragma unroll
-      for (int j = 0; j < QC * NV; ++j) p_elem(j);
+      for (int j = 0; j < NE; ++j) p_elem(j);
     }
     // A tile sum above 2^24 means some score exceeds the max in use by more
     // than 24 (log2 units), or overflowed: take this tile's true max, rescale
-    // the state and recompute the tile's exponentials (rare: the first tile
-    // sets the max, and scores rarely climb that far above it).
+    // the state (O already holds every tile before this one) and recompute
+    // the tile's exponentials (rare: the first tile sets the max, and scores
+    // rarely climb that far above it).
     bool big = false;
 #pragma unroll
     for (int qc = 0; qc < QC; ++qc) big |= !(l_t[qc] <= kOverflowSum);
@@ -557,7 +593,7 @@ void attn_fwd_kernel(FwdParams p) {
         l_t[qc] = 0.f;
       }
 #pragma unroll
-      for (int j = 0; j < QC * NV; ++j) p_elem(j);
+      for (int j = 0; j < NE; ++j) p_elem(j);
     }
 #pragma unroll
     for (int qc = 0; qc < QC; ++qc) l_run[qc] += l_t[qc];
@@ -566,9 +602,8 @@ void attn_fwd_kernel(FwdParams p) {
       if (needs_mask(t + 1)) apply_mask(t + 1, sn);
     }
   };
-  // vs: the ring slot of tile t
-  auto phase_y = [&](auto vs) {
-    // O^T += V^T P^T; step st covers keys KK st .. KK st + KK - 1
+  // O += V(t) P(t) of the last tile, after every phase
+  auto last_pv = [&](auto vs, PBuf& pl) {
     bf16x8 vx[PF + 1];
 #pragma unroll
     for (int i = 0; i < PF; ++i) vx[i] = v_read(vs, i);
@@ -577,39 +612,28 @@ void attn_fwd_kernel(FwdParams p) {
       if (i + PF < NP) vx[(i + PF) % (PF + 1)] = v_read(vs, i + PF);
       const int st = i / (D / MN), db = i % (D / MN);
 #pragma unroll
-      for (int qc = 0; qc < QC; ++qc)
-        acc[db][qc] = mfma_bf16<MN>(vx[i % (PF + 1)], pbf[qc][st], acc[db][qc]);
+      for (int qc = 0; qc < QC; ++qc) acc[db][qc] = mfma_bf16<MN>(vx[i % (PF + 1)], pl[qc][st], acc[db][qc]);
     }
   };
-  // one tile with its ring slots computed at run time (prologue and tail)
-  auto step = [&](int t, Scores& sc, Scores& sn, auto has_next_tag) {
-    phase_x(t, (t + 1) % P, sc, sn, has_next_tag);
-    phase_y(t % P);
-  };
-  // tile t = t0 + J of the unrolled loop, t0 a multiple of P: both slots are
-  // compile-time constants
-  auto step_c = [&](int t0, auto j_tag, Scores& sc, Scores& sn) {
-    constexpr int J = decltype(j_tag)::value;
-    phase_x(t0 + J, SlotC<(J + 1) % P>{}, sc, sn, BoolTag<true>{});
-    phase_y(SlotC<J>{});
-  };
 
-  // Load schedule.  Group j loads K(j) into K slot j % P and V(j-1) into V
-  // slot (j-1) % P; the step over tile t reads K(t+1) and V(t), i.e. group
-  // t+1.  Groups are issued P-1 ahead: after the barrier that opens tile t,
-  // group t+P goes into the slots that group t used (read during tile t-1 and
-  // finished by every wave).  A group past either end of the sequence loads a
-  // clamped, valid tile into its (free) slots, so every group is the same
-  // number of loads and each wait below is one constant vmcnt.
+  // Load schedule.  Group j loads K(j) into K slot j % P and V(j-2) into V
+  // slot (j-2) % P; the phase of tile t reads K(t+1) and V(t-1), i.e. group
+  // t+1.  Groups are issued P-1 ahead: after the barrier that opens the
+  // phase of tile t, group t+P goes into the slots that the phase of tile t-1
+  // read (K(t), V(t-2)), which every wave has finished.  A group past either
+  // end of the sequence loads a clamped, valid tile into its (free) slots, so
+  // every group is the same number of loads and each wait below is one
+  // constant vmcnt.
   auto issue_group = [&](int j) {
     issue_tile(min(j, n_tiles - 1), j % P, k_head, 0);
-    issue_tile(max(min(j - 1, n_tiles - 1), 0), (j + P - 1) % P, v_head, 1);
+    issue_tile(max(min(j - 2, n_tiles - 1), 0), (j + P - 2) % P, v_head, 1);
   };
   constexpr int GROUP_LOADS = 2 * C::LOADS_PER_WAVE;
   auto sync_prologue = [&]() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 1) * GROUP_LOADS) : "memory");
     __syncthreads();
   };
+  // every load of groups up to the one that the next phase reads has landed
   auto sync_steady = [&]() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 2) * GROUP_LOADS) : "memory");
     __syncthreads();
@@ -619,7 +643,8 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int j = 0; j < P; ++j) issue_group(j);
     sync_prologue();
-    Scores sa, sb;
+    Scores sa, sb;  // S(t) of even tiles in sa, of odd tiles in sb
+    PBuf pa, pb;    // P(t) of even tiles in pa, of odd tiles in pb
     s_tile(SlotC<0>{}, sa);
     if (needs_mask(0)) apply_mask(0, sa);
     {
@@ -627,47 +652,61 @@ void attn_fwd_kernel(FwdParams p) {
       lane_max(sa, mx);
       update_max(mx);
     }
-    // steady state, unrolled by the ring depth P (even: the score buffers
-    // alternate without copies, and every LDS offset is a constant), then
-    // by two with run-time slots for the last tiles
-    int t = 0;
-    static_assert(P == 2 || P == 4, "ring depths of 2 or 4: even, so the score buffers stay in step");
+    sync_steady();
+    issue_group(P);
+    if (n_tiles > 1)
+      phase(0, SlotC<1>{}, 0, sa, sb, pa, pb, BoolTag<false>{}, BoolTag<true>{});
+    else
+      phase(0, 0, 0, sa, sb, pa, pb, BoolTag<false>{}, BoolTag<false>{});
+    // Steady state from tile 1, unrolled by the ring depth P: tile t = t0 + J
+    // with t0 = 1 mod P, so the ring slots of K(t+1) and V(t-1) and the
+    // parity of t are compile-time constants (every LDS offset an
+    // immediate, the buffers alternate without copies).  Then the last
+    // tiles with run-time slots; t is odd there.
+    static_assert(P == 2 || P == 4, "ring depths of 2 or 4: even, so the buffers stay in step");
+    int t = 1;
     for (; t + P < n_tiles; t += P) {
       sync_steady();
       issue_group(t + P);
-      step_c(t, SlotC<0>{}, sa, sb);
+      phase(t, SlotC<2 % P>{}, SlotC<0>{}, sb, sa, pb, pa, BoolTag<true>{}, BoolTag<true>{});
       sync_steady();
       issue_group(t + 1 + P);
-      step_c(t, SlotC<1>{}, sb, sa);
+      phase(t + 1, SlotC<3 % P>{}, SlotC<1>{}, sa, sb, pa, pb, BoolTag<true>{}, BoolTag<true>{});
       if constexpr (P >= 4) {
         sync_steady();
         issue_group(t + 2 + P);
-        step_c(t, SlotC<2>{}, sa, sb);
+        phase(t + 2, SlotC<0>{}, SlotC<2>{}, sb, sa, pb, pa, BoolTag<true>{}, BoolTag<true>{});
         sync_steady();
         issue_group(t + 3 + P);
-        step_c(t, SlotC<3>{}, sb, sa);
+        phase(t + 3, SlotC<1>{}, SlotC<3>{}, sa, sb, pa, pb, BoolTag<true>{}, BoolTag<true>{});
       }
     }
     for (; t + 2 < n_tiles; t += 2) {
       sync_steady();
       issue_group(t + P);
-      step(t, sa, sb, BoolTag<true>{});
+      phase(t, (t + 1) % P, (t - 1) % P, sb, sa, pb, pa, BoolTag<true>{}, BoolTag<true>{});
       sync_steady();
       issue_group(t + 1 + P);
-      step(t + 1, sb, sa, BoolTag<true>{});
+      phase(t + 1, (t + 2) % P, t % P, sa, sb, pa, pb, BoolTag<true>{}, BoolTag<true>{});
     }
     if (t + 1 < n_tiles) {
       sync_steady();
       issue_group(t + P);
-      step(t, sa, sb, BoolTag<true>{});
+      phase(t, (t + 1) % P, (t - 1) % P, sb, sa, pb, pa, BoolTag<true>{}, BoolTag<true>{});
       sync_steady();
       issue_group(t + 1 + P);
-      step(t + 1, sb, sa, BoolTag<false>{});
-    } else {
+      phase(t + 1, 0, t % P, sa, sb, pa, pb, BoolTag<true>{}, BoolTag<false>{});
+    } else if (t < n_tiles) {
       sync_steady();
       issue_group(t + P);
-      step(t, sa, sb, BoolTag<false>{});
+      phase(t, 0, (t - 1) % P, sb, sa, pb, pa, BoolTag<true>{}, BoolTag<false>{});
     }
+    // the last tile's O += V P, once its V tile (group n_tiles + 1) has landed
+    sync_steady();
+    if ((n_tiles - 1) % 2 == 0)
+      last_pv((n_tiles - 1) % P, pa);
+    else
+      last_pv((n_tiles - 1) % P, pb);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may outlive the workgroup
   }
 
