@@ -80,14 +80,15 @@ def read_traffic(workload: str):
 
 
 def read_clock(workload: str):
-    """Shader clock (GHz) during the kernel from the committed GRBM_COUNT summary (or None)."""
-    return read_profile(f"attn_fwd_{workload}_clock.md", "shader_clock_ghz")
+    """Shader clock (GHz) during the kernel from the committed counter summary
+    (GRBM_COUNT over the dispatch), or None."""
+    return read_profile(f"attn_fwd_{workload}_counters.md", "shader_clock_ghz")
 
 
 def read_mfma_busy(workload: str):
     """Fraction of SIMD cycles with the MFMA pipe busy during the kernel, from
-    the committed SQ_VALU_MFMA_BUSY_CYCLES summary (or None)."""
-    return read_profile(f"attn_fwd_{workload}_mfma_busy.md", "mfma_busy_frac")
+    the same summary (SQ_VALU_MFMA_BUSY_CYCLES), or None."""
+    return read_profile(f"attn_fwd_{workload}_counters.md", "mfma_busy_frac")
 
 
 # ---------------------------------------------------------------- CPU baseline
