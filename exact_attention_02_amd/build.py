@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "attn_abi.hip"), os.path.join(CSRC, "attn_bwd.hip"),
            os.path.join(CSRC, "attn_mla.hip")]
 DEPENDS = [os.path.join(CSRC, "attn_fwd_kernel.hpp"), os.path.join(CSRC, "attn_bwd_kernel.hpp"),
+           os.path.join(CSRC, "abi_util.hpp"),
            os.path.join(CSRC, "attn_mla_kernel.hpp"),
            os.path.join(os.path.dirname(PKG_DIR), "include", "attn.h")]
 

@@ -14,8 +14,12 @@
 
 #include "../../include/attn.h"
 #include "attn_fwd_kernel.hpp"
+#include "abi_util.hpp"
 
 namespace {
+
+using ea02::abi::device_cus;
+using ea02::abi::overlaps;
 
 using ea02::FwdParams;
 using ea02::MergeParams;
@@ -36,19 +40,6 @@ constexpr int kNarrowNW = 1, kNarrowP = 2, kNarrowBN = 32, kNarrowMN = 32;
 constexpr int kNarrowPairs = 64;
 constexpr int kMaxSplits = 256;
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b || !na || !nb) return false;
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + nb && y < x + na;
-}
-
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return 256;
-  return cus;
-}
 
 enum class Kind { kWide, kMid, kNarrow };
 

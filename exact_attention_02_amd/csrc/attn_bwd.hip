@@ -11,8 +11,12 @@
 
 #include "../../include/attn.h"
 #include "attn_bwd_kernel.hpp"
+#include "abi_util.hpp"
 
 namespace {
+
+using ea02::abi::device_cus;
+using ea02::abi::overlaps;
 
 using ea02::BwdParams;
 
@@ -48,19 +52,6 @@ int64_t worth_splitting(int64_t n, int64_t tiles_max, int64_t share, double part
   return saved > cost ? n : 1;
 }
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b || !na || !nb) return false;
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + nb && y < x + na;
-}
-
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return 256;
-  return cus;
-}
 
 struct Shape {
   int64_t B, H_q, H_kv, N_q, N_kv, D;

@@ -11,8 +11,12 @@
 
 #include "../../include/attn.h"
 #include "attn_mla_kernel.hpp"
+#include "abi_util.hpp"
 
 namespace {
+
+using ea02::abi::device_cus;
+using ea02::abi::overlaps;
 
 using ea02::MlaParams;
 using ea02::MlaProjParams;
@@ -20,20 +24,7 @@ constexpr int kMlaP = 4;
 constexpr int kMlaPairs = 64;  // (token, head) pairs per workgroup
 constexpr int kMlaMaxSplits = 256;
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b || !na || !nb) return false;
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + nb && y < x + na;
-}
 bool mis16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
-
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return 256;
-  return cus;
-}
 
 size_t mla_ws_bytes(int64_t B, int64_t H, int64_t S, int64_t n_splits) {
   if (n_splits <= 1) return 0;
