@@ -493,6 +493,7 @@ def main():
             log(f"[bwd] parity {parity}")
         achieved = flops / (avg * 1e-3) / 1e12
         traffic = read_profile(f"attn_bwd_{w.name}_hbm_traffic.md", "hbm_bytes_per_launch", BWD_SOURCES)
+        busy = read_profile(f"attn_bwd_{w.name}_hbm_traffic.md", "mfma_busy_frac", BWD_SOURCES)
         print(json.dumps({
             "metric": "attention bwd TFLOPS (dQ, dK, dV; 2.5x the forward FLOPs) and % of MI355X bf16 MFMA peak",
             "value": round(flops / (r["wall_ms_per_step"] * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
@@ -502,7 +503,8 @@ def main():
                        "N_q": w.Nq, "D": w.D, "causal": w.causal, "seed": w.seed},
             "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                         "traffic": traffic, "kernel": "attn_bwd (prep, dK/dV and dQ kernels)",
+                         "traffic": traffic, "mfma_busy": busy,
+                         "kernel": "attn_bwd (prep, dK/dV and dQ kernels)",
                          "avg_launch_ms": round(avg, 4), "median_launch_ms": round(float(np.median(ev)), 4),
                          "n_splits": r["n_splits"], "algorithmic_flops_per_launch": flops,
                          "algorithmic_bytes_per_launch": nbytes},
