@@ -27,6 +27,11 @@
 //    read, while P and dS, rounded to bf16, are the B operands exactly as the
 //    accumulator holds them (the query order this implies is the order the
 //    transpose read returns).
+//    With one wave per SIMD nothing hides a wave's own stalls, so the 32-row
+//    blocks are software-pipelined: the softmax VALU of block b issues
+//    between the MFMAs of block b-1's dV/dK products and block b+1's S/dP
+//    products.  Every MFMA is a compiler builtin, so the compiler sees the
+//    accumulators' latencies (it places them in AGPRs, next to K and V).
 //  * attn_bwd_dq_kernel: the forward's layout (a lane owns one (row, head)
 //    pair of a kv group, K/V tiles stream through LDS): S^T = K Q^T,
 //    dP^T = V dO^T, dS^T = P^T (dP^T - Dl), dQ^T += K^T dS^T with K^T from the
@@ -38,6 +43,8 @@
 #include "attn_fwd_kernel.hpp"
 
 namespace ea02 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct BwdParams {
   const uint16_t* q;     // [B, H_q, N_q, D] bf16
@@ -113,17 +120,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void attn_bwd_
   }
 }
 
-// acc += a b with the accumulator pinned to AGPRs.  With one wave per SIMD the
-// dK/dV kernel holds 128 accumulator registers beside K, V and the score
-// tiles; in AGPRs they leave the VGPRs to the S and dP products (which the
-// build keeps in VGPRs, where the softmax reads them) and no copies between
-// the two files remain in the tile loop.  The compiler does not look inside
-// the asm for MFMA hazards: the two wait states cover a VALU write of an
-// operand just before, and the kernel waits before it reads the AGPRs.
-__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
 // ---------------------------------------------------------------- dK, dV
 template <int D, int NW, int P, int BP>
 struct BwdKvCfg {
@@ -196,6 +192,9 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
       vf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.v + kr + ks * 16 + half * 8));
     }
   }
+  // K and V are MFMA B operands only: kept in AGPRs (an MFMA reads them there)
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
 
   // Q, dO, L2 and Dl of the kv group's G heads: [G, N_q, ...] contiguous
   const size_t qg_rows = ((size_t)b * p.H_q + (size_t)g * G) * (size_t)N_q;
@@ -269,86 +268,199 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   }
   const float sl2 = p.scale_log2;
 
-  auto compute = [&](int t, int slot) {
-    int hs, row0;
-    tile_rows(t, hs, row0);
-    const uint8_t* qt = lds + slot * C::STAGE_BYTES;
-    const uint8_t* dot = qt + C::TILE_BYTES;
-    const float* stl = reinterpret_cast<const float*>(qt + 2 * C::TILE_BYTES + wave * C::STAT_BYTES);
-    const float* std_ = stl + 64;
-    // masked tile: rows that cannot see some key of this wave, or rows past N_q
-    const bool masked = (p.causal && row0 + off < kw + 31) || row0 + BP > N_q;
+  // Software pipeline over the 32-row blocks b of the workgroup's tiles
+  // (block b is rows 32 (b % 2) .. of the range's tile b / 2).  Per block:
+  //   A(b): S and dP (D/8 MFMAs on Q and dO rows read from LDS),
+  //   E(b): P = 2^(S scale - L2) and dS = P (dP - Dl) (the VALU, one
+  //         exponential per element), rounded to bf16,
+  //   B(b): dV^T += dO^T P and dK^T += Q^T dS (D/8 MFMAs on transpose reads).
+  // Phase b runs B(b-1) and then A(b+1) with the elements of E(b) spread over
+  // both, so the softmax VALU of a block issues under the MFMAs of its
+  // neighbours: with one wave per SIMD no other wave would hide it.  S and dP
+  // of a block are held for one phase, P and dS for the next; even blocks use
+  // the first set of registers, odd blocks the second.
+  auto stage = [&](int slot) { return lds + slot * C::STAGE_BYTES; };
+  constexpr int PF = 3;          // LDS operand prefetch distance (MFMA pairs)
+  constexpr int NPAIR = D / 16;  // MFMA pairs of A (k-steps) and of B ((st, db) pairs)
+  constexpr int NEL = 16;        // elements of E per lane and block
+  static_assert(NEL % NPAIR == 0, "elements spread evenly over the MFMA pairs");
+  auto a_part = [&](const uint8_t* tb, int c, f32x16& s, f32x16& dp, auto&& hook) {
+    const uint8_t* qt = tb;
+    const uint8_t* dot = tb + C::TILE_BYTES;
+    const int row = c * 32 + col;
+    s = f32x16{};
+    dp = f32x16{};
+    bf16x8 qx[PF + 1], ox[PF + 1];
 #pragma unroll
-    for (int c = 0; c < NBLK; ++c) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int i = 0; i < PF; ++i) {
+      qx[i] = row_read(qt, row, 2 * i + half);
+      ox[i] = row_read(dot, row, 2 * i + half);
+    }
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read(qt, c * 32 + col, 2 * ks + half), kf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read(dot, c * 32 + col, 2 * ks + half), vf[ks], dp, 0, 0, 0);
+    for (int ks = 0; ks < NPAIR; ++ks) {
+      if (ks + PF < NPAIR) {
+        qx[(ks + PF) % (PF + 1)] = row_read(qt, row, 2 * (ks + PF) + half);
+        ox[(ks + PF) % (PF + 1)] = row_read(dot, row, 2 * (ks + PF) + half);
       }
-      // element r holds query row row0 + c*32 + 8(r/4) + 4 half + r%4
-      f32x4 l4[4], d4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        l4[j] = *reinterpret_cast<const f32x4*>(stl + c * 32 + 8 * j + 4 * half);
-        d4[j] = *reinterpret_cast<const f32x4*>(std_ + c * 32 + 8 * j + 4 * half);
-      }
-      f32x8 pf, sf;
-      bf16x8 pb[2], dsb[2];
-      // masked tiles only (a wave-uniform branch): invisible scores become
-      // -inf, so their P and dS are 0 with no per-element test below
-      if (masked) {
-        const int lo_vis = my_key - off - row0 - c * 32 - 4 * half;  // visible: index >= lo_vis
-        const int hi_vis = N_q - row0 - c * 32 - 4 * half;           // and index < hi_vis
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int idx = 8 * (r >> 2) + (r & 3);
-          if ((p.causal && idx < lo_vis) || idx >= hi_vis) s[r] = -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2, -l4[r >> 2][r & 3]));
-        pf[r & 7] = pe;
-        sf[r & 7] = pe * (dp[r] - d4[r >> 2][r & 3]);
-        if ((r & 7) == 7) {
-          pb[r >> 3] = __builtin_convertvector(pf, bf16x8);
-          dsb[r >> 3] = __builtin_convertvector(sf, bf16x8);
-        }
-      }
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          mfma_agpr(dvT[db], tr_read(dot + c * 32 * C::ROW_BYTES, st, db), pb[st]);
-          mfma_agpr(dkT[db], tr_read(qt + c * 32 * C::ROW_BYTES, st, db), dsb[st]);
-        }
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qx[ks % (PF + 1)], kf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ox[ks % (PF + 1)], vf[ks], dp, 0, 0, 0);
+      hook(ks);
     }
   };
+  auto b_part = [&](const uint8_t* tb, int c, const u32x4* pb, const u32x4* dsb, auto&& hook) {
+    const uint8_t* qt = tb + c * 32 * C::ROW_BYTES;
+    const uint8_t* dot = tb + C::TILE_BYTES + c * 32 * C::ROW_BYTES;
+    bf16x8 qx[PF + 1], ox[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      ox[i] = tr_read(dot, i / (D / 32), i % (D / 32));
+      qx[i] = tr_read(qt, i / (D / 32), i % (D / 32));
+    }
+#pragma unroll
+    for (int i = 0; i < NPAIR; ++i) {
+      if (i + PF < NPAIR) {
+        ox[(i + PF) % (PF + 1)] = tr_read(dot, (i + PF) / (D / 32), (i + PF) % (D / 32));
+        qx[(i + PF) % (PF + 1)] = tr_read(qt, (i + PF) / (D / 32), (i + PF) % (D / 32));
+      }
+      const int st = i / (D / 32), db = i % (D / 32);
+      dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ox[i % (PF + 1)], as_bf16x8(pb[st]), dvT[db], 0, 0, 0);
+      dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qx[i % (PF + 1)], as_bf16x8(dsb[st]), dkT[db], 0, 0, 0);
+      hook(i);
+    }
+  };
+  // masked tile (a wave-uniform test): rows that cannot see some key of this
+  // wave, or rows past N_q; their scores become -inf, so P and dS are 0
+  auto mask_block = [&](int t, int c, f32x16& s) {
+    int hs, row0;
+    tile_rows(t, hs, row0);
+    if ((p.causal && row0 + off < kw + 31) || row0 + BP > N_q) {
+      // element r holds query row row0 + c*32 + 8(r/4) + 4 half + r%4
+      const int lo_vis = my_key - off - row0 - c * 32 - 4 * half;  // visible: index >= lo_vis
+      const int hi_vis = N_q - row0 - c * 32 - 4 * half;           // and index < hi_vis
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int idx = 8 * (r >> 2) + (r & 3);
+        if ((p.causal && idx < lo_vis) || idx >= hi_vis) s[r] = -INFINITY;
+      }
+    }
+  };
+  // phase of block b: B(b-1) (HAS_PREV) with elements [0, EA) of E(b), then
+  // A(b+1) (HAS_NEXT) with the rest
+  auto phase = [&](auto has_prev_tag, auto has_next_tag, const uint8_t* tb_prev, const u32x4* pb_prev,
+                   const u32x4* ds_prev, const uint8_t* tb_cur, int c_cur, const f32x16& s_cur,
+                   const f32x16& dp_cur, u32x4* pb_cur, u32x4* ds_cur, const uint8_t* tb_next, int c_next,
+                   f32x16& s_next, f32x16& dp_next) {
+    constexpr bool HAS_PREV = decltype(has_prev_tag)::value;
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    constexpr int EA = HAS_PREV ? (HAS_NEXT ? NEL / 2 : NEL) : 0;
+    static_assert(EA % NPAIR == 0 && (NEL - EA) % NPAIR == 0, "whole elements per MFMA pair");
+    // this lane's rows' L2 and Dl (element r: row 8(r/4) + 4 half + r%4 of
+    // the block), read per half of the elements as they are needed
+    const float* stl = reinterpret_cast<const float*>(tb_cur + 2 * C::TILE_BYTES + wave * C::STAT_BYTES) +
+                       c_cur * 32 + 4 * half;
+    f32x4 l4[2], d4[2];
+    auto read_stats = [&](int h) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        l4[j] = *reinterpret_cast<const f32x4*>(stl + 8 * (2 * h + j));
+        d4[j] = *reinterpret_cast<const f32x4*>(stl + 64 + 8 * (2 * h + j));
+      }
+    };
+    // P and dS of elements r-1, r packed to bf16 pairs as soon as both exist
+    float pe_odd = 0.f, sf_odd = 0.f;
+    auto e_elem = [&](int r) {
+      if ((r & 7) == 0) read_stats(r >> 3);
+      const int j = (r >> 2) & 1;
+      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], sl2, -l4[j][r & 3]));
+      const float sv = pe * (dp_cur[r] - d4[j][r & 3]);
+      if ((r & 1) == 0) {
+        pe_odd = pe;
+        sf_odd = sv;
+      } else {
+        const f32x2 pp = {pe_odd, pe}, ss = {sf_odd, sv};
+        pb_cur[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, bf16x2));
+        ds_cur[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(ss, bf16x2));
+        // packed here, not carried as fp32 into the next phase
+        if ((r & 7) == 7) asm volatile("" : "+v"(pb_cur[r >> 3]), "+v"(ds_cur[r >> 3]));
+      }
+    };
+    if constexpr (HAS_PREV)
+      b_part(tb_prev, 1 - c_cur, pb_prev, ds_prev, [&](int i) {
+#pragma unroll
+        for (int e = 0; e < EA / NPAIR; ++e) e_elem(i * (EA / NPAIR) + e);
+      });
+    if constexpr (HAS_PREV && HAS_NEXT) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (HAS_NEXT)
+      a_part(tb_next, c_next, s_next, dp_next, [&](int i) {
+#pragma unroll
+        for (int e = 0; e < (NEL - EA) / NPAIR; ++e) e_elem(EA + i * ((NEL - EA) / NPAIR) + e);
+      });
+    if constexpr (!HAS_PREV && !HAS_NEXT) {
+#pragma unroll
+      for (int r = 0; r < NEL; ++r) e_elem(r);
+    }
+  };
+  auto no_hook = [](int) {};
 
-  // Load ring: the i-th tile of the range goes to slot i % P, issued P-1
-  // tiles ahead; past the range's end a clamped tile is re-loaded so every
-  // wait is one constant vmcnt.
+  // Load ring: the i-th tile of the range goes to slot i % P.  The phase of
+  // block 2i+1 opens with a barrier after which tile i+1 (read there by
+  // A(2i+2)) has landed and tile i-1 (last read by B(2i-1) in the phase
+  // before) is no longer read: tile i+P-1 is issued into its slot.  Past the
+  // range's end a clamped tile is re-loaded so every wait is one constant
+  // vmcnt.
+  static_assert(NBLK == 2 && P >= 3, "two 32-row blocks per tile; a ring of at least three tiles");
   const int n_mine = t_hi - t_lo;
   if (n_mine > 0) {
 #pragma unroll
     for (int j = 0; j < P - 1; ++j) issue(t_lo + min(j, n_mine - 1), j);
-    for (int i = 0; i < n_mine; ++i) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 2) * C::GROUP_LOADS) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 2) * C::GROUP_LOADS) : "memory");
+    __syncthreads();
+    f32x16 s0, dp0, s1, dp1;
+    u32x4 p0[2], d0[2], p1[2], d1[2];
+    // the phase of block 2i+1 (i < n_mine - 1) and its opening barrier
+    auto barrier_issue = [&](int i) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 3) * C::GROUP_LOADS) : "memory");
       __syncthreads();
       issue(t_lo + min(i + P - 1, n_mine - 1), (i + P - 1) % P);
-      compute(t_lo + i, i % P);
+    };
+    auto odd_phase = [&](int i) {
+      const uint8_t* tb = stage(i % P);
+      barrier_issue(i);
+      phase(BoolTag<true>{}, BoolTag<true>{}, tb, p0, d0, tb, 1, s1, dp1, p1, d1, stage((i + 1) % P), 0, s0, dp0);
+      mask_block(t_lo + i + 1, 0, s0);
+    };
+    // tile 0: A(0); block 0 (no B before it); block 1
+    a_part(stage(0), 0, s0, dp0, no_hook);
+    mask_block(t_lo, 0, s0);
+    phase(BoolTag<false>{}, BoolTag<true>{}, nullptr, nullptr, nullptr, stage(0), 0, s0, dp0, p0, d0, stage(0), 1, s1,
+          dp1);
+    mask_block(t_lo, 1, s1);
+    int i = 1;
+    if (n_mine > 1) {
+      odd_phase(0);
+      // steady state: tiles 1 .. n_mine - 2 (both blocks with a B before and an A after)
+      for (; i + 1 < n_mine; ++i) {
+        const uint8_t* tb = stage(i % P);
+        phase(BoolTag<true>{}, BoolTag<true>{}, stage((i + P - 1) % P), p1, d1, tb, 0, s0, dp0, p0, d0, tb, 1, s1,
+              dp1);
+        mask_block(t_lo + i, 1, s1);
+        odd_phase(i);
+      }
+      // last tile: block 0 as in the steady state
+      const uint8_t* tb = stage(i % P);
+      phase(BoolTag<true>{}, BoolTag<true>{}, stage((i + P - 1) % P), p1, d1, tb, 0, s0, dp0, p0, d0, tb, 1, s1, dp1);
+      mask_block(t_lo + i, 1, s1);
+    } else {
+      i = 0;
     }
+    // the last block: no A after it
+    barrier_issue(i);
+    phase(BoolTag<true>{}, BoolTag<false>{}, stage(i % P), p0, d0, stage(i % P), 1, s1, dp1, p1, d1, nullptr, 0, s0,
+          dp0);
+    b_part(stage((n_mine - 1) % P), 1, p1, d1, no_hook);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may outlive the workgroup
   }
 
-  // the last accumulation has landed before the AGPRs are read (the
-  // accumulators pass through the asm, so no read moves above it)
-  if constexpr (D == 128)
-    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(dkT[0]), "+a"(dkT[1]), "+a"(dkT[2]), "+a"(dkT[3]),
-                 "+a"(dvT[0]), "+a"(dvT[1]), "+a"(dvT[2]), "+a"(dvT[3]));
-  else
-    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(dkT[0]), "+a"(dkT[1]), "+a"(dvT[0]), "+a"(dvT[1]));
   // dK^T, dV^T: the lane holds key my_key, d = db*32 + 8(r/4) + 4 half + r%4.
   // A split writes its fp32 partial sums (a range with no tile writes zeros).
   if (p.n_kv_splits > 1) {
