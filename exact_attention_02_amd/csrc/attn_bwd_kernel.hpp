@@ -46,6 +46,15 @@ namespace ea02 {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+template <class T>
+struct IsSlotC {
+  static constexpr bool value = false;
+};
+template <int V>
+struct IsSlotC<SlotC<V>> {
+  static constexpr bool value = true;
+};
+
 struct BwdParams {
   const uint16_t* q;     // [B, H_q, N_q, D] bf16
   const uint16_t* k;     // [B, H_kv, N_kv, D]
@@ -196,13 +205,13 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
 
-  // Q, dO, L2 and Dl of the kv group's G heads: [G, N_q, ...] contiguous
+  // Q, dO, L2 and Dl of the kv group's G heads: [G, N_q, ...] contiguous.
+  // Each tile is read through buffer resources that start at its first row
+  // and end at the group's last row: the lane offsets are loop constants and
+  // rows past the end come back as zeros (rows past N_q of a head read the
+  // next head's rows; both kinds are masked).
   const size_t qg_rows = ((size_t)b * p.H_q + (size_t)g * G) * (size_t)N_q;
-  const u32x4 q_rsrc = make_rsrc(p.q + qg_rows * D, (uint32_t)((size_t)G * N_q * C::ROW_BYTES));
-  const u32x4 do_rsrc = make_rsrc(p.dout + qg_rows * D, (uint32_t)((size_t)G * N_q * C::ROW_BYTES));
-  const u32x4 l_rsrc = make_rsrc(p.lse2 + qg_rows, (uint32_t)((size_t)G * N_q * 4));
-  const u32x4 d_rsrc = make_rsrc(p.delta + qg_rows, (uint32_t)((size_t)G * N_q * 4));
-
+  const int group_rows = G * N_q;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
   const int ld_row_in = lane / C::DC;
   const int ld_chunk = lane % C::DC;
@@ -217,48 +226,33 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     row0 = r_start + (n_rt - 1 - g) * BP;
   };
   // one tile (Q, dO, and this wave's private copy of L2 and Dl) into stage slot
+  int ld_off[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int r = (wave * C::LPW + i) * C::RPL + ld_row_in;
+    ld_off[i] = r * C::ROW_BYTES + ((ld_chunk ^ bwd_swz<D>(r)) << 4);
+  }
+  const int st_off = min(lane, BP - 1) * 4;
   auto issue = [&](int t, int slot) {
     int hs, row0;
     tile_rows(t, hs, row0);
+    const int first = hs * N_q + row0;  // first row of the tile in the group
+    const size_t at = qg_rows + (size_t)first;
+    const uint32_t rows_left = (uint32_t)(group_rows - first);
+    const u32x4 q_rsrc = make_rsrc(p.q + at * D, rows_left * C::ROW_BYTES);
+    const u32x4 do_rsrc = make_rsrc(p.dout + at * D, rows_left * C::ROW_BYTES);
     const uint32_t st = lds_base + slot * C::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int li = wave * C::LPW + i;
-      const int r = li * C::RPL + ld_row_in;
-      const int row = min(row0 + r, N_q - 1);
-      const int byte = (hs * N_q + row) * C::ROW_BYTES + ((ld_chunk ^ bwd_swz<D>(r)) << 4);
-      dma_16B(q_rsrc, byte, st + li * 1024);
-      dma_16B(do_rsrc, byte, st + C::TILE_BYTES + li * 1024);
+      dma_16B(q_rsrc, ld_off[i], st + li * 1024);
+      dma_16B(do_rsrc, ld_off[i], st + C::TILE_BYTES + li * 1024);
     }
-    const int srow = min(row0 + min(lane, BP - 1), N_q - 1);
     const uint32_t sb = st + 2 * C::TILE_BYTES + wave * C::STAT_BYTES;
-    dma_4B(l_rsrc, (hs * N_q + srow) * 4, sb);
-    dma_4B(d_rsrc, (hs * N_q + srow) * 4, sb + 256);
+    dma_4B(make_rsrc(p.lse2 + at, rows_left * 4), st_off, sb);
+    dma_4B(make_rsrc(p.delta + at, rows_left * 4), st_off, sb + 256);
   };
 
-  // transpose-read offsets (tile-relative): rows 16 st + 4 half + L/4 (+8 for
-  // the second read), d = db*32 + 16 (G16 & 1) + 4 (L & 3); the swizzle of
-  // those rows does not depend on st
-  const int L16 = lane & 15;
-  int tr_off[2][D / 32];
-#pragma unroll
-  for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int row = 4 * half + (L16 >> 2) + 8 * hi;
-      const int d = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
-      tr_off[hi][db] = row * C::ROW_BYTES + (((d >> 3) ^ bwd_swz<D>(row)) << 4) + (d & 7) * 2;
-    }
-  auto tr_read = [&](const uint8_t* base, int st, int db) {
-    const uint8_t* a = base + (16 * st) * C::ROW_BYTES;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[0][db]));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[1][db]));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  auto row_read = [&](const uint8_t* base, int row, int chunk) {
-    return as_bf16x8(*reinterpret_cast<const u32x4*>(base + row * C::ROW_BYTES +
-                                                      ((chunk ^ bwd_swz<D>(row)) << 4)));
-  };
 
   f32x16 dkT[D / 32], dvT[D / 32];
 #pragma unroll
@@ -279,48 +273,100 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   // neighbours: with one wave per SIMD no other wave would hide it.  S and dP
   // of a block are held for one phase, P and dS for the next; even blocks use
   // the first set of registers, odd blocks the second.
-  auto stage = [&](int slot) { return lds + slot * C::STAGE_BYTES; };
   constexpr int PF = 3;          // LDS operand prefetch distance (MFMA pairs)
   constexpr int NPAIR = D / 16;  // MFMA pairs of A (k-steps) and of B ((st, db) pairs)
   constexpr int NEL = 16;        // elements of E per lane and block
   static_assert(NEL % NPAIR == 0, "elements spread evenly over the MFMA pairs");
-  auto a_part = [&](const uint8_t* tb, int c, f32x16& s, f32x16& dp, auto&& hook) {
-    const uint8_t* qt = tb;
-    const uint8_t* dot = tb + C::TILE_BYTES;
-    const int row = c * 32 + col;
+
+  // Per-lane LDS byte offsets of the operand reads: set 0 relative to stage
+  // 0, set 1 to stage 2 (kept opaque: two stages do not fit the 16-bit
+  // immediate of an LDS instruction).  The steady-state loop is unrolled by
+  // the ring depth, so a read knows its stage at compile time and takes the
+  // rest of its address (stage parity, block, step, tensor) as the immediate.
+  // Transpose reads: rows 16 st + 4 half + L/4 (+8 for the second read),
+  // d = db*32 + 16 (G16 & 1) + 4 (L & 3); the swizzle of those rows does not
+  // depend on st.  Row reads: 16-byte chunk 2 ks + half of row 32 c + col (the
+  // swizzle does not depend on c).  Row statistics: this wave's copy, rows
+  // 4 half .. of a block.
+  const int L16 = lane & 15;
+  int tr_off[2][2][D / 32], rr_off[2][NPAIR], stat_off[2];
+#pragma unroll
+  for (int set = 0; set < 2; ++set) {
+    const int base = set * 2 * C::STAGE_BYTES;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int row = 4 * half + (L16 >> 2) + 8 * hi;
+        const int d = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (L16 & 3);
+        const int o = row * C::ROW_BYTES + (((d >> 3) ^ bwd_swz<D>(row)) << 4) + (d & 7) * 2;
+        tr_off[set][hi][db] = set ? opaque_vgpr(base + o) : o;
+      }
+#pragma unroll
+    for (int ks = 0; ks < NPAIR; ++ks) {
+      const int o = col * C::ROW_BYTES + (((2 * ks + half) ^ bwd_swz<D>(col)) << 4);
+      rr_off[set][ks] = set ? opaque_vgpr(base + o) : o;
+    }
+    const int o = 2 * C::TILE_BYTES + wave * C::STAT_BYTES + 16 * half;
+    stat_off[set] = set ? opaque_vgpr(base + o) : o;
+  }
+  // offset set and immediate stage offset of a ring slot (SlotC: known at
+  // compile time; int: set 0 and a run-time offset)
+  auto sset = [&](auto slot) {
+    if constexpr (IsSlotC<decltype(slot)>::value) return decltype(slot)::value >> 1;
+    else return 0;
+  };
+  auto sbase = [&](auto slot) {
+    if constexpr (IsSlotC<decltype(slot)>::value) return (decltype(slot)::value & 1) * C::STAGE_BYTES;
+    else return int(slot) * C::STAGE_BYTES;
+  };
+  // rows c*32 .. of Q (tensor 0) or dO (tensor 1), transposed: the A operand
+  // of step st, d block db
+  auto tr_read = [&](auto slot, int tensor, int c, int st, int db) {
+    const int imm = sbase(slot) + tensor * C::TILE_BYTES + (c * 32 + 16 * st) * C::ROW_BYTES;
+    const uint8_t* a = lds + imm;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[sset(slot)][0][db]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + tr_off[sset(slot)][1][db]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // row c*32 + col of Q (tensor 0) or dO (tensor 1), chunk 2 ks + half
+  auto row_read = [&](auto slot, int tensor, int c, int ks) {
+    const int imm = sbase(slot) + tensor * C::TILE_BYTES + c * 32 * C::ROW_BYTES;
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(lds + imm + rr_off[sset(slot)][ks]));
+  };
+
+  auto a_part = [&](auto slot, int c, f32x16& s, f32x16& dp, auto&& hook) {
     s = f32x16{};
     dp = f32x16{};
     bf16x8 qx[PF + 1], ox[PF + 1];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      qx[i] = row_read(qt, row, 2 * i + half);
-      ox[i] = row_read(dot, row, 2 * i + half);
+      qx[i] = row_read(slot, 0, c, i);
+      ox[i] = row_read(slot, 1, c, i);
     }
 #pragma unroll
     for (int ks = 0; ks < NPAIR; ++ks) {
       if (ks + PF < NPAIR) {
-        qx[(ks + PF) % (PF + 1)] = row_read(qt, row, 2 * (ks + PF) + half);
-        ox[(ks + PF) % (PF + 1)] = row_read(dot, row, 2 * (ks + PF) + half);
+        qx[(ks + PF) % (PF + 1)] = row_read(slot, 0, c, ks + PF);
+        ox[(ks + PF) % (PF + 1)] = row_read(slot, 1, c, ks + PF);
       }
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qx[ks % (PF + 1)], kf[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ox[ks % (PF + 1)], vf[ks], dp, 0, 0, 0);
       hook(ks);
     }
   };
-  auto b_part = [&](const uint8_t* tb, int c, const u32x4* pb, const u32x4* dsb, auto&& hook) {
-    const uint8_t* qt = tb + c * 32 * C::ROW_BYTES;
-    const uint8_t* dot = tb + C::TILE_BYTES + c * 32 * C::ROW_BYTES;
+  auto b_part = [&](auto slot, int c, const u32x4* pb, const u32x4* dsb, auto&& hook) {
     bf16x8 qx[PF + 1], ox[PF + 1];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      ox[i] = tr_read(dot, i / (D / 32), i % (D / 32));
-      qx[i] = tr_read(qt, i / (D / 32), i % (D / 32));
+      ox[i] = tr_read(slot, 1, c, i / (D / 32), i % (D / 32));
+      qx[i] = tr_read(slot, 0, c, i / (D / 32), i % (D / 32));
     }
 #pragma unroll
     for (int i = 0; i < NPAIR; ++i) {
       if (i + PF < NPAIR) {
-        ox[(i + PF) % (PF + 1)] = tr_read(dot, (i + PF) / (D / 32), (i + PF) % (D / 32));
-        qx[(i + PF) % (PF + 1)] = tr_read(qt, (i + PF) / (D / 32), (i + PF) % (D / 32));
+        ox[(i + PF) % (PF + 1)] = tr_read(slot, 1, c, (i + PF) / (D / 32), (i + PF) % (D / 32));
+        qx[(i + PF) % (PF + 1)] = tr_read(slot, 0, c, (i + PF) / (D / 32), (i + PF) % (D / 32));
       }
       const int st = i / (D / 32), db = i % (D / 32);
       dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ox[i % (PF + 1)], as_bf16x8(pb[st]), dvT[db], 0, 0, 0);
@@ -346,24 +392,22 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   };
   // phase of block b: B(b-1) (HAS_PREV) with elements [0, EA) of E(b), then
   // A(b+1) (HAS_NEXT) with the rest
-  auto phase = [&](auto has_prev_tag, auto has_next_tag, const uint8_t* tb_prev, const u32x4* pb_prev,
-                   const u32x4* ds_prev, const uint8_t* tb_cur, int c_cur, const f32x16& s_cur,
-                   const f32x16& dp_cur, u32x4* pb_cur, u32x4* ds_cur, const uint8_t* tb_next, int c_next,
-                   f32x16& s_next, f32x16& dp_next) {
+  auto phase = [&](auto has_prev_tag, auto has_next_tag, auto slot_prev, const u32x4* pb_prev, const u32x4* ds_prev,
+                   auto slot_cur, int c_cur, const f32x16& s_cur, const f32x16& dp_cur, u32x4* pb_cur,
+                   u32x4* ds_cur, auto slot_next, int c_next, f32x16& s_next, f32x16& dp_next) {
     constexpr bool HAS_PREV = decltype(has_prev_tag)::value;
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     constexpr int EA = HAS_PREV ? (HAS_NEXT ? NEL / 2 : NEL) : 0;
     static_assert(EA % NPAIR == 0 && (NEL - EA) % NPAIR == 0, "whole elements per MFMA pair");
     // this lane's rows' L2 and Dl (element r: row 8(r/4) + 4 half + r%4 of
     // the block), read per half of the elements as they are needed
-    const float* stl = reinterpret_cast<const float*>(tb_cur + 2 * C::TILE_BYTES + wave * C::STAT_BYTES) +
-                       c_cur * 32 + 4 * half;
+    const uint8_t* stl = lds + sbase(slot_cur) + c_cur * 32 * 4 + stat_off[sset(slot_cur)];
     f32x4 l4[2], d4[2];
     auto read_stats = [&](int h) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        l4[j] = *reinterpret_cast<const f32x4*>(stl + 8 * (2 * h + j));
-        d4[j] = *reinterpret_cast<const f32x4*>(stl + 64 + 8 * (2 * h + j));
+        l4[j] = *reinterpret_cast<const f32x4*>(stl + 32 * (2 * h + j));
+        d4[j] = *reinterpret_cast<const f32x4*>(stl + 256 + 32 * (2 * h + j));
       }
     };
     // P and dS of elements r-1, r packed to bf16 pairs as soon as both exist
@@ -385,13 +429,13 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
       }
     };
     if constexpr (HAS_PREV)
-      b_part(tb_prev, 1 - c_cur, pb_prev, ds_prev, [&](int i) {
+      b_part(slot_prev, 1 - c_cur, pb_prev, ds_prev, [&](int i) {
 #pragma unroll
         for (int e = 0; e < EA / NPAIR; ++e) e_elem(i * (EA / NPAIR) + e);
       });
     if constexpr (HAS_PREV && HAS_NEXT) __builtin_amdgcn_sched_barrier(0);
     if constexpr (HAS_NEXT)
-      a_part(tb_next, c_next, s_next, dp_next, [&](int i) {
+      a_part(slot_next, c_next, s_next, dp_next, [&](int i) {
 #pragma unroll
         for (int e = 0; e < (NEL - EA) / NPAIR; ++e) e_elem(EA + i * ((NEL - EA) / NPAIR) + e);
       });
@@ -408,7 +452,7 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   // before) is no longer read: tile i+P-1 is issued into its slot.  Past the
   // range's end a clamped tile is re-loaded so every wait is one constant
   // vmcnt.
-  static_assert(NBLK == 2 && P >= 3, "two 32-row blocks per tile; a ring of at least three tiles");
+  static_assert(NBLK == 2 && P == 4, "two 32-row blocks per tile; a ring of four tiles");
   const int n_mine = t_hi - t_lo;
   if (n_mine > 0) {
 #pragma unroll
@@ -417,47 +461,51 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     __syncthreads();
     f32x16 s0, dp0, s1, dp1;
     u32x4 p0[2], d0[2], p1[2], d1[2];
-    // the phase of block 2i+1 (i < n_mine - 1) and its opening barrier
     auto barrier_issue = [&](int i) {
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 3) * C::GROUP_LOADS) : "memory");
       __syncthreads();
       issue(t_lo + min(i + P - 1, n_mine - 1), (i + P - 1) % P);
     };
-    auto odd_phase = [&](int i) {
-      const uint8_t* tb = stage(i % P);
+    // both blocks of tile i (0 < i < n_mine - 1), in slot sc; tile i-1 in
+    // slot sp, tile i+1 in slot sn
+    auto steady_tile = [&](int i, auto sp, auto sc, auto sn) {
+      phase(BoolTag<true>{}, BoolTag<true>{}, sp, p1, d1, sc, 0, s0, dp0, p0, d0, sc, 1, s1, dp1);
+      mask_block(t_lo + i, 1, s1);
       barrier_issue(i);
-      phase(BoolTag<true>{}, BoolTag<true>{}, tb, p0, d0, tb, 1, s1, dp1, p1, d1, stage((i + 1) % P), 0, s0, dp0);
+      phase(BoolTag<true>{}, BoolTag<true>{}, sc, p0, d0, sc, 1, s1, dp1, p1, d1, sn, 0, s0, dp0);
       mask_block(t_lo + i + 1, 0, s0);
     };
     // tile 0: A(0); block 0 (no B before it); block 1
-    a_part(stage(0), 0, s0, dp0, no_hook);
+    a_part(SlotC<0>{}, 0, s0, dp0, no_hook);
     mask_block(t_lo, 0, s0);
-    phase(BoolTag<false>{}, BoolTag<true>{}, nullptr, nullptr, nullptr, stage(0), 0, s0, dp0, p0, d0, stage(0), 1, s1,
-          dp1);
+    phase(BoolTag<false>{}, BoolTag<true>{}, SlotC<0>{}, nullptr, nullptr, SlotC<0>{}, 0, s0, dp0, p0, d0, SlotC<0>{},
+          1, s1, dp1);
     mask_block(t_lo, 1, s1);
     int i = 1;
     if (n_mine > 1) {
-      odd_phase(0);
-      // steady state: tiles 1 .. n_mine - 2 (both blocks with a B before and an A after)
-      for (; i + 1 < n_mine; ++i) {
-        const uint8_t* tb = stage(i % P);
-        phase(BoolTag<true>{}, BoolTag<true>{}, stage((i + P - 1) % P), p1, d1, tb, 0, s0, dp0, p0, d0, tb, 1, s1,
-              dp1);
-        mask_block(t_lo + i, 1, s1);
-        odd_phase(i);
+      barrier_issue(0);
+      phase(BoolTag<true>{}, BoolTag<true>{}, SlotC<0>{}, p0, d0, SlotC<0>{}, 1, s1, dp1, p1, d1, SlotC<1>{}, 0, s0,
+            dp0);
+      mask_block(t_lo + 1, 0, s0);
+      // steady state from tile 1, unrolled by the ring depth: tile i = 1 mod 4
+      // sits in slot 1, and every operand read takes its slot as an immediate
+      for (; i + 4 < n_mine; i += 4) {
+        steady_tile(i, SlotC<0>{}, SlotC<1>{}, SlotC<2>{});
+        steady_tile(i + 1, SlotC<1>{}, SlotC<2>{}, SlotC<3>{});
+        steady_tile(i + 2, SlotC<2>{}, SlotC<3>{}, SlotC<0>{});
+        steady_tile(i + 3, SlotC<3>{}, SlotC<0>{}, SlotC<1>{});
       }
+      for (; i + 1 < n_mine; ++i) steady_tile(i, (i + P - 1) % P, i % P, (i + 1) % P);
       // last tile: block 0 as in the steady state
-      const uint8_t* tb = stage(i % P);
-      phase(BoolTag<true>{}, BoolTag<true>{}, stage((i + P - 1) % P), p1, d1, tb, 0, s0, dp0, p0, d0, tb, 1, s1, dp1);
+      phase(BoolTag<true>{}, BoolTag<true>{}, (i + P - 1) % P, p1, d1, i % P, 0, s0, dp0, p0, d0, i % P, 1, s1, dp1);
       mask_block(t_lo + i, 1, s1);
     } else {
       i = 0;
     }
     // the last block: no A after it
     barrier_issue(i);
-    phase(BoolTag<true>{}, BoolTag<false>{}, stage(i % P), p0, d0, stage(i % P), 1, s1, dp1, p1, d1, nullptr, 0, s0,
-          dp0);
-    b_part(stage((n_mine - 1) % P), 1, p1, d1, no_hook);
+    phase(BoolTag<true>{}, BoolTag<false>{}, i % P, p0, d0, i % P, 1, s1, dp1, p1, d1, 0, 0, s0, dp0);
+    b_part(i % P, 1, p1, d1, no_hook);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may outlive the workgroup
   }
 
@@ -628,22 +676,30 @@ void attn_bwd_dq_kernel(BwdParams p) {
     dl[qc] = p.delta[bhr];
   }
 
+  // each K/V tile through buffer resources that start at its first key and
+  // end at the head's last key: lane offsets are loop constants and keys past
+  // the end come back as zeros (masked)
   const size_t kv_base = ((size_t)b * p.H_kv + g) * (size_t)N_kv * D;
-  const uint32_t head_bytes = (uint32_t)N_kv * C::ROW_BYTES;
-  const u32x4 k_rsrc = make_rsrc(p.k + kv_base, head_bytes);
-  const u32x4 v_rsrc = make_rsrc(p.v + kv_base, head_bytes);
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
   const int ld_row_in = lane / C::DC;
   const int ld_chunk = lane % C::DC;
+  int ld_off[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int r = (wave * C::LPW + i) * C::RPL + ld_row_in;
+    ld_off[i] = r * C::ROW_BYTES + ((ld_chunk ^ dq_swz<D, MN>(r)) << 4);
+  }
   auto issue = [&](int t, int slot) {
+    const size_t at = kv_base + (size_t)t * BN * D;
+    const uint32_t bytes_left = (uint32_t)(N_kv - t * BN) * C::ROW_BYTES;
+    const u32x4 k_rsrc = make_rsrc(p.k + at, bytes_left);
+    const u32x4 v_rsrc = make_rsrc(p.v + at, bytes_left);
     const uint32_t st = lds_base + slot * C::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int li = wave * C::LPW + i;
-      const int r = li * C::RPL + ld_row_in;
-      const int byte = min(t * BN + r, N_kv - 1) * C::ROW_BYTES + ((ld_chunk ^ dq_swz<D, MN>(r)) << 4);
-      dma_16B(k_rsrc, byte, st + li * 1024);
-      dma_16B(v_rsrc, byte, st + C::TILE_BYTES + li * 1024);
+      dma_16B(k_rsrc, ld_off[i], st + li * 1024);
+      dma_16B(v_rsrc, ld_off[i], st + C::TILE_BYTES + li * 1024);
     }
   };
 

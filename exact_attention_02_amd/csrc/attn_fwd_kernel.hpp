@@ -227,9 +227,15 @@ struct Cfg {
 // 4 adjacent chunks (MN = 32) or 8 rows x 2 adjacent chunks (MN = 16) of
 // aligned rows.  For MN = 16 one swizzle serves both (its bits 1.. take 8
 // values over 8 aligned rows), so a K load and a V load share an offset.
+// At D = 128 rows r and r + 8 also take chunk indices that differ in more
+// than bit 0 (the second half of the rows runs the first half's pattern
+// reversed): with the plain 2 (r & 7) + (r >> 3) the 128-bit row reads of
+// the K tile took two passes each on gfx950 (SQ_LDS_BANK_CONFLICT: 4 cycles
+// per read), with this one they take none; the transpose reads stay free of
+// conflicts either way.
 template <int D>
 __device__ __forceinline__ int kv16_swz(int row) {
-  if constexpr (D == 128) return 2 * (row & 7) + ((row >> 3) & 1);
+  if constexpr (D == 128) return (2 * (row & 7) ^ (14 * ((row >> 3) & 1))) | ((row >> 3) & 1);
   else return 2 * ((row >> 1) & 3) + ((row >> 3) & 1);
 }
 template <int D, int MN>
