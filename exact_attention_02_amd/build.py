@@ -27,13 +27,11 @@ HIPCC_FLAGS = [
     # no packed-fp32 VALU instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# Per-source flags.  The backward's score MFMAs (S, dP) return their results
-# in VGPRs, where the softmax reads them; its dK/dV accumulators are pinned to
-# AGPRs in the source.  Without this the compiler gives every MFMA of the file
-# AGPR results and copies S and dP back on every tile.  (The same treatment of
-# the MLA core removes its copies too but measured slower: that kernel is
-# bound by latency, not issue.)
-SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source flags (none at present).  The backward was built with
+# -mllvm -amdgpu-mfma-vgpr-form while its dK/dV accumulators were inline-asm
+# MFMAs on AGPRs; with every MFMA a builtin, the compiler's own placement
+# (accumulators in AGPRs) measured faster than that flag's VGPR form.
+SOURCE_FLAGS: dict = {}
 
 
 def hipcc() -> str:
