@@ -1,8 +1,9 @@
 // C ABI of the fused attention forward (declared in include/attn.h):
 // argument validation, kernel-shape and split choice, and kernel launches.
-// The library allocates nothing and never synchronises; its only state is
-// the static scratch of attn_fwd_splitkv_static and that scratch's address
-// per device.
+// The library allocates nothing and never synchronises.  Its only state is in
+// two file-scope device arrays (the static scratch of attn_fwd_splitkv_static
+// and the work-stealing counters, which every launch leaves at zero) and, on
+// the host, their addresses per device and the counter slot of each stream.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -39,6 +40,7 @@ constexpr int kMidNW = 4, kMidP = 2, kMidBN = 64, kMidMN = 32;
 constexpr int kNarrowNW = 1, kNarrowP = 2, kNarrowBN = 32, kNarrowMN = 32;
 constexpr int kNarrowPairs = 64;
 constexpr int kMaxSplits = 256;
+constexpr int kMaxDevices = 64;
 
 
 enum class Kind { kWide, kMid, kNarrow };
@@ -192,6 +194,84 @@ int64_t choose_splits(const Problem& a) {
   return splits_for(sh, ((n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg) * a.B * a.H_kv, a.N_kv);
 }
 
+}  // namespace
+
+// ---- counters of the work stealing between XCDs (claim_item): one slot of 16
+// ints per (device, stream), in this file-scope device array (one copy per
+// GPU).  Launches on one stream run one after another, and each leaves its
+// slot at zero, so a slot serves every launch of its stream.  As with the
+// static scratch, host code only uses the address that hipGetSymbolAddress
+// returns for the current device.
+static constexpr int kStealSlots = 256;
+static constexpr int kStealSlotInts = 16;
+static __device__ __attribute__((aligned(256))) int steal_counters[kStealSlots * kStealSlotInts];
+
+namespace {
+
+// The eight-wave single pass steals work when its grid covers at least this
+// many rounds of the device (shorter launches measured no gain); it keeps the
+// first 70 % of each XCD's list static and launches up to 10 % more
+// workgroups per list for the fast XCDs to claim with.
+constexpr int64_t kStealMinRounds = 8;
+constexpr int64_t kStealStaticPct = 70;
+constexpr int64_t kStealSparePct = 10;
+
+struct StealSlots {
+  int* base = nullptr;
+  int used = 0;
+  hipStream_t stream[kStealSlots];
+  bool zeroed[kStealSlots];
+};
+std::mutex g_steal_mu;
+StealSlots g_steal[kMaxDevices];
+
+// Counter slot of `stream` on the current device, or nullptr for the static
+// order: under graph capture (a replay may overlap later launches on the
+// stream), for hipStreamPerThread (one handle for many streams), when the
+// device's slots are taken, or when a runtime call fails.  A new slot is
+// zeroed on the stream before its first launch.
+int* steal_slot(hipStream_t stream) {
+  if (stream == hipStreamPerThread) return nullptr;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+    (void)hipGetLastError();  // the query's error is not the launch's
+    return nullptr;
+  }
+  if (cap != hipStreamCaptureStatusNone) return nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_steal_mu);
+  StealSlots& d = g_steal[dev];
+  if (!d.base) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(steal_counters)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    d.base = static_cast<int*>(ptr);
+  }
+  int i = 0;
+  while (i < d.used && d.stream[i] != stream) ++i;
+  if (i == d.used) {
+    if (d.used == kStealSlots) return nullptr;
+    d.stream[i] = stream;
+    d.zeroed[i] = false;
+    ++d.used;
+  }
+  int* slot = d.base + i * kStealSlotInts;
+  if (!d.zeroed[i]) {
+    if (hipMemsetAsync(slot, 0, kStealSlotInts * sizeof(int), stream) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    d.zeroed[i] = true;
+  }
+  return slot;
+}
+
 // Launch after every check passed: one pass when n_splits <= 1, else the split
 // pass into the workspace followed by the merge.
 int run(const Problem& a, int64_t n_splits, void* ws, void* stream) {
@@ -230,7 +310,18 @@ int run(const Problem& a, int64_t n_splits, void* ws, void* stream) {
   p.causal = a.is_causal;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int g32 = static_cast<int>(grid);
+  p.steal = nullptr;
+  p.n_items = static_cast<int>(grid);
+  p.n_static = static_cast<int>(grid);
+  int64_t launch_grid = grid;
+  if (!split && sh.kind == Kind::kWide && grid >= kStealMinRounds * device_cus() && grid < (int64_t(1) << 30)) {
+    if (int* slot = steal_slot(s)) {
+      p.steal = slot;
+      p.n_static = static_cast<int>(8 * (grid / 8 * kStealStaticPct / 100));
+      launch_grid = grid + 8 * ((grid / 8 * kStealSparePct + 99) / 100);
+    }
+  }
+  const int g32 = static_cast<int>(launch_grid);
   hipError_t err;
   if (!split)
     err = (a.D == 128) ? launch_fwd<128, false>(sh.kind, p, g32, s) : launch_fwd<64, false>(sh.kind, p, g32, s);
@@ -308,7 +399,6 @@ static __device__ __attribute__((aligned(256))) uint8_t scratch[kStaticScratchBy
 
 namespace {
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 

@@ -99,7 +99,69 @@ struct FwdParams {
                       // a masked score (-inf) never meets a zero factor
   uint32_t q_sign;    // 0x80008000 when sm_scale < 0 (Q is negated on load), else 0
   int causal;
+  // Work stealing between the XCDs (eight-wave single pass; claim_item).
+  int* steal;         // nine claim counters, zero on entry and on exit; null: static order
+  int n_items;        // workgroups of the static order (the grid may hold more)
+  int n_static;       // workgroups below this index take their own item (a multiple of 8)
 };
+
+// Work stealing.  The hardware hands workgroup i to XCD i mod 8, so in the
+// static order XCD x runs items x, x + 8, x + 16, ... (list x, heaviest
+// first), and the slowest XCD sets the launch time.  With counters, the
+// workgroups from n_static on claim instead: first the next item of their own
+// list (steal[x] counts the claims on list x past its static part), else one
+// from the list with the most items left.  The grid holds spare workgroups
+// for the fast XCDs; a workgroup that finds every list empty does nothing.
+// steal[8] counts finished claims, and the last claimer zeroes all nine
+// counters, so they are zero again for the next launch on the stream.  Each
+// item is computed the same way whoever runs it, so the results do not depend
+// on the schedule.
+__device__ __forceinline__ int steal_list_len(int n_items, int x) { return (n_items - x + 7) >> 3; }
+
+// Called by all lanes of one wave; returns the claimed item or -1 (uniform).
+__device__ __forceinline__ int claim_item(const FwdParams& p, int lane) {
+  typedef __attribute__((address_space(1))) int global_int;
+  global_int* ctr = (global_int*)p.steal;  // a global-memory pointer (global, not flat, atomics)
+  const int n = p.n_items, own = blockIdx.x & 7, j0 = p.n_static >> 3;
+  int item = -1;
+  if (lane == 0) {
+    const int k = __hip_atomic_fetch_add(ctr + own, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (j0 + k < steal_list_len(n, own)) item = 8 * (j0 + k) + own;
+  }
+  item = __shfl(item, 0);
+  // A list that looks empty is empty: the counters only grow, so a load can
+  // only under-report a claim.  Each failed claim empties its list for good,
+  // so eight rounds suffice.
+  for (int round = 0; round < 8 && item < 0; ++round) {
+    int left = -1, list = lane;
+    if (lane < 8)
+      left = steal_list_len(n, lane) - j0 - __hip_atomic_load(ctr + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const int ol = __shfl_xor(left, o), oi = __shfl_xor(list, o);
+      if (ol > left || (ol == left && oi < list)) {
+        left = ol;
+        list = oi;
+      }
+    }
+    left = __shfl(left, 0);
+    list = __shfl(list, 0);
+    if (left <= 0) break;
+    if (lane == 0) {
+      const int k = __hip_atomic_fetch_add(ctr + list, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (j0 + k < steal_list_len(n, list)) item = 8 * (j0 + k) + list;
+    }
+    item = __shfl(item, 0);
+  }
+  if (lane == 0) {
+    // every claim of this workgroup has completed before it counts as done
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int done = __hip_atomic_fetch_add(ctr + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (int)gridDim.x - p.n_static - 1)
+      for (int c = 0; c < 9; ++c) __hip_atomic_exchange(ctr + c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return item;
+}
 
 template <bool V>
 struct BoolTag {
@@ -285,8 +347,21 @@ void attn_fwd_kernel(FwdParams p) {
   const int col = lane % MN;
 
   // ---- work decomposition: heaviest pair blocks first (causal), then the
-  //      key splits, kv heads fastest
-  const int bid = blockIdx.x;
+  //      key splits, kv heads fastest.  Item bid of that order; the
+  //      eight-wave single pass may claim it instead (claim_item).
+  int bid = blockIdx.x;
+  if constexpr (!SPLIT && NW == 8) {
+    if (p.steal != nullptr && bid >= p.n_static) {
+      __shared__ int claimed;
+      if (wave == 0) {
+        const int item = claim_item(p, lane);
+        if (lane == 0) claimed = item;
+      }
+      __syncthreads();
+      bid = __builtin_amdgcn_readfirstlane(claimed);
+      if (bid < 0) return;
+    }
+  }
   const int head_wg = bid % p.n_heads_wg;
   const int rest = bid / p.n_heads_wg;
   const int split = SPLIT ? rest % p.n_splits : 0;

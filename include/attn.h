@@ -13,8 +13,18 @@
  * (Causal, GQA, MQA); page "Flash Attention 与 Kernel 优化", sections
  * "对外接口", "causal mask" and "输出与保存状态" (log-sum-exp output).
  *
- * Link with libea02_attn.so.  All functions are thread-safe; the library
- * keeps no state between calls and never allocates device memory.
+ * Link with libea02_attn.so.  All functions are thread-safe and the library
+ * never allocates device memory.  Results never depend on earlier calls.  The
+ * only state a call leaves is host bookkeeping: long single-pass forwards
+ * (eight-wave launches of at least eight rounds of the device) balance their
+ * work between the XCDs through a few claim counters per (device, stream) in
+ * a static device array, which every launch returns to zero.  Up to 256
+ * streams per device get such a slot; calls on further streams, on
+ * hipStreamPerThread or under graph capture use the static work order, with
+ * bit-identical results.  The first such call on a stream also enqueues a
+ * 64-byte clear of its slot.  A slot belongs to a stream handle: a stream
+ * created with the handle of a destroyed one must not start a forward while
+ * the destroyed stream's forward still runs.
  * Kernel shapes (not part of the contract): kv heads with more than 64
  * (query row, query head) pairs run on eight-wave workgroups with 64-key
  * tiles, or on four-wave ones when that grid is small (uneven causal rows

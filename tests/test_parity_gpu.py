@@ -446,6 +446,60 @@ def test_concurrent_host_threads(ea):
             assert torch.equal(o.view(torch.int16), ro.view(torch.int16)) and torch.equal(l, rl)
 
 
+def test_work_stealing_schedule(ea):
+    """A long single pass (causal GQA-4, N = 16384: eight rounds of the
+    device) lets the XCDs claim work through per-stream counters; captured
+    into a graph it runs the static work order.  Every schedule gives the
+    same bits: repeated calls on one stream (each launch must leave its
+    counters at zero for the next), two streams running at once (separate
+    counters), and graph replays interleaved with eager calls."""
+    dev = torch.device("cuda", 0)
+    w = workloads.WORKLOADS["gqa4_n16384_causal"]
+    print(f"[steal] {w.name}", flush=True)
+    q, k, v = (x.to(dev) for x in workloads.workload_inputs(w))
+
+    def bufs():
+        return (torch.full(w.q_shape(), float("nan"), dtype=torch.bfloat16, device=dev),
+                torch.full((w.B, w.H_q, w.Nq), float("nan"), dtype=torch.float32, device=dev))
+
+    def same(a, b):
+        return torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+
+    ref = bufs()
+    ea.attn_fwd(q, k, v, *ref, is_causal=True, sm_scale=w.sm_scale)
+    for _ in range(3):
+        o = bufs()
+        ea.attn_fwd(q, k, v, *o, is_causal=True, sm_scale=w.sm_scale)
+        torch.cuda.synchronize()
+        assert same(o, ref), "repeated call on one stream differs"
+    assert bool(torch.isfinite(ref[0]).all()) and bool(torch.isfinite(ref[1]).all())
+
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs = [bufs() for _ in streams]
+    torch.cuda.synchronize()
+    for it in range(3):
+        for s, o in zip(streams, outs):
+            with torch.cuda.stream(s):
+                ea.attn_fwd(q, k, v, *o, is_causal=True, sm_scale=w.sm_scale)
+        torch.cuda.synchronize()
+        for o in outs:
+            assert same(o, ref), f"concurrent streams, round {it}: result differs"
+
+    g_out = bufs()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ea.attn_fwd(q, k, v, *g_out, is_causal=True, sm_scale=w.sm_scale)
+    for it in range(3):
+        g_out[0].fill_(float("nan"))
+        g_out[1].fill_(float("nan"))
+        graph.replay()
+        o = bufs()
+        ea.attn_fwd(q, k, v, *o, is_causal=True, sm_scale=w.sm_scale)
+        torch.cuda.synchronize()
+        assert same(g_out, ref), f"graph replay {it} (static order) differs"
+        assert same(o, ref), f"eager call after replay {it} differs"
+
+
 def test_status_error_raises(ea):
     dev = torch.device("cuda", 0)
     q = torch.zeros((1, 4, 16, 96), dtype=torch.bfloat16, device=dev)
