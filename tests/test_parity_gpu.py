@@ -8,6 +8,7 @@ and |LSE - LSE_ref| <= 1e-3; no NaN or Inf anywhere.
 """
 from __future__ import annotations
 
+import dataclasses
 import json
 import math
 import os
@@ -410,7 +411,7 @@ def test_side_stream(ea):
 def test_concurrent_host_threads(ea):
     """Two host threads enqueue forwards (single pass and key splits) on
     their own streams at the same time; every result equals, bit for bit,
-    the same call made alone.  The library keeps no state between calls."""
+    the same call made alone: no result depends on another call."""
     import threading
     dev = torch.device("cuda", 0)
     cases = []
@@ -446,17 +447,23 @@ def test_concurrent_host_threads(ea):
             assert torch.equal(o.view(torch.int16), ro.view(torch.int16)) and torch.equal(l, rl)
 
 
-def test_work_stealing_schedule(ea):
-    """A long single pass (causal GQA-4, N = 16384: eight rounds of the
-    device) lets the XCDs claim work through per-stream counters; captured
+@pytest.mark.parametrize("D", [128, 64])
+def test_work_stealing_schedule(ea, D):
+    """A long single pass (causal GQA-4, N = 16384, D = 128 and 64: eight
+    rounds of the device) lets the XCDs claim work through per-stream counters; captured
     into a graph it runs the static work order.  Every schedule gives the
     same bits: repeated calls on one stream (each launch must leave its
     counters at zero for the next), two streams running at once (separate
-    counters), and graph replays interleaved with eager calls."""
+    counters), the per-thread default stream and graph replays interleaved
+    with eager calls (both in the static order)."""
     dev = torch.device("cuda", 0)
     w = workloads.WORKLOADS["gqa4_n16384_causal"]
-    print(f"[steal] {w.name}", flush=True)
-    q, k, v = (x.to(dev) for x in workloads.workload_inputs(w))
+    print(f"[steal] {w.name} D={D}", flush=True)
+    if D == 128:
+        q, k, v = (x.to(dev) for x in workloads.workload_inputs(w))
+    else:
+        w = dataclasses.replace(w, D=64)
+        q, k, v = (x.to(dev) for x in workloads.make_inputs(w.B, w.H_q, w.H_kv, w.N, 64, seed=w.seed + 64))
 
     def bufs():
         return (torch.full(w.q_shape(), float("nan"), dtype=torch.bfloat16, device=dev),
@@ -484,6 +491,14 @@ def test_work_stealing_schedule(ea):
         torch.cuda.synchronize()
         for o in outs:
             assert same(o, ref), f"concurrent streams, round {it}: result differs"
+
+    # hipStreamPerThread (handle 2) names a different stream in every thread:
+    # the static order
+    o = bufs()
+    torch.cuda.synchronize()
+    ea.attn_fwd(q, k, v, *o, is_causal=True, sm_scale=w.sm_scale, stream=2)
+    torch.cuda.synchronize()
+    assert same(o, ref), "per-thread default stream differs"
 
     g_out = bufs()
     graph = torch.cuda.CUDAGraph()
