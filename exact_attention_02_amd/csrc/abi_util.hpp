@@ -28,5 +28,21 @@ inline int device_cus() {
   return cus;
 }
 
+// Work stealing between the XCDs (work_item in attn_fwd_kernel.hpp).  The
+// claim counters of `stream` on the current device (a slot of a static
+// device array, zero between launches), or nullptr when the launch must keep
+// the static order (graph capture, hipStreamPerThread, no free slot).
+int* steal_slot(hipStream_t stream);
+
+// How a launch of `items` workgroups (wg_per_cu of them fit on a CU) runs:
+// counters (nullptr: static order), the workgroups that keep their own item,
+// and the grid to launch (items plus spare workgroups for the fast XCDs).
+struct StealPlan {
+  int* counters;
+  int n_static;
+  int64_t launch_grid;
+};
+StealPlan plan_steal(hipStream_t stream, int64_t items, int64_t wg_per_cu);
+
 }  // namespace abi
 }  // namespace ea02

@@ -196,22 +196,22 @@ int64_t choose_splits(const Problem& a) {
 
 }  // namespace
 
-// ---- counters of the work stealing between XCDs (claim_item): one slot of 16
-// ints per (device, stream), in this file-scope device array (one copy per
+// ---- counters of the work stealing between XCDs (work_item): one slot of
+// 16 ints per (device, stream), in this file-scope device array (one copy per
 // GPU).  Launches on one stream run one after another, and each leaves its
-// slot at zero, so a slot serves every launch of its stream.  As with the
-// static scratch, host code only uses the address that hipGetSymbolAddress
-// returns for the current device.
+// slot at zero, so a slot serves every launch of its stream (forward and
+// backward kernels alike).  As with the static scratch, host code only uses
+// the address that hipGetSymbolAddress returns for the current device.
 static constexpr int kStealSlots = 256;
 static constexpr int kStealSlotInts = 16;
 static __device__ __attribute__((aligned(256))) int steal_counters[kStealSlots * kStealSlotInts];
 
 namespace {
 
-// The eight-wave single pass steals work when its grid covers at least this
-// many rounds of the device (shorter launches measured no gain); it keeps the
-// first 70 % of each XCD's list static and launches up to 10 % more
-// workgroups per list for the fast XCDs to claim with.
+// A launch steals work when its grid covers at least this many rounds of the
+// device (shorter launches measured no gain); it keeps the first 70 % of each
+// XCD's list static and launches up to 10 % more workgroups per list for the
+// fast XCDs to claim with.
 constexpr int64_t kStealMinRounds = 8;
 constexpr int64_t kStealStaticPct = 70;
 constexpr int64_t kStealSparePct = 10;
@@ -225,11 +225,11 @@ struct StealSlots {
 std::mutex g_steal_mu;
 StealSlots g_steal[kMaxDevices];
 
-// Counter slot of `stream` on the current device, or nullptr for the static
-// order: under graph capture (a replay may overlap later launches on the
-// stream), for hipStreamPerThread (one handle for many streams), when the
-// device's slots are taken, or when a runtime call fails.  A new slot is
-// zeroed on the stream before its first launch.
+}  // namespace
+
+namespace ea02 {
+namespace abi {
+
 int* steal_slot(hipStream_t stream) {
   if (stream == hipStreamPerThread) return nullptr;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -272,6 +272,25 @@ int* steal_slot(hipStream_t stream) {
   return slot;
 }
 
+StealPlan plan_steal(hipStream_t stream, int64_t items, int64_t wg_per_cu) {
+  StealPlan plan{nullptr, static_cast<int>(items), items};
+  if (items < kStealMinRounds * wg_per_cu * device_cus() || items >= (int64_t(1) << 30)) return plan;
+  int* slot = steal_slot(stream);
+  if (!slot) return plan;
+  plan.counters = slot;
+  plan.n_static = static_cast<int>(8 * (items / 8 * kStealStaticPct / 100));
+  plan.launch_grid = items + 8 * ((items / 8 * kStealSparePct + 99) / 100);
+  return plan;
+}
+
+}  // namespace abi
+}  // namespace ea02
+
+namespace {
+
+using ea02::abi::plan_steal;
+using ea02::abi::StealPlan;
+
 // Launch after every check passed: one pass when n_splits <= 1, else the split
 // pass into the workspace followed by the merge.
 int run(const Problem& a, int64_t n_splits, void* ws, void* stream) {
@@ -310,18 +329,13 @@ int run(const Problem& a, int64_t n_splits, void* ws, void* stream) {
   p.causal = a.is_causal;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  p.steal = nullptr;
+  // the eight-wave single pass balances the XCDs (work_item)
+  const StealPlan plan = (!split && sh.kind == Kind::kWide) ? plan_steal(s, grid, sh.wg_per_cu)
+                                                           : StealPlan{nullptr, static_cast<int>(grid), grid};
+  p.steal = plan.counters;
   p.n_items = static_cast<int>(grid);
-  p.n_static = static_cast<int>(grid);
-  int64_t launch_grid = grid;
-  if (!split && sh.kind == Kind::kWide && grid >= kStealMinRounds * device_cus() && grid < (int64_t(1) << 30)) {
-    if (int* slot = steal_slot(s)) {
-      p.steal = slot;
-      p.n_static = static_cast<int>(8 * (grid / 8 * kStealStaticPct / 100));
-      launch_grid = grid + 8 * ((grid / 8 * kStealSparePct + 99) / 100);
-    }
-  }
-  const int g32 = static_cast<int>(launch_grid);
+  p.n_static = plan.n_static;
+  const int g32 = static_cast<int>(plan.launch_grid);
   hipError_t err;
   if (!split)
     err = (a.D == 128) ? launch_fwd<128, false>(sh.kind, p, g32, s) : launch_fwd<64, false>(sh.kind, p, g32, s);

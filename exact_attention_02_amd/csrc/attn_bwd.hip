@@ -194,16 +194,29 @@ size_t workspace_layout(const Shape& a, int64_t n_kv, int64_t n_q, size_t* kv_of
 // Prep, dK/dV (+ the sum of its splits), dQ.  With no query rows only the
 // dK/dV kernel runs: every key block then has no row tile and writes zeros.
 template <int D>
-hipError_t launch_all(const BwdParams& p, int q_nw, hipStream_t s) {
+hipError_t launch_all(const BwdParams& p_in, int q_nw, hipStream_t s) {
   hipError_t e;
+  // Both kernels balance the XCDs by work stealing when their grids are long
+  // enough (work_item); they run one after the other on the stream and share
+  // its counters.
+  BwdParams p = p_in;
+  const int64_t kv_items = int64_t(p.n_heads_wg) * p.n_key_blocks * p.n_kv_splits;
+  const int64_t q_items = int64_t(p.n_heads_wg) * p.n_pair_blocks * p.n_q_splits;
+  const ea02::abi::StealPlan kv_plan = ea02::abi::plan_steal(s, kv_items, 1);
+  const ea02::abi::StealPlan q_plan = p.rows > 0 ? ea02::abi::plan_steal(s, q_items, q_nw == kQMidNW ? 2 : 1)
+                                                 : ea02::abi::StealPlan{nullptr, static_cast<int>(q_items), q_items};
+  p.steal = kv_plan.counters ? kv_plan.counters : q_plan.counters;
+  p.kv_items = static_cast<int>(kv_items);
+  p.kv_static = kv_plan.n_static;
+  p.q_items = static_cast<int>(q_items);
+  p.q_static = q_plan.n_static;
   if (p.rows > 0) {
     const int64_t prep_blocks = (p.rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
     hipLaunchKernelGGL((ea02::attn_bwd_prep_kernel<D>), dim3(static_cast<unsigned>(prep_blocks)), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL((ea02::attn_bwd_dkdv_kernel<D, kKvNW, kKvP, kKvBP>),
-                     dim3(static_cast<unsigned>(p.n_heads_wg * p.n_key_blocks * p.n_kv_splits)), dim3(kKvNW * 64),
-                     0, s, p);
+                     dim3(static_cast<unsigned>(kv_plan.launch_grid)), dim3(kKvNW * 64), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.n_kv_splits > 1) {
     const int64_t quads = int64_t(p.n_heads_wg) * p.N_kv * D / 4;
@@ -212,7 +225,7 @@ hipError_t launch_all(const BwdParams& p, int q_nw, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.rows > 0) {
-    const dim3 grid(static_cast<unsigned>(p.n_heads_wg * p.n_pair_blocks * p.n_q_splits));
+    const dim3 grid(static_cast<unsigned>(q_plan.launch_grid));
     if (q_nw == kQMidNW)
       hipLaunchKernelGGL((ea02::attn_bwd_dq_kernel<D, kQMidNW, kQMidP, kQBN, 32>), grid, dim3(kQMidNW * 64), 0, s, p);
     else

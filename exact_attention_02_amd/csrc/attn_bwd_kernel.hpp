@@ -86,6 +86,12 @@ struct BwdParams {
   uint32_t k_sign;       // 0x80008000 when sm_scale < 0: K negated in S (dK/dV kernel)
   uint32_t q_sign;       // 0x80008000 when sm_scale < 0: Q negated in S^T (dQ kernel)
   int64_t rows;          // B * H_q * N_q
+  // Work stealing between the XCDs (work_item): nine claim counters, zero
+  // on entry and on exit, or null for the static order; per kernel, the
+  // workgroups of the static order and how many of them keep their item.
+  int* steal;
+  int kv_items, kv_static;  // dK/dV kernel
+  int q_items, q_static;    // dQ kernel
 };
 
 // 16-byte chunk swizzle for tiles read both row-wise (16 lanes, 16 rows, one
@@ -163,8 +169,11 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
   const int col = lane & 31;
 
   // heaviest key blocks first (causal: block 0 sees every row), kv heads
-  // fastest, then the row-range splits of one key block
-  const int bid = blockIdx.x;
+  // fastest, then the row-range splits of one key block; item bid of that
+  // order, possibly claimed from another XCD's list (work_item)
+  __shared__ int claimed;
+  const int bid = work_item(p.steal, p.kv_items, p.kv_static, wave, lane, claimed);
+  if (bid < 0) return;
   const int head_wg = bid % p.n_heads_wg;
   const int rest = bid / p.n_heads_wg;
   const int split = rest % p.n_kv_splits;
@@ -628,8 +637,11 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const int col = lane % MN;
 
   // heaviest pair blocks first (causal: the last rows see every key), kv
-  // heads fastest, then the key-range splits of one pair block
-  const int bid = blockIdx.x;
+  // heads fastest, then the key-range splits of one pair block; item bid of
+  // that order, possibly claimed from another XCD's list (work_item)
+  __shared__ int claimed;
+  const int bid = work_item(p.steal, p.q_items, p.q_static, wave, lane, claimed);
+  if (bid < 0) return;
   const int head_wg = bid % p.n_heads_wg;
   const int rest = bid / p.n_heads_wg;
   const int qsplit = rest % p.n_q_splits;

@@ -99,7 +99,7 @@ struct FwdParams {
                       // a masked score (-inf) never meets a zero factor
   uint32_t q_sign;    // 0x80008000 when sm_scale < 0 (Q is negated on load), else 0
   int causal;
-  // Work stealing between the XCDs (eight-wave single pass; claim_item).
+  // Work stealing between the XCDs (eight-wave single pass; work_item).
   int* steal;         // nine claim counters, zero on entry and on exit; null: static order
   int n_items;        // workgroups of the static order (the grid may hold more)
   int n_static;       // workgroups below this index take their own item (a multiple of 8)
@@ -115,14 +115,15 @@ struct FwdParams {
 // steal[8] counts finished claims, and the last claimer zeroes all nine
 // counters, so they are zero again for the next launch on the stream.  Each
 // item is computed the same way whoever runs it, so the results do not depend
-// on the schedule.
+// on the schedule.  Used by the forward's eight-wave single pass and by both
+// backward kernels.
 __device__ __forceinline__ int steal_list_len(int n_items, int x) { return (n_items - x + 7) >> 3; }
 
 // Called by all lanes of one wave; returns the claimed item or -1 (uniform).
-__device__ __forceinline__ int claim_item(const FwdParams& p, int lane) {
+__device__ __forceinline__ int claim_work_item(int* steal, int n_items, int n_static, int lane) {
   typedef __attribute__((address_space(1))) int global_int;
-  global_int* ctr = (global_int*)p.steal;  // a global-memory pointer (global, not flat, atomics)
-  const int n = p.n_items, own = blockIdx.x & 7, j0 = p.n_static >> 3;
+  global_int* ctr = (global_int*)steal;  // a global-memory pointer (global, not flat, atomics)
+  const int n = n_items, own = blockIdx.x & 7, j0 = n_static >> 3;
   int item = -1;
   if (lane == 0) {
     const int k = __hip_atomic_fetch_add(ctr + own, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -157,10 +158,24 @@ __device__ __forceinline__ int claim_item(const FwdParams& p, int lane) {
     // every claim of this workgroup has completed before it counts as done
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int done = __hip_atomic_fetch_add(ctr + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == (int)gridDim.x - p.n_static - 1)
+    if (done == (int)gridDim.x - n_static - 1)
       for (int c = 0; c < 9; ++c) __hip_atomic_exchange(ctr + c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return item;
+}
+
+// The work item of this workgroup: its own index below n_static or without
+// counters, else a claimed one (-1: none left).  Every thread of the
+// workgroup calls it; `claimed` is a workgroup-shared int.
+__device__ __forceinline__ int work_item(int* steal, int n_items, int n_static, int wave, int lane, int& claimed) {
+  const int bid = blockIdx.x;
+  if (steal == nullptr || bid < n_static) return bid;
+  if (wave == 0) {
+    const int item = claim_work_item(steal, n_items, n_static, lane);
+    if (lane == 0) claimed = item;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(claimed);
 }
 
 template <bool V>
@@ -348,19 +363,12 @@ void attn_fwd_kernel(FwdParams p) {
 
   // ---- work decomposition: heaviest pair blocks first (causal), then the
   //      key splits, kv heads fastest.  Item bid of that order; the
-  //      eight-wave single pass may claim it instead (claim_item).
+  //      eight-wave single pass may claim it instead (work_item).
   int bid = blockIdx.x;
   if constexpr (!SPLIT && NW == 8) {
-    if (p.steal != nullptr && bid >= p.n_static) {
-      __shared__ int claimed;
-      if (wave == 0) {
-        const int item = claim_item(p, lane);
-        if (lane == 0) claimed = item;
-      }
-      __syncthreads();
-      bid = __builtin_amdgcn_readfirstlane(claimed);
-      if (bid < 0) return;
-    }
+    __shared__ int claimed;
+    bid = work_item(p.steal, p.n_items, p.n_static, wave, lane, claimed);
+    if (bid < 0) return;
   }
   const int head_wg = bid % p.n_heads_wg;
   const int rest = bid / p.n_heads_wg;
