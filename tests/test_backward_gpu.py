@@ -345,3 +345,51 @@ def test_backward_timed_workloads_sampled(ea, name):
         _check("dV", dv[0, g, keys], rv[g], f"{name} dV g{g}")
     print(f"[bwd-timed] {name}: {len(heads)} heads x {rows.size} rows, {len(groups)} groups x "
           f"{keys.size} keys pass", flush=True)
+
+
+def test_backward_stealing_schedule(ea):
+    """At causal GQA-4 N=32768 both backward kernels have grids of at least
+    eight rounds of the device, so their workgroups claim work between the
+    XCDs through the stream's counters; captured into a graph the same call
+    runs the static order.  dQ, dK and dV agree bit for bit across repeated
+    eager calls (each launch must leave the counters at zero) and graph
+    replays interleaved with eager calls."""
+    w = workloads.WORKLOADS["gqa4_n32768_causal"]
+    print(f"[bwd-steal] {w.name}", flush=True)
+    dev = _dev()
+    q, k, v, dO = (x.to(dev) for x in _inputs(w.B, w.H_q, w.H_kv, w.N, w.N, w.D, w.seed))
+    o, lse = ea.fwd(q, k, v, is_causal=True)
+    ns = ea.attn_bwd_num_splits(w.B, w.H_q, w.H_kv, w.N, w.N, w.D, True)
+    ws = torch.empty(ea.attn_bwd_workspace_size(w.B, w.H_q, w.H_kv, w.N, w.N, w.D, True, ns),
+                     dtype=torch.uint8, device=dev)
+
+    def grads():
+        return tuple(torch.full_like(x, float("nan")) for x in (q, k, v))
+
+    def run(g):
+        ea.attn_bwd(q, k, v, o, dO, lse, *g, is_causal=True, sm_scale=w.sm_scale, n_splits=ns, workspace=ws)
+
+    def same(a, b):
+        return all(torch.equal(x.view(torch.int16), y.view(torch.int16)) for x, y in zip(a, b))
+
+    ref = grads()
+    run(ref)
+    torch.cuda.synchronize()
+    for it in range(2):
+        g = grads()
+        run(g)
+        torch.cuda.synchronize()
+        assert same(g, ref), f"repeated eager call {it} differs"
+    g_out = grads()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(g_out)
+    for it in range(2):
+        for x in g_out:
+            x.fill_(float("nan"))
+        graph.replay()
+        g = grads()
+        run(g)
+        torch.cuda.synchronize()
+        assert same(g_out, ref), f"graph replay {it} (static order) differs"
+        assert same(g, ref), f"eager call after replay {it} differs"
