@@ -454,8 +454,9 @@ def test_work_stealing_schedule(ea, D):
     into a graph it runs the static work order.  Every schedule gives the
     same bits: repeated calls on one stream (each launch must leave its
     counters at zero for the next), two streams running at once (separate
-    counters), the per-thread default stream and graph replays interleaved
-    with eager calls (both in the static order)."""
+    counters), two host threads on their own streams, the per-thread default
+    stream and graph replays interleaved with eager calls (both in the static
+    order)."""
     dev = torch.device("cuda", 0)
     w = workloads.WORKLOADS["gqa4_n16384_causal"]
     print(f"[steal] {w.name} D={D}", flush=True)
@@ -491,6 +492,33 @@ def test_work_stealing_schedule(ea, D):
         torch.cuda.synchronize()
         for o in outs:
             assert same(o, ref), f"concurrent streams, round {it}: result differs"
+
+    # two host threads, each on its own stream, claim counter slots at once
+    import threading
+    t_outs = [[bufs() for _ in range(2)] for _ in range(2)]
+    errors = []
+    torch.cuda.synchronize()
+
+    def worker(j):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for o in t_outs[j]:
+                    ea.attn_fwd(q, k, v, *o, is_causal=True, sm_scale=w.sm_scale)
+            st.synchronize()
+        except Exception as exc:  # reported below, in the test's thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=worker, args=(j,)) for j in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for j in range(2):
+        for o in t_outs[j]:
+            assert same(o, ref), f"host thread {j}: result differs"
 
     # hipStreamPerThread (handle 2) names a different stream in every thread:
     # the static order
