@@ -45,6 +45,8 @@ METRIC = "attention fwd TFLOPS and % of MI355X bf16 MFMA peak (GQA causal, N=1Kâ
 CSRC = os.path.join(ROOT, "exact_attention_02_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("attn_fwd_kernel.hpp", "attn_abi.hip")]
 BWD_SOURCES = [os.path.join(CSRC, f) for f in ("attn_bwd_kernel.hpp", "attn_bwd.hip")]
+# the latent core's kernels: attn_mla_kernel and the forward header's merge
+MLA_SOURCES = [os.path.join(CSRC, f) for f in ("attn_mla_kernel.hpp", "attn_mla.hip", "attn_fwd_kernel.hpp")]
 
 
 def log(*a):
@@ -421,6 +423,35 @@ def time_mla(ea, torch, name, mw, steps, warmup):
     log(f"[mla] {name:22s} splits {ns:3d}  core {t * 1e3:8.1f} us  "
         f"{mw.core_bytes() / t / 1e6:7.0f} GB/s  {mw.core_flops() / t / 1e9:7.1f} TFLOP/s   "
         f"absorb+core+up {res_t['full'] * 1e3:8.1f} us")
+    if steps is None:
+        return None
+    return {"core_ms": t, "step_ms": res_t["full"], "n_splits": ns,
+            "tensors": (q_lat, kv, out_lat, lse_m)}
+
+
+def mla_parity(mw, tensors):
+    """The latent core's output and LSE against the oracle on the core's own
+    inputs (the absorbed queries this run produced, the latent cache), for
+    every head of the first and the last batch element; tolerance as the MLA
+    GPU tests (2e-2 absolute plus 2e-2 relative on O, 1e-3 on the LSE)."""
+    import oracle
+    q_lat, kv, out_lat, lse_m = tensors
+    t0 = time.perf_counter()
+    worst_o = worst_l = 0.0
+    ok = True
+    for b in sorted({0, mw.B - 1}):
+        q64 = q_lat[b:b + 1].float().cpu().numpy().astype(np.float64)
+        kv64 = kv[b:b + 1].float().cpu().numpy().astype(np.float64)
+        O, L = oracle.mla_latent_attention(q64, kv64, mw.d_c, is_causal=mw.causal, sm_scale=mw.sm_scale)
+        o = out_lat[b:b + 1].float().cpu().numpy().astype(np.float64)
+        l = lse_m[b:b + 1].cpu().numpy().astype(np.float64)
+        err_o, err_l = np.abs(o - O), np.abs(l - L)
+        ok &= bool(np.isfinite(o).all() and np.isfinite(l).all())
+        ok &= bool((err_o <= 2e-2 + 2e-2 * np.abs(O)).all()) and bool(err_l.max() <= 1e-3)
+        worst_o, worst_l = max(worst_o, float(err_o.max())), max(worst_l, float(err_l.max()))
+    return {"sampled_pass": ok, "batch_elements": sorted({0, mw.B - 1}), "heads": mw.H,
+            "max_abs_err_O": worst_o, "max_abs_err_LSE": worst_l,
+            "wall_s": round(time.perf_counter() - t0, 1)}
 
 
 def main():
@@ -468,11 +499,38 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
         return
 
-    if args.mla_sweep or args.mla:
+    if args.mla_sweep:
         for name, mw in workloads.MLA_WORKLOADS.items():
-            if args.mla_sweep or name == args.mla:
-                time_mla(ea, torch, name, mw, None if args.mla_sweep else args.steps,
-                         None if args.mla_sweep else args.warmup)
+            time_mla(ea, torch, name, mw, None, None)
+        return
+    if args.mla:
+        # one MLA workload: the latent core (split pass + merge) against the
+        # roofline that binds it, one JSON line
+        mw = workloads.MLA_WORKLOADS[args.mla]
+        r = time_mla(ea, torch, args.mla, mw, args.steps, args.warmup)
+        t_s = r["core_ms"] * 1e-3
+        gbs, tfs = mw.core_bytes() / t_s / 1e9, mw.core_flops() / t_s / 1e12
+        hbm_frac, mfma_frac = gbs / PEAK_HBM_GBS, tfs / PEAK_BF16_TFLOPS
+        traffic = read_profile(f"attn_{args.mla}_hbm_traffic.md", "core_hbm_bytes_per_launch", MLA_SOURCES)
+        if hbm_frac >= mfma_frac:
+            roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(hbm_frac, 4)}
+        else:
+            roof = {"bound": "mfma", "achieved": round(tfs, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(mfma_frac, 4)}
+        roof.update({"traffic": traffic, "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
+                     "kernel": "attn_mla_decode (attn_mla_kernel split pass + merge)",
+                     "median_launch_ms": round(r["core_ms"], 5), "n_splits": r["n_splits"],
+                     "algorithmic_bytes_per_launch": mw.core_bytes(),
+                     "algorithmic_flops_per_launch": mw.core_flops()})
+        parity = None if args.no_cpu_baseline else mla_parity(mw, r["tensors"])
+        print(json.dumps({
+            "metric": "MLA absorbed decode: latent core time against its binding roofline",
+            "value": round(r["core_ms"] * 1e3, 2), "unit": "us", "higher_is_better": False,
+            "step_us": round(r["step_ms"] * 1e3, 2), "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": mw.name, "B": mw.B, "H": mw.H, "S": mw.S, "T": mw.T, "d_c": mw.d_c,
+                       "d_r": mw.d_r, "causal": mw.causal, "seed": mw.seed},
+            "roofline": roof, "parity": parity}), flush=True)
         return
 
     if args.backward:
