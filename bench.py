@@ -430,8 +430,8 @@ def time_mla(ea, torch, name, mw, steps, warmup):
 
 
 def mla_parity(mw, tensors):
-    """The latent core's output and LSE against the oracle on the core's own
-    inputs (the absorbed queries this run produced, the latent cache), for
+    """Part of the CPU-baseline leg of --mla: the latent core's output and LSE
+    against the oracle on the core's own inputs (the absorbed queries this run produced, the latent cache), for
     every head of the first and the last batch element; tolerance as the MLA
     GPU tests (2e-2 absolute plus 2e-2 relative on O, 1e-3 on the LSE)."""
     import oracle
