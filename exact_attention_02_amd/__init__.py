@@ -26,7 +26,7 @@ from .build import LIB_PATH
 __all__ = ["attn_fwd", "fwd", "attn_fwd_splitkv", "fwd_splitkv", "attn_splitkv_num_splits",
            "attn_fwd_splitkv_static", "attn_static_scratch_bytes",
            "attn_splitkv_workspace_size", "attn_bwd", "bwd", "attn_bwd_num_splits",
-           "attn_bwd_workspace_size",
+           "attn_bwd_workspace_size", "attention",
            "attn_mla_decode", "attn_mla_num_splits", "attn_mla_workspace_size", "mla_absorb_q",
            "mla_up_project", "mla_decode",
            "attn_status_string", "attn_abi_version",
@@ -349,6 +349,48 @@ def bwd(q, k, v, out, dout, lse, is_causal: bool = False, sm_scale: float | None
     attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, is_causal=is_causal, sm_scale=sm_scale,
              n_splits=ns, workspace=ws, stream=stream)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- autograd
+# The pages' autograd wrapper (page "Flash Attention 与 Kernel 优化", section
+# "Autograd 包装与反向传播"): the forward saves q, k, v, O and the LSE, and
+# the backward recomputes the probabilities from the LSE.  Here both passes
+# are this library's entry points; the class only routes tensors.
+_AUTOGRAD_FN = None
+
+
+def _autograd_fn():
+    global _AUTOGRAD_FN
+    if _AUTOGRAD_FN is None:
+        import torch
+
+        class FlashAttention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, is_causal, sm_scale):
+                if q.shape[2] == k.shape[2]:
+                    out, lse = fwd(q, k, v, is_causal=is_causal, sm_scale=sm_scale)
+                else:
+                    out, lse = fwd_splitkv(q, k, v, is_causal=is_causal, sm_scale=sm_scale)
+                ctx.save_for_backward(q, k, v, out, lse)
+                ctx.is_causal, ctx.sm_scale = is_causal, sm_scale
+                return out
+
+            @staticmethod
+            def backward(ctx, dout):
+                q, k, v, out, lse = ctx.saved_tensors
+                dq, dk, dv = bwd(q, k, v, out, dout.contiguous(), lse, is_causal=ctx.is_causal,
+                                 sm_scale=ctx.sm_scale)
+                return dq, dk, dv, None, None
+
+        _AUTOGRAD_FN = FlashAttention
+    return _AUTOGRAD_FN
+
+
+def attention(q, k, v, is_causal: bool = False, sm_scale: float | None = None):
+    """Differentiable attention: out = softmax(sm_scale q k^T [causal]) v with
+    gradients for q, k and v (bf16, [B, H, N, D] contiguous on one device;
+    N_q may differ from N_kv, causal then bottom-right aligned)."""
+    return _autograd_fn().apply(q, k, v, bool(is_causal), sm_scale)
 
 
 # ---------------------------------------------------------------- MLA decode

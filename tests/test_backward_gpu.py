@@ -393,3 +393,35 @@ def test_backward_stealing_schedule(ea):
         torch.cuda.synchronize()
         assert same(g_out, ref), f"graph replay {it} (static order) differs"
         assert same(g, ref), f"eager call after replay {it} differs"
+
+
+@pytest.mark.parametrize("N_q,N_kv,D,causal", [(200, 200, 128, True), (200, 200, 64, False), (96, 300, 128, True)])
+def test_autograd_wrapper(ea, N_q, N_kv, D, causal):
+    """ea.attention as a torch.autograd.Function: its output and the q, k, v
+    gradients that autograd returns are bit for bit those of the direct
+    entry points (forward, then attn_bwd on the saved O and LSE), and agree
+    with the oracle's gradients of the same loss within the backward
+    tolerance."""
+    q, k, v, dO = _inputs(1, 4, 2, N_q, N_kv, D, seed=4400 + N_q + D)
+    dev = _dev()
+    scale = 1.0 / math.sqrt(D)
+    qd, kd, vd = (x.to(dev).requires_grad_(True) for x in (q, k, v))
+    out = ea.attention(qd, kd, vd, is_causal=causal)
+    out.backward(dO.to(dev))
+    torch.cuda.synchronize()
+    qp, kp, vp = q.to(dev), k.to(dev), v.to(dev)
+    if N_q == N_kv:
+        o_ref, l_ref = ea.fwd(qp, kp, vp, is_causal=causal)
+    else:
+        o_ref, l_ref = ea.fwd_splitkv(qp, kp, vp, is_causal=causal)
+    dq, dk, dv = ea.bwd(qp, kp, vp, o_ref, dO.to(dev), l_ref, is_causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach().view(torch.int16), o_ref.view(torch.int16))
+    for name, got, ref in (("dQ", qd.grad, dq), ("dK", kd.grad, dk), ("dV", vd.grad, dv)):
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"{name} differs from attn_bwd"
+    q64, k64, v64, d64 = (workloads.to_float64(x) for x in (q, k, v, dO))
+    rq, rk, rv = oracle.attention_backward(q64, k64, v64, d64, is_causal=causal, sm_scale=scale,
+                                           out=workloads.to_float64(o_ref.cpu()))
+    _check("dQ", qd.grad.cpu(), rq, f"autograd {N_q}x{N_kv} D{D}")
+    _check("dK", kd.grad.cpu(), rk, f"autograd {N_q}x{N_kv} D{D}")
+    _check("dV", vd.grad.cpu(), rv, f"autograd {N_q}x{N_kv} D{D}")
