@@ -182,9 +182,10 @@ int check_alias(const Problem& a, const void* ws, size_t ws_used) {
   return ATTN_OK;
 }
 
+// bf16 partial outputs, then fp32 partial LSEs
 size_t workspace_bytes(int64_t B, int64_t H_q, int64_t N_q, int64_t D, int64_t n_splits) {
   if (n_splits <= 1) return 0;
-  return size_t(n_splits) * size_t(B * H_q * N_q) * size_t(D + 1) * 4;
+  return size_t(n_splits) * size_t(B * H_q * N_q) * size_t(2 * D + 4);
 }
 
 // Number of key splits the library picks (splits_for on the problem's shape).
@@ -308,8 +309,9 @@ int run(const Problem& a, int64_t n_splits, void* ws, void* stream) {
   p.v = static_cast<const uint16_t*>(a.v);
   p.o = static_cast<uint16_t*>(a.out);
   p.lse = a.lse;
-  p.o_part = split ? static_cast<float*>(ws) : nullptr;
-  p.lse_part = split ? static_cast<float*>(ws) + size_t(n_splits) * size_t(rows) * size_t(a.D) : nullptr;
+  p.o_part = split ? static_cast<uint16_t*>(ws) : nullptr;
+  p.lse_part = split ? reinterpret_cast<float*>(static_cast<uint16_t*>(ws) + size_t(n_splits) * size_t(rows) * size_t(a.D))
+                     : nullptr;
   p.B = static_cast<int>(a.B);
   p.H_q = static_cast<int>(a.H_q);
   p.H_kv = static_cast<int>(a.H_kv);
@@ -484,4 +486,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" int attn_abi_version(void) { return 7; }
+extern "C" int attn_abi_version(void) { return 8; }

@@ -86,7 +86,7 @@ struct FwdParams {
   const uint16_t* v;  // [B, H_kv, N_kv, D] bf16
   uint16_t* o;        // [B, H_q, N_q, D] bf16 (single pass)
   float* lse;         // [B, H_q, N_q] natural log (single pass)
-  float* o_part;      // [n_splits, B, H_q, N_q, D] fp32 (split pass)
+  uint16_t* o_part;   // [n_splits, B, H_q, N_q, D] bf16 (split pass)
   float* lse_part;    // [n_splits, B, H_q, N_q] log2 units (split pass)
   int B, H_q, H_kv, N_q, N_kv;
   int G;              // H_q / H_kv
@@ -827,14 +827,15 @@ void attn_fwd_kernel(FwdParams p) {
       const bool seen = l_tot > 0.f;
       const float inv = seen ? 1.f / l_tot : 0.f;
       const size_t slot = (size_t)split * ((size_t)p.B * p.H_q * p.N_q) + bhr;
-      float* orow = p.o_part + slot * D;
+      uint16_t* orow = p.o_part + slot * D;
 #pragma unroll
       for (int db = 0; db < D / MN; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < ACC / 4; ++g4) {
           const f32x4 f = {acc[db][qc][4 * g4 + 0] * inv, acc[db][qc][4 * g4 + 1] * inv,
                            acc[db][qc][4 * g4 + 2] * inv, acc[db][qc][4 * g4 + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + db * MN + g4 * (256 / MN) + 4 * kgrp) = f;
+          const bf16x4 bv = __builtin_convertvector(f, bf16x4);
+          *reinterpret_cast<u32x2*>(orow + db * MN + g4 * (256 / MN) + 4 * kgrp) = __builtin_bit_cast(u32x2, bv);
         }
       if (kgrp == 0) p.lse_part[slot] = seen ? m_used[qc] + __log2f(l_tot) : -INFINITY;
     }
@@ -853,8 +854,8 @@ void attn_fwd_kernel(FwdParams p) {
 // per launch so that a thread sees at most a few splits: few rows (a decode
 // step) still spread over many threads.
 struct MergeParams {
-  const float* o_part;    // [n_splits, rows, D]
-  const float* lse_part;  // [n_splits, rows]
+  const uint16_t* o_part;  // [n_splits, rows, D] bf16: each split's O, normalised by its own sum
+  const float* lse_part;   // [n_splits, rows] log2 units
   uint16_t* o;            // [rows, D] bf16
   float* lse;             // [rows]
   int64_t rows;           // B * H_q * N_q
@@ -874,7 +875,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT))) void attn_merge_
   const size_t stride = (size_t)p.rows;
   const int n = p.n_splits;
   const float* lse_r = p.lse_part + row;
-  const float* o_r = p.o_part + (size_t)row * D + 4 * c;
+  const uint16_t* o_r = p.o_part + (size_t)row * D + 4 * c;
 
   float m = -INFINITY;
   for (int s0 = j; s0 < n; s0 += kMergeBatch * SL) {
@@ -897,7 +898,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT))) void attn_merge_
       for (int u = 0; u < kMergeBatch; ++u) {
         const int s = min(s0 + u * SL, n - 1);
         l[u] = s0 + u * SL < n ? lse_r[s * stride] : -INFINITY;
-        x[u] = *reinterpret_cast<const f32x4*>(o_r + s * stride * D);
+        x[u] = __builtin_convertvector(__builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(o_r + s * stride * D)), f32x4);
       }
 #pragma unroll
       for (int u = 0; u < kMergeBatch; ++u) {

@@ -28,7 +28,7 @@ bool mis16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; 
 
 size_t mla_ws_bytes(int64_t B, int64_t H, int64_t S, int64_t n_splits) {
   if (n_splits <= 1) return 0;
-  return size_t(n_splits) * size_t(B * H * S) * size_t(ea02::kMlaDc + 1) * 4;
+  return size_t(n_splits) * size_t(B * H * S) * size_t(2 * ea02::kMlaDc + 4);  // bf16 partial O, fp32 LSE
 }
 
 // size checks shared by the core's entry points
@@ -100,8 +100,9 @@ extern "C" int attn_mla_decode(const void* q_lat, const void* kv, void* out_lat,
   p.kv = static_cast<const uint16_t*>(kv);
   p.o = static_cast<uint16_t*>(out_lat);
   p.lse = lse;
-  p.o_part = split ? static_cast<float*>(workspace) : nullptr;
-  p.lse_part = split ? static_cast<float*>(workspace) + size_t(ns) * size_t(rows) * ea02::kMlaDc : nullptr;
+  p.o_part = split ? static_cast<uint16_t*>(workspace) : nullptr;
+  p.lse_part = split ? reinterpret_cast<float*>(static_cast<uint16_t*>(workspace) + size_t(ns) * size_t(rows) * ea02::kMlaDc)
+                     : nullptr;
   p.B = static_cast<int>(B);
   p.H = static_cast<int>(H);
   p.S = static_cast<int>(S);

@@ -41,7 +41,7 @@ struct MlaParams {
   const uint16_t* kv;  // [B, T, 576] bf16 latent cache
   uint16_t* o;         // [B, H, S, 512] bf16 (single pass)
   float* lse;          // [B, H, S] natural log (single pass)
-  float* o_part;       // [n_splits, B*H*S, 512] fp32 (split pass)
+  uint16_t* o_part;    // [n_splits, B*H*S, 512] bf16 (split pass)
   float* lse_part;     // [n_splits, B*H*S] log2 units (split pass)
   int B, H, S, T;
   int n_pairs;         // S * H
@@ -284,14 +284,15 @@ void attn_mla_kernel(MlaParams p) {
     const bool seen = l_tot > 0.f;
     const float inv = seen ? 1.f / l_tot : 0.f;
     const size_t slot = (size_t)split * ((size_t)p.B * p.H * p.S) + bhr;
-    float* orow = p.o_part + slot * kMlaDc + dbase;
+    uint16_t* orow = p.o_part + slot * kMlaDc + dbase;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = db * 32 + 8 * g4 + 4 * half;
-        *reinterpret_cast<f32x4*>(orow + d0) = f32x4{acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv,
-                                                     acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv};
+        const f32x4 f = {acc[db][4 * g4] * inv, acc[db][4 * g4 + 1] * inv, acc[db][4 * g4 + 2] * inv,
+                         acc[db][4 * g4 + 3] * inv};
+        *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4));
       }
     if (kh == 0 && half == 0) p.lse_part[slot] = seen ? m_used + __log2f(l_tot) : -INFINITY;
   }

@@ -123,7 +123,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  * keys, with O_s and LSE_s the attention output and log-sum-exp over K_s
  * alone,
  *   LSE = log sum_s exp(LSE_s),   out = sum_s exp(LSE_s - LSE) * O_s,
- * which is exactly attention over all visible keys.  The partials are fp32.
+ * which is exactly attention over all visible keys.  Each O_s is stored in
+ * bf16 (normalised by its own sum, so |O_s| is bounded by the largest |v|)
+ * and each LSE_s in fp32; the merge sums in fp32.
  *
  * Semantics as attn_fwd, with i in [0, N_q), j in [0, N_kv), and under
  * is_causal the mask aligned to the bottom-right corner: query row i sees keys
@@ -203,7 +205,7 @@ int64_t attn_splitkv_num_splits(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_
 
 /*
  * attn_splitkv_workspace_size -- bytes of workspace for n_splits key ranges:
- * 0 when n_splits <= 1, else n_splits * B * H_q * N_q * (D + 1) * 4 (fp32
+ * 0 when n_splits <= 1, else n_splits * B * H_q * N_q * (2 * D + 4) (bf16
  * partial outputs, then fp32 partial log-sum-exps).  0 for invalid sizes.
  */
 size_t attn_splitkv_workspace_size(int64_t B, int64_t H_q, int64_t N_q, int64_t D, int64_t n_splits);
@@ -338,7 +340,8 @@ int attn_mla_decode(const void* q_lat, const void* kv, void* out_lat, float* lse
 int64_t attn_mla_num_splits(int64_t B, int64_t H, int64_t S, int64_t T, int is_causal);
 
 /* Workspace bytes of attn_mla_decode: 0 when n_splits <= 1, else
- * n_splits * B * H * S * (512 + 1) * 4.  0 for invalid sizes. */
+ * n_splits * B * H * S * (2 * 512 + 4) (bf16 partial outputs, then fp32
+ * partial log-sum-exps).  0 for invalid sizes. */
 size_t attn_mla_workspace_size(int64_t B, int64_t H, int64_t S, int64_t n_splits);
 
 /*

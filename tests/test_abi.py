@@ -38,7 +38,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.attn_abi_version() == 7
+    assert lib.attn_abi_version() == 8
 
 
 def test_status_strings_distinct(lib):
@@ -154,7 +154,7 @@ def test_splitkv_single_pass_needs_no_workspace(lib):
 
 def test_workspace_size_formula():
     for (B, H_q, N_q, D, ns) in [(1, 32, 1, 128, 16), (2, 8, 100, 64, 3), (1, 1, 1, 64, 256)]:
-        assert ea.attn_splitkv_workspace_size(B, H_q, N_q, D, ns) == ns * B * H_q * N_q * (D + 1) * 4
+        assert ea.attn_splitkv_workspace_size(B, H_q, N_q, D, ns) == ns * B * H_q * N_q * (2 * D + 4)
     assert ea.attn_splitkv_workspace_size(1, 32, 1, 128, 1) == 0
     assert ea.attn_splitkv_workspace_size(1, 32, 1, 128, 0) == 0
     assert ea.attn_splitkv_workspace_size(1, 32, 1, 128, 257) == 0
@@ -331,7 +331,7 @@ def test_mla_invalid_arguments_rejected(lib, kw, code):
 def test_mla_empty_and_sizes(lib):
     assert call_mla(lib, q=0, kv=0, o=0, l=0, ws=0, B=0) == STATUS["ATTN_OK"]
     assert call_mla(lib, q=0, kv=0, o=0, l=0, ws=0, S=0) == STATUS["ATTN_OK"]
-    assert ea.attn_mla_workspace_size(2, 128, 1, 8) == 8 * 2 * 128 * 513 * 4
+    assert ea.attn_mla_workspace_size(2, 128, 1, 8) == 8 * 2 * 128 * (2 * 512 + 4)
     assert ea.attn_mla_workspace_size(2, 128, 1, 1) == 0
     assert ea.attn_mla_num_splits(1, 128, 1, 16384, True) >= 2
     assert ea.attn_mla_num_splits(256, 128, 1, 16384, True) == 1
@@ -368,8 +368,8 @@ def call_static(lib, q=Q, k=K, v=V, o=O, l=L, B=1, H_q=4, H_kv=2, N_q=16, N_kv=4
     (dict(N_kv=0), "ATTN_ERR_NO_KEYS"),
     (dict(o=0), "ATTN_ERR_NULL_POINTER"),
     (dict(k=K + 2), "ATTN_ERR_ALIGNMENT"),
-    # 256 splits of 160 rows at D=128: 21 MB of partials, above the 16 MiB scratch
-    (dict(N_q=40, D=128, n_splits=256), "ATTN_ERR_STATIC_SCRATCH"),
+    # 256 splits of 320 rows at D=128: 21 MB of partials, above the 16 MiB scratch
+    (dict(N_q=80, D=128, n_splits=256), "ATTN_ERR_STATIC_SCRATCH"),
     (dict(l=Q + 64), "ATTN_ERR_ALIAS"),
 ])
 def test_static_invalid_arguments_rejected(lib, kw, code):
@@ -379,11 +379,13 @@ def test_static_invalid_arguments_rejected(lib, kw, code):
 def test_static_scratch_size_and_limit(lib):
     assert ea.attn_static_scratch_bytes() == 16 << 20
     # the largest request that fits is accepted up to the alias check
+    # 320 rows at D=128: the limit falls below the 256-split maximum
     ns = 1
-    while ea.attn_splitkv_workspace_size(1, 4, 40, 128, ns + 1) <= ea.attn_static_scratch_bytes():
+    while ns < 256 and ea.attn_splitkv_workspace_size(1, 4, 80, 128, ns + 1) <= ea.attn_static_scratch_bytes():
         ns += 1
-    assert call_static(lib, N_q=40, D=128, n_splits=ns, o=Q) == STATUS["ATTN_ERR_ALIAS"]
-    assert call_static(lib, N_q=40, D=128, n_splits=ns + 1, o=Q) == STATUS["ATTN_ERR_STATIC_SCRATCH"]
+    assert ns < 256
+    assert call_static(lib, N_q=80, D=128, n_splits=ns, o=Q) == STATUS["ATTN_ERR_ALIAS"]
+    assert call_static(lib, N_q=80, D=128, n_splits=ns + 1, o=Q) == STATUS["ATTN_ERR_STATIC_SCRATCH"]
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(N_q=0)])
