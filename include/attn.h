@@ -367,9 +367,11 @@ int mla_up_project(const void* out_lat, const void* w_uv, void* out, int64_t B, 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);
 
-/* Library ABI version, currently 6 (1: attn_fwd; 2: + split-KV; 3: + backward;
+/* Library ABI version, currently 8 (1: attn_fwd; 2: + split-KV; 3: + backward;
  * 4: + MLA decode; 5: backward row-range splits, attn_bwd_num_splits; 6:
- * backward dQ key-range splits, is_causal in attn_bwd_workspace_size). */
+ * backward dQ key-range splits, is_causal in attn_bwd_workspace_size; 7: +
+ * attn_fwd_splitkv_static; 8: bf16 split partial outputs, smaller
+ * attn_splitkv_workspace_size and attn_mla_workspace_size). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus
