@@ -21,6 +21,7 @@ rows, which see few keys, have gradients ten times the tensor's typical size
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 
 import numpy as np
@@ -347,15 +348,18 @@ def test_backward_timed_workloads_sampled(ea, name):
           f"{keys.size} keys pass", flush=True)
 
 
-def test_backward_stealing_schedule(ea):
-    """At causal GQA-4 N=32768 both backward kernels have grids of at least
+@pytest.mark.parametrize("D", [128, 64])
+def test_backward_stealing_schedule(ea, D):
+    """At causal GQA-4 N=32768 (D=128 and 64) both backward kernels have grids of at least
     eight rounds of the device, so their workgroups claim work between the
     XCDs through the stream's counters; captured into a graph the same call
     runs the static order.  dQ, dK and dV agree bit for bit across repeated
     eager calls (each launch must leave the counters at zero) and graph
     replays interleaved with eager calls."""
     w = workloads.WORKLOADS["gqa4_n32768_causal"]
-    print(f"[bwd-steal] {w.name}", flush=True)
+    if D != w.D:
+        w = dataclasses.replace(w, D=D, seed=w.seed + D)
+    print(f"[bwd-steal] {w.name} D={D}", flush=True)
     dev = _dev()
     q, k, v, dO = (x.to(dev) for x in _inputs(w.B, w.H_q, w.H_kv, w.N, w.N, w.D, w.seed))
     o, lse = ea.fwd(q, k, v, is_causal=True)

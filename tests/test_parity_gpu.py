@@ -154,6 +154,32 @@ def test_large_workloads_full(ea, name):
         assert el <= LSE_ATOL, f"{name} b{b} h{h}: max LSE err {el:.3e}"
 
 
+def test_large_d64_full(ea):
+    """Every output row of causal GQA-4 N=16384 at D=64 against the oracle:
+    the D=64 build of the eight-wave kernel at a grid long enough for the XCD
+    work stealing (2048 workgroups).  Same process pool as above."""
+    import concurrent.futures as cf
+    import multiprocessing
+    B, H_q, H_kv, N, D = 1, 32, 8, 16384, 64
+    print(f"[full] d64 N={N}", flush=True)
+    q, k, v = workloads.make_inputs(B, H_q, H_kv, N, D, seed=964)
+    scale = 1.0 / math.sqrt(D)
+    o, l = _run(ea, q, k, v, True, scale)
+    q64, k64, v64 = (workloads.to_float64(t) for t in (q, k, v))
+    o32, l32 = o.float().numpy(), l.numpy()
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    tasks = [(b, h, True, scale) for b in range(B) for h in range(H_q)]
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=multiprocessing.get_context("fork"),
+                                initializer=_full_init, initargs=(q64, k64, v64, o32, l32)) as ex:
+        results = list(ex.map(_full_head, tasks))
+    print(f"[full] d64: {len(results)} heads, max |dO| {max(r[4] for r in results):.3e}, "
+          f"max |dLSE| {max(r[5] for r in results):.3e}", flush=True)
+    for b, h, finite, bad, eo, el in results:
+        assert finite, f"d64 b{b} h{h}: non-finite output"
+        assert bad == 0, f"d64 b{b} h{h}: {bad} O elements out of tolerance, max abs err {eo:.3e}"
+        assert el <= LSE_ATOL, f"d64 b{b} h{h}: max LSE err {el:.3e}"
+
+
 def test_gqa8_n4096_some_heads_full(ea):
     """Two heads of different kv groups, every row, at the full GQA-8 shape."""
     w = workloads.WORKLOADS["gqa8_n4096_causal"]
