@@ -43,10 +43,14 @@ PEAK_HBM_GBS = 8000.0
 MFMA_FLOP_PER_CLK = 256 * 4096  # dense bf16 MFMA, whole chip (2.5 PFLOP/s at 2.4 GHz)
 METRIC = "attention fwd TFLOPS and % of MI355X bf16 MFMA peak (GQA causal, N=1K–32K)"
 CSRC = os.path.join(ROOT, "exact_attention_02_amd", "csrc")
-KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("attn_fwd_kernel.hpp", "attn_abi.hip")]
-BWD_SOURCES = [os.path.join(CSRC, f) for f in ("attn_bwd_kernel.hpp", "attn_bwd.hip")]
+# Sources whose hash ties a committed profile to the kernels it measured; the
+# build script is part of each list because its per-source flags change the
+# binaries too.
+BUILD_SCRIPT = os.path.join(ROOT, "exact_attention_02_amd", "build.py")
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("attn_fwd_kernel.hpp", "attn_abi.hip")] + [BUILD_SCRIPT]
+BWD_SOURCES = [os.path.join(CSRC, f) for f in ("attn_bwd_kernel.hpp", "attn_bwd.hip")] + [BUILD_SCRIPT]
 # the latent core's kernels: attn_mla_kernel and the forward header's merge
-MLA_SOURCES = [os.path.join(CSRC, f) for f in ("attn_mla_kernel.hpp", "attn_mla.hip", "attn_fwd_kernel.hpp")]
+MLA_SOURCES = [os.path.join(CSRC, f) for f in ("attn_mla_kernel.hpp", "attn_mla.hip", "attn_fwd_kernel.hpp")] + [BUILD_SCRIPT]
 
 
 def log(*a):
