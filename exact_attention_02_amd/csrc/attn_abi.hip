@@ -105,14 +105,17 @@ hipError_t launch_fwd(Kind kind, const FwdParams& p, int grid, hipStream_t strea
 }
 
 // One block per output row; the block's split lanes grow with the split count
-// so that each thread merges at most about kMergeBatch splits (blocks of 64,
-// 256 or 1024 threads).
+// so that each thread merges at most kMergeBatch splits (blocks of 64, 256 or
+// 1024 threads), or up to 4 kMergeBatch in the largest block, all loaded in
+// one round.
 template <int D>
 hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
   constexpr int tpr = D / 4;
-  if (m.n_splits <= ea02::kMergeBatch * (64 / tpr)) return ea02::launch_merge_rows<D, 64>(m, stream);
-  if (m.n_splits <= ea02::kMergeBatch * (256 / tpr)) return ea02::launch_merge_rows<D, 256>(m, stream);
-  return ea02::launch_merge_rows<D, 1024>(m, stream);
+  constexpr int kb = ea02::kMergeBatch;
+  if (m.n_splits <= kb * (64 / tpr)) return ea02::launch_merge_rows<D, 64, kb>(m, stream);
+  if (m.n_splits <= kb * (256 / tpr)) return ea02::launch_merge_rows<D, 256, kb>(m, stream);
+  if (m.n_splits <= kb * (1024 / tpr)) return ea02::launch_merge_rows<D, 1024, kb>(m, stream);
+  return ea02::launch_merge_rows<D, 1024, 4 * kb>(m, stream);
 }
 
 // Arguments shared by both entry points, after validation.

@@ -849,10 +849,13 @@ void attn_fwd_kernel(FwdParams p) {
 //   LSE = (M + log2 sum_s w_s) ln 2.
 // A thread owns 4 consecutive d of one row and every SL-th split ("split
 // lane"); it takes its own max over its splits first, then sums its weighted
-// partial outputs with loads issued four splits at a time, and the SL split
-// lanes of the row are combined through LDS by the same rule.  SL is chosen
-// per launch so that a thread sees at most a few splits: few rows (a decode
-// step) still spread over many threads.
+// partial outputs, and the SL split lanes of the row are combined through LDS
+// by the same rule.  SL is chosen per launch so that a thread sees at most a
+// few splits: few rows (a decode step) still spread over many threads.  With
+// at most KB splits per thread, every partial output loads in the same round
+// as the LSEs; with more, a first pass over the LSEs finds the max and a
+// second loads four splits at a time.  Both add a thread's splits in the same
+// order.
 struct MergeParams {
   const uint16_t* o_part;  // [n_splits, rows, D] bf16: each split's O, normalised by its own sum
   const float* lse_part;   // [n_splits, rows] log2 units
@@ -864,7 +867,7 @@ struct MergeParams {
 
 constexpr int kMergeBatch = 4;  // splits whose loads a thread issues together
 
-template <int D, int NT>
+template <int D, int NT, int KB>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT))) void attn_merge_kernel(MergeParams p) {
   constexpr int TPR = D / 4;  // threads per row and split lane
   constexpr int SL = NT / TPR;
@@ -878,33 +881,54 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT))) void attn_merge_
   const uint16_t* o_r = p.o_part + (size_t)row * D + 4 * c;
 
   float m = -INFINITY;
-  for (int s0 = j; s0 < n; s0 += kMergeBatch * SL) {
-    float l[kMergeBatch];
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const int s = s0 + u * SL;
-      l[u] = s < n ? lse_r[s * stride] : -INFINITY;
-    }
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) m = fmaxf(m, l[u]);
-  }
   float wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (m != -INFINITY) {
-    for (int s0 = j; s0 < n; s0 += kMergeBatch * SL) {
-      float l[kMergeBatch];
-      f32x4 x[kMergeBatch];
+  if (n <= KB * SL) {
+    float l[KB];
+    f32x4 x[KB];
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const int s = min(s0 + u * SL, n - 1);
-        l[u] = s0 + u * SL < n ? lse_r[s * stride] : -INFINITY;
-        x[u] = __builtin_convertvector(__builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(o_r + s * stride * D)), f32x4);
-      }
+    for (int u = 0; u < KB; ++u) {
+      const int s = min(j + u * SL, n - 1);
+      l[u] = j + u * SL < n ? lse_r[s * stride] : -INFINITY;
+      x[u] = __builtin_convertvector(__builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(o_r + s * stride * D)), f32x4);
+    }
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
+    for (int u = 0; u < KB; ++u) m = fmaxf(m, l[u]);
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
         const float w = __builtin_amdgcn_exp2f(l[u] - m);  // 2^-inf = 0
         wsum += w;
         acc += w * x[u];
+      }
+    }
+  } else {
+    for (int s0 = j; s0 < n; s0 += kMergeBatch * SL) {
+      float l[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int s = s0 + u * SL;
+        l[u] = s < n ? lse_r[s * stride] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) m = fmaxf(m, l[u]);
+    }
+    if (m != -INFINITY) {
+      for (int s0 = j; s0 < n; s0 += kMergeBatch * SL) {
+        float l[kMergeBatch];
+        f32x4 x[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const int s = min(s0 + u * SL, n - 1);
+          l[u] = s0 + u * SL < n ? lse_r[s * stride] : -INFINITY;
+          x[u] = __builtin_convertvector(__builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(o_r + s * stride * D)), f32x4);
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const float w = __builtin_amdgcn_exp2f(l[u] - m);  // 2^-inf = 0
+          wsum += w;
+          acc += w * x[u];
+        }
       }
     }
   }
@@ -938,7 +962,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT))) void attn_merge_
 // most 2^31 work-items each (a dispatch counts its work-items in 32 bits).
 // Each launch takes a contiguous run of rows through offset pointers; m.rows
 // stays the stride between splits.
-template <int D, int NT>
+template <int D, int NT, int KB>
 hipError_t launch_merge_rows(const MergeParams& m, hipStream_t stream) {
   constexpr int64_t kRowsPerLaunch = (int64_t(1) << 31) / NT;
   for (int64_t r0 = 0; r0 < m.rows; r0 += kRowsPerLaunch) {
@@ -948,7 +972,7 @@ hipError_t launch_merge_rows(const MergeParams& m, hipStream_t stream) {
     c.lse_part = m.lse_part + r0;
     c.o = m.o + r0 * D;
     c.lse = m.lse + r0;
-    hipLaunchKernelGGL((attn_merge_kernel<D, NT>), dim3(static_cast<unsigned>(n)), dim3(NT), 0, stream, c);
+    hipLaunchKernelGGL((attn_merge_kernel<D, NT, KB>), dim3(static_cast<unsigned>(n)), dim3(NT), 0, stream, c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

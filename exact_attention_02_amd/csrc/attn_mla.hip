@@ -131,12 +131,14 @@ extern "C" int attn_mla_decode(const void* q_lat, const void* kv, void* out_lat,
     m.rows = rows;
     m.n_splits = p.n_splits;
     // 128 threads per row (4 of the 512 values each) times 2 or 8 split
-    // lanes.  (Slicing a row over several blocks, to spread a decode step's
-    // few rows over more CUs, measured no faster: the merge is bound by the
-    // bytes of fp32 partials it reads, and many-row steps got slower.)
-    const hipError_t e = m.n_splits <= ea02::kMergeBatch * 2
-                             ? ea02::launch_merge_rows<ea02::kMlaDc, 256>(m, s)
-                             : ea02::launch_merge_rows<ea02::kMlaDc, 1024>(m, s);
+    // lanes, each thread with up to 4 or 16 splits loaded in one round.
+    // (Slicing a row over several blocks, to spread a decode step's few rows
+    // over more CUs, measured no faster: the merge is bound by the bytes of
+    // partials it reads, and many-row steps got slower.)
+    constexpr int kb = ea02::kMergeBatch;
+    const hipError_t e = m.n_splits <= kb * 2   ? ea02::launch_merge_rows<ea02::kMlaDc, 256, kb>(m, s)
+                         : m.n_splits <= kb * 8 ? ea02::launch_merge_rows<ea02::kMlaDc, 1024, kb>(m, s)
+                                                : ea02::launch_merge_rows<ea02::kMlaDc, 1024, 4 * kb>(m, s);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;

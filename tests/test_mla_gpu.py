@@ -95,6 +95,19 @@ def test_latent_core(ea, T, causal, n_splits):
     _check_attn(o, l, O, L, f"T{T} c{int(causal)} s{n_splits}")
 
 
+@pytest.mark.parametrize("n_splits", [7, 24, 100, 256])
+def test_latent_core_merge_shapes(ea, n_splits):
+    """Split counts that take each merge launch shape at D = 512: 256-thread
+    blocks (up to 8 splits), 1024 with 4 splits per thread (up to 32), 1024
+    with 16 (up to 128), and the two-pass merge beyond."""
+    B, H, S, T = 2, 16, 1, 5000
+    q_lat, kv = _latent_inputs(B, H, S, T, seed=13050 + n_splits)
+    sc = 1 / math.sqrt(192)
+    o, l = _run_core(ea, q_lat, kv, sc, True, n_splits)
+    O, L = oracle.mla_latent_attention(_f64(q_lat), _f64(kv), 512, is_causal=True, sm_scale=sc)
+    _check_attn(o, l, O, L, f"T{T} s{n_splits}")
+
+
 @pytest.mark.parametrize("H,S,T", [(128, 1, 300), (128, 2, 129), (7, 5, 70), (3, 4, 4), (40, 3, 65)])
 @pytest.mark.parametrize("n_splits", [1, 4])
 def test_latent_core_heads_and_tokens(ea, H, S, T, n_splits):

@@ -157,8 +157,11 @@ def test_decode_workloads_full(ea, name):
     _check(o, l, O_ref, L_ref, what=name)
 
 
-@pytest.mark.parametrize("n_splits", [1, 2, 16, 256])
+@pytest.mark.parametrize("n_splits", [1, 2, 7, 16, 100, 256])
 def test_decode_split_counts(ea, n_splits):
+    """Split counts that take each merge launch shape: 64-thread blocks (up to
+    8 splits at D = 128), 256 (up to 32), 1024 with 4 splits per thread (up to
+    128) and 1024 with 16 (up to 512)."""
     _case(ea, 2, 16, 4, 1, 5000, 128, True, seed=8700, n_splits=n_splits)
 
 
