@@ -444,9 +444,12 @@ void attn_fwd_kernel(FwdParams p) {
   const uint16_t* v_head = p.v + kv_base;
   // one tile of K (ring 0) or V (ring 1) into ring slot `slot`; tile numbers
   // count from the split's first key
-  auto issue_tile = [&](int tile, int slot, const uint16_t* head, int ring) {
+  // A load that no phase reads (the ring's fill before the first V tile and
+  // past the last tiles) keeps its place in the load count but gets an empty
+  // resource: no memory access, zeros into a free slot.
+  auto issue_tile = [&](int tile, int slot, const uint16_t* head, int ring, bool live) {
     const int row0 = kbase + tile * BN;
-    const u32x4 rsrc = make_rsrc(head + (size_t)row0 * D, (uint32_t)(N_kv - row0) * C::ROW_BYTES);
+    const u32x4 rsrc = make_rsrc(head + (size_t)row0 * D, live ? (uint32_t)(N_kv - row0) * C::ROW_BYTES : 0u);
 #pragma unroll
     for (int i = 0; i < C::LOADS_PER_WAVE; ++i)
       dma_16B(rsrc, ring == 0 ? ld_off_k[i] : ld_off_v[i], lds_base + (ring * P + slot) * C::TILE_BYTES + (wave * C::LOADS_PER_WAVE + i) * 1024);
@@ -710,12 +713,12 @@ void attn_fwd_kernel(FwdParams p) {
   // t+1.  Groups are issued P-1 ahead: after the barrier that opens the
   // phase of tile t, group t+P goes into the slots that the phase of tile t-1
   // read (K(t), V(t-2)), which every wave has finished.  A group past either
-  // end of the sequence loads a clamped, valid tile into its (free) slots, so
-  // every group is the same number of loads and each wait below is one
-  // constant vmcnt.
+  // end of the sequence still issues its loads, with empty resources, into
+  // its (free) slots, so every group is the same number of loads and each
+  // wait below is one constant vmcnt.
   auto issue_group = [&](int j) {
-    issue_tile(min(j, n_tiles - 1), j % P, k_head, 0);
-    issue_tile(max(min(j - 2, n_tiles - 1), 0), (j + P - 2) % P, v_head, 1);
+    issue_tile(min(j, n_tiles - 1), j % P, k_head, 0, j < n_tiles);
+    issue_tile(max(min(j - 2, n_tiles - 1), 0), (j + P - 2) % P, v_head, 1, j >= 2 && j - 2 < n_tiles);
   };
   constexpr int GROUP_LOADS = 2 * C::LOADS_PER_WAVE;
   auto sync_prologue = [&]() {

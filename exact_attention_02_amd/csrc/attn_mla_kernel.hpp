@@ -146,16 +146,20 @@ void attn_mla_kernel(MlaParams p) {
 
   // tile loads: load li moves bytes [1024 li, 1024 li + 1024) of the tile,
   // lane -> (row, stored chunk j) and fetches chunk j ^ swz(row) of that row
+  // A load that no tile step reads (past the last tile) keeps its place in
+  // the load count but gets an empty resource: no memory access.
   const u32x4 rsrc = make_rsrc(p.kv + (size_t)b * T * kMlaDqk, (uint32_t)((size_t)T * kMlaRowBytes));
+  const u32x4 rsrc_none = make_rsrc(p.kv, 0u);
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
   auto issue = [&](int t, int slot) {
+    const u32x4 rs = t < n_tiles ? rsrc : rsrc_none;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int e = (wave * LPW + i) * 64 + lane;
       const int row = e / kMlaChunks;
       const int j = e - row * kMlaChunks;
       const int key = min(kbase + t * BN + row, T - 1);
-      dma_16B(rsrc, key * kMlaRowBytes + ((j ^ mla_swz(row)) << 4),
+      dma_16B(rs, key * kMlaRowBytes + ((j ^ mla_swz(row)) << 4),
               lds_base + slot * TILE_BYTES + (wave * LPW + i) * 1024);
     }
   };
@@ -254,11 +258,11 @@ void attn_mla_kernel(MlaParams p) {
 
   if (n_tiles > 0) {
 #pragma unroll
-    for (int j = 0; j < P - 1; ++j) issue(min(j, n_tiles - 1), j);
+    for (int j = 0; j < P - 1; ++j) issue(j, j);
     for (int t = 0; t < n_tiles; ++t) {
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 2) * LPW) : "memory");
       __syncthreads();  // tile t landed; every wave is done with tile t-1 and the partials
-      issue(min(t + P - 1, n_tiles - 1), (t + P - 1) % P);
+      issue(t + P - 1, (t + P - 1) % P);
       compute(t, t % P);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
