@@ -53,9 +53,10 @@
 //    aligned: row i sits at key position i + N_kv - N_q.
 //  * Split of the key axis (SPLIT): blockIdx also selects one of n_splits
 //    contiguous ranges of the workgroup's key tiles, and the workgroup writes
-//    an fp32 partial result (O normalised by its own l, and log2 l + m) that
-//    the merge kernel combines through the log-sum-exps (page "Attention
-//    Kernel 实现与正确性验证", section 2.4, split-T with a safe-softmax merge).
+//    a partial result (O normalised by its own l, in bf16, and log2 l + m in
+//    fp32) that the merge kernel combines through the log-sum-exps (page
+//    "Attention Kernel 实现与正确性验证", section 2.4, split-T with a
+//    safe-softmax merge).
 //  * Pairs past the end are clamped to the last valid one on load (their
 //    outputs are not stored).  Each K/V tile is read through a buffer
 //    resource that ends at the head's last key, so key rows past N_kv come
@@ -334,8 +335,8 @@ __device__ __forceinline__ int v_swz(int row) {
 // the MFMAs) measured slower.
 // MN: MFMA size, 32 (v_mfma_f32_32x32x16_bf16: one 32-query column block per
 // wave) or 16 (v_mfma_f32_16x16x32_bf16: two 16-query column blocks).
-// SPLIT: write the fp32 partial result of one key range instead of the final
-// bf16 output.
+// SPLIT: write the partial result of one key range (bf16 O, fp32 log2-unit
+// LSE) instead of the final output.
 template <int D, int NW, int P, int QB, int BN_, int MN, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))

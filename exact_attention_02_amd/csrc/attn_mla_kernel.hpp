@@ -46,7 +46,7 @@ struct MlaParams {
   int B, H, S, T;
   int n_pairs;         // S * H
   int causal_off;      // T - S when causal, else 0
-  int n_pair_blocks;   // ceil(n_pairs / 32)
+  int n_pair_blocks;   // ceil(n_pairs / 64): workgroups per batch element and split
   int n_splits;
   float scale_log2;    // max(|sm_scale| log2 e, FLT_MIN)
   uint32_t q_sign;     // 0x80008000 when sm_scale < 0
