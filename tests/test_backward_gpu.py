@@ -429,3 +429,46 @@ def test_autograd_wrapper(ea, N_q, N_kv, D, causal):
     _check("dQ", qd.grad.cpu(), rq, f"autograd {N_q}x{N_kv} D{D}")
     _check("dK", kd.grad.cpu(), rk, f"autograd {N_q}x{N_kv} D{D}")
     _check("dV", vd.grad.cpu(), rv, f"autograd {N_q}x{N_kv} D{D}")
+
+
+def _draw_backward_cases(seed: int = 20261202, n: int = 12):
+    """Seeded random backward problems in four groups, so that every launch
+    shape runs: many kv heads with short rows (the eight-wave dQ kernel);
+    small square grids with a drawn row-range split count (the four-wave dQ
+    kernel, partial dK/dV sums); causal chunks with N_q < N_kv (bottom-right
+    mask); and square grids fed this library's own forward (chained)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kind = i % 4
+        D = int(rng.choice([64, 128]))
+        n_splits, chained = 0, False
+        if kind == 0:
+            B, H_kv, G = 2, 128, int(rng.choice([1, 2]))
+            N_q = int(rng.integers(65, 256 // G + 1))
+            N_kv = N_q if rng.random() < 0.5 else int(rng.integers(N_q, 400))
+            causal = bool(rng.random() < 0.3)
+        elif kind == 1:
+            B, H_kv, G = int(rng.integers(1, 3)), int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 4, 8]))
+            N_q = N_kv = int(rng.integers(2, 600))
+            causal = bool(rng.random() < 0.5)
+            n_splits = int(rng.choice([0, 1, 2, 3, 5]))
+        elif kind == 2:
+            B, H_kv, G = 1, int(rng.choice([2, 8])), int(rng.choice([1, 4]))
+            N_q = int(rng.integers(1, 300))
+            N_kv = int(rng.integers(N_q, 900))
+            causal = True
+        else:
+            B, H_kv, G = int(rng.integers(1, 3)), int(rng.choice([1, 4, 8])), int(rng.choice([1, 2, 4]))
+            N_q = N_kv = int(rng.integers(2, 500))
+            causal = bool(rng.random() < 0.5)
+            chained = True
+        cases.append((B, H_kv * G, H_kv, N_q, N_kv, D, causal, n_splits, chained, 9500 + i))
+    return cases
+
+
+@pytest.mark.parametrize("B,H_q,H_kv,N_q,N_kv,D,causal,n_splits,chained,seed", _draw_backward_cases())
+def test_backward_random_shapes(ea, B, H_q, H_kv, N_q, N_kv, D, causal, n_splits, chained, seed):
+    """dQ, dK and dV of every element against the oracle on a seeded random
+    shape (the draw is fixed, so the cases are the same on every run)."""
+    _case(ea, B, H_q, H_kv, N_q, N_kv, D, causal, seed=seed, chained=chained, n_splits=n_splits)
