@@ -235,3 +235,41 @@ def test_mla_deterministic(ea):
     a = _run_core(ea, q_lat, kv, 0.07, True, 0)
     b = _run_core(ea, q_lat, kv, 0.07, True, 0)
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+
+
+def _draw_mla_cases(seed: int = 20261203, n: int = 10):
+    """Seeded random MLA problems: batch, head count (not only multiples of
+    32), query tokens per step (bottom-right causal when S > 1), cache length
+    and split count (the library's or a forced one)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 4))
+        H = int(rng.choice([1, 5, 16, 40, 128]))
+        S = int(rng.integers(1, 5))
+        T = int(rng.integers(S, 2000))
+        causal = bool(rng.random() < 0.6)
+        n_splits = int(rng.choice([0, 1, 2, 5, 17]))
+        cases.append((B, H, S, T, causal, n_splits, 13600 + i))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,S,T,causal,n_splits,seed", _draw_mla_cases())
+def test_mla_random_shapes(ea, B, H, S, T, causal, n_splits, seed):
+    """The latent core against the oracle on a seeded random shape, then the
+    whole pipeline (absorb, core with the library's splits, up-projection)
+    against the naive definition on the same draw."""
+    sc = 1 / math.sqrt(192)
+    q_lat, kv = _latent_inputs(B, H, S, T, seed)
+    o, l = _run_core(ea, q_lat, kv, sc, causal, n_splits)
+    O, L = oracle.mla_latent_attention(_f64(q_lat), _f64(kv), 512, is_causal=causal, sm_scale=sc)
+    _check_attn(o, l, O, L, f"core B{B} H{H} S{S} T{T} c{int(causal)} s{n_splits}")
+    dev = _dev()
+    c_kv, k_pe, q_nope, q_pe, W_uk, W_uv = workloads.make_mla_inputs(B, H, S, T, seed)
+    kvd = torch.cat([c_kv, k_pe], dim=-1).contiguous()
+    out, _ = ea.mla_decode(q_nope.to(dev), q_pe.to(dev), kvd.to(dev), W_uk.to(dev), W_uv.to(dev),
+                           is_causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.mla_naive(_f64(c_kv), _f64(k_pe), _f64(q_nope), _f64(q_pe), _f64(W_uk), _f64(W_uv),
+                           is_causal=causal, sm_scale=sc)
+    _check_scaled(out.cpu(), ref, f"pipeline B{B} H{H} S{S} T{T} c{int(causal)}")
