@@ -172,8 +172,11 @@ extern "C" int mla_absorb_q(const void* q_nope, const void* q_pe, const void* w_
   hipStream_t s = static_cast<hipStream_t>(stream);
   // one block per (head, 128-column slice), every row of the head in it
   const int kp = static_cast<int>((d_nope + 15) & ~int64_t(15));
-  hipLaunchKernelGGL(ea02::mla_absorb_kernel, dim3(static_cast<unsigned>(H * (ea02::kMlaDc / ea02::kAbsorbSlice))),
-                     dim3(256), ea02::absorb_lds_bytes(kp), s, p);
+  const dim3 grid(static_cast<unsigned>(H * (ea02::kMlaDc / ea02::kAbsorbSlice)));
+  if (d_nope % 8 == 0 && (reinterpret_cast<uintptr_t>(q_nope) & 15) == 0)
+    hipLaunchKernelGGL(ea02::mla_absorb_kernel<true>, grid, dim3(256), ea02::absorb_lds_bytes(kp), s, p);
+  else
+    hipLaunchKernelGGL(ea02::mla_absorb_kernel<false>, grid, dim3(256), ea02::absorb_lds_bytes(kp), s, p);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_LAUNCH;
   return ATTN_OK;
 }

@@ -333,6 +333,9 @@ __device__ __forceinline__ int absorb_swz(int row) { return 4 * (row & 3) + ((ro
 // A = W^T from the LDS transpose read, B = the matching 8 values of d of a
 // query row staged in LDS (q_nope rows are only 2-byte aligned).  W_uk is
 // read from memory exactly once.  Dynamic LDS: absorb_lds_bytes(kp).
+// VEC_X: the query rows are loaded in 16-byte chunks (d_nope a multiple of 8
+// and q_nope 16-byte aligned), else value by value.
+template <bool VEC_X>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void mla_absorb_kernel(MlaProjParams p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t absorb_lds[];
   constexpr int n_cs = kMlaDc / kAbsorbSlice;
@@ -380,8 +383,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void mla_absor
   for (int r0 = 0; r0 < p.rows_per_head; r0 += 32) {
     __syncthreads();  // the W slice is staged; the previous rows are read
     // 32 query rows, zero past d_nope and past the last row; thread t takes
-    // row t / 8 and every 8th value of it
-    {
+    // row t / 8 and every 8th 16-byte chunk (VEC_X) or value of it
+    if constexpr (VEC_X) {
+      const int r = tid >> 3, c0 = tid & 7;
+      const int rr = r0 + r;
+      const bool live = rr < p.rows_per_head;
+      const uint16_t* xr = p.x + (live ? row_index(rr) * dn : 0);
+      u32x4 xc[kAbsorbMaxK / 64];
+#pragma unroll
+      for (int i = 0; i < kAbsorbMaxK / 64; ++i) {
+        const int c = c0 + 8 * i;
+        xc[i] = (live && 8 * c < dn) ? *reinterpret_cast<const u32x4*>(xr + 8 * c) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < kAbsorbMaxK / 64; ++i) {
+        const int c = c0 + 8 * i;
+        if (8 * c < kp) *reinterpret_cast<u32x4*>(xs + r * xstride + 8 * c) = xc[i];
+      }
+    } else {
       const int r = tid >> 3, d0 = tid & 7;
       const int rr = r0 + r;
       const bool live = rr < p.rows_per_head;

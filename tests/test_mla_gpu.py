@@ -172,21 +172,25 @@ def test_projections(ea):
     _check_scaled(y.cpu(), oracle.mla_up_project(_f64(x), _f64(W_uv)), "up")
 
 
+@pytest.mark.parametrize("offset", [1, 0])
 @pytest.mark.parametrize("d_nope,B,H,S", [(128, 1, 128, 1), (128, 32, 128, 1), (1, 2, 3, 1), (17, 5, 4, 7),
                                            (64, 3, 8, 12), (100, 1, 6, 70), (192, 2, 4, 33),
-                                           (256, 4, 5, 9)])
-def test_absorb_shapes(ea, d_nope, B, H, S):
+                                           (256, 4, 5, 9), (8, 3, 2, 40), (24, 2, 3, 5)])
+def test_absorb_shapes(ea, d_nope, B, H, S, offset):
     """mla_absorb_q over d_nope 1..256 (zero-padded to whole k-steps inside),
     row counts spanning several 32-row blocks with a ragged last one, and a
-    q_nope that starts 2 bytes past a 16-byte boundary."""
+    q_nope that starts 2 bytes past a 16-byte boundary (offset 1: the
+    value-by-value query loads) or on one (offset 0: 16-byte query loads
+    where d_nope is a multiple of 8)."""
     dev = _dev()
     g = torch.Generator(device="cpu")
     g.manual_seed(13400 + d_nope + B * H * S)
     q_nope = torch.randn((B, H, S, d_nope), generator=g).to(torch.bfloat16)
     q_pe = torch.randn((B, H, S, 64), generator=g).to(torch.bfloat16)
     W_uk = (torch.randn((H, d_nope, 512), generator=g) / math.sqrt(d_nope)).to(torch.bfloat16)
-    buf = torch.empty(q_nope.numel() + 1, dtype=torch.bfloat16, device=dev)
-    qn = buf[1:].view(q_nope.shape)
+    buf = torch.empty(q_nope.numel() + 8, dtype=torch.bfloat16, device=dev)
+    assert buf.data_ptr() % 16 == 0
+    qn = buf[offset:offset + q_nope.numel()].view(q_nope.shape)
     qn.copy_(q_nope.to(dev))
     q_lat = torch.full((B, H, S, 576), float("nan"), dtype=torch.bfloat16, device=dev)
     ea.mla_absorb_q(qn, q_pe.to(dev), W_uk.to(dev), q_lat)
