@@ -18,6 +18,11 @@ inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// A dispatch counts its work-items in 32 bits.  Most workgroups a launch of
+// `threads`-thread workgroups may take, leaving room for the spare workgroups
+// of work stealing (plan_steal adds at most a tenth plus 8).
+inline int64_t max_launch_blocks(int64_t threads) { return (int64_t(UINT32_MAX) / threads - 8) * 8 / 9; }
+
 // Compute units of the current device; 256 (MI355X) when the runtime cannot
 // say (e.g. no device visible, as in argument-check tests on a CPU host).
 inline int device_cus() {

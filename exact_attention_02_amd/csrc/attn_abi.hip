@@ -68,6 +68,8 @@ int64_t splits_for(const Shape& sh, int64_t wgs, int64_t n_kv) {
   int64_t n = (target + wgs - 1) / wgs;
   n = std::min<int64_t>(n, tiles / 8);
   n = std::min<int64_t>(n, kMaxSplits);
+  // the split grid stays within one dispatch
+  n = std::min<int64_t>(n, ea02::abi::max_launch_blocks(64 * kWideNW) / wgs);
   return n < 1 ? 1 : n;
 }
 
@@ -88,6 +90,10 @@ Shape pick_shape(int64_t n_pairs, int64_t D, int64_t n_heads, int64_t N_q, int64
   if (causal && 2 * N_q > N_kv && wide_wgs < 2 * cus) return kMidShape;
   if (wide_wgs * splits_for(kWideShape, wide_wgs, N_kv) < cus) return kMidShape;
   return kWideShape;
+}
+
+int shape_threads(Kind kind) {
+  return 64 * (kind == Kind::kNarrow ? kNarrowNW : kind == Kind::kMid ? kMidNW : kWideNW);
 }
 
 template <int D, bool SPLIT>
@@ -154,7 +160,7 @@ int check_sizes(const Problem& a, int64_t n_splits, bool* empty) {
   const Shape sh = problem_shape(a);
   const int64_t grid = ((n_pairs + sh.pairs_per_wg - 1) / sh.pairs_per_wg) * a.B * a.H_kv *
                        (n_splits > 1 ? n_splits : 1);
-  if (grid > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
+  if (grid > ea02::abi::max_launch_blocks(shape_threads(sh.kind))) return ATTN_ERR_SIZE_OVERFLOW;
   if (a.B == 0 || a.H_q == 0 || a.N_q == 0) {
     *empty = true;
     return ATTN_OK;

@@ -81,7 +81,13 @@ int check_sizes(const Shape& a, int64_t n_splits, float sm_scale, bool* empty) {
   // the smaller dQ pair blocks give the larger grid
   const int64_t pair_blocks = (a.N_q * G + 32 * kQMidNW - 1) / (32 * kQMidNW);
   const int64_t splits = n_splits > 1 ? n_splits : 1;
-  if (a.B * a.H_kv * key_blocks * splits > INT32_MAX || a.B * a.H_kv * pair_blocks > INT32_MAX)
+  // every launch within one dispatch's 32-bit work-item count: dK/dV, dQ
+  // (two threads per pair in either shape) and the prep kernel (D/8 threads
+  // per row)
+  const int64_t prep_blocks = (a.B * a.H_q * a.N_q * (a.D / 8) + 255) / 256;
+  if (a.B * a.H_kv * key_blocks * splits > ea02::abi::max_launch_blocks(64 * kKvNW) ||
+      a.B * a.H_kv * pair_blocks > ea02::abi::max_launch_blocks(64 * kQMidNW) ||
+      prep_blocks > ea02::abi::max_launch_blocks(256))
     return ATTN_ERR_SIZE_OVERFLOW;
   if (a.B == 0 || a.H_q == 0 || (a.N_q == 0 && a.N_kv == 0)) *empty = true;
   return ATTN_OK;
@@ -117,7 +123,7 @@ int64_t choose_kv_splits(const Shape& a) {
   n = std::min({n, tiles_max, kMaxBwdSplits});
   const int64_t plane2 = 2 * heads * a.N_kv * a.D * 4;
   n = std::min(n, kAutoPartBytes / plane2);
-  n = std::min(n, int64_t(INT32_MAX) / (heads * key_blocks));  // the grid stays below 2^31
+  n = std::min(n, ea02::abi::max_launch_blocks(64 * kKvNW) / (heads * key_blocks));  // one dispatch
   return worth_splitting(n, tiles_max, share, double(plane2), double(plane2) / 2);
 }
 
@@ -150,7 +156,7 @@ int64_t choose_q_splits_nw(const Shape& a, int nw) {
   n = std::min({n, tiles_max, kMaxBwdSplits});
   const int64_t plane = a.B * a.H_q * a.N_q * a.D * 4;
   n = std::min(n, kAutoPartBytes / plane);
-  n = std::min(n, int64_t(INT32_MAX) / (heads * pair_blocks));
+  n = std::min(n, ea02::abi::max_launch_blocks(64 * nw) / (heads * pair_blocks));
   return worth_splitting(n, tiles_max, share, double(plane), double(plane) / 2);
 }
 

@@ -43,7 +43,7 @@ int mla_check_sizes(int64_t B, int64_t H, int64_t S, int64_t T, int64_t d_c, int
       S * H > (int64_t(1) << 30) || B * H * S > INT32_MAX)
     return ATTN_ERR_SIZE_OVERFLOW;
   const int64_t pbs = (S * H + kMlaPairs - 1) / kMlaPairs;
-  if (pbs * B * std::max<int64_t>(n_splits, 1) > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
+  if (pbs * B * std::max<int64_t>(n_splits, 1) > ea02::abi::max_launch_blocks(256)) return ATTN_ERR_SIZE_OVERFLOW;
   return ATTN_OK;
 }
 
@@ -187,8 +187,9 @@ extern "C" int mla_up_project(const void* out_lat, const void* w_uv, void* out, 
   if (d_c != ea02::kMlaDc || d_v < 32 || d_v > 1024 || d_v % 32 != 0) return ATTN_ERR_HEAD_DIM;
   if (B > (1 << 24) || H > (1 << 16) || S > (1 << 24) || B * S > INT32_MAX / 2 || B * H * S > INT32_MAX)
     return ATTN_ERR_SIZE_OVERFLOW;
+  // a dispatch counts its work-items in 32 bits
   const int64_t blocks = (B * S + 31) / 32 * H * (d_v / 32);
-  if (blocks > INT32_MAX) return ATTN_ERR_SIZE_OVERFLOW;
+  if (blocks > ea02::abi::max_launch_blocks(64)) return ATTN_ERR_SIZE_OVERFLOW;
   if (B == 0 || H == 0 || S == 0) return ATTN_OK;
   if (!out_lat || !w_uv || !out) return ATTN_ERR_NULL_POINTER;
   if (mis16(out_lat) || mis16(w_uv) || (reinterpret_cast<uintptr_t>(out) & 1u)) return ATTN_ERR_ALIGNMENT;

@@ -53,7 +53,9 @@ enum attn_status {
   ATTN_ERR_SCALE = 5,          /* sm_scale is NaN or infinite                  */
   ATTN_ERR_SIZE_OVERFLOW = 6,  /* N > 2^24, N*D*2 > 2^31 (one kv head's K rows
                                   take 32-bit byte offsets), B*H_q*N >= 2^31,
-                                  or the launch grid exceeds 2^31-1           */
+                                  or a launch would pass one dispatch's 2^32
+                                  work-items (with room for the spare
+                                  workgroups of work stealing)                */
   ATTN_ERR_NULL_POINTER = 7,   /* a buffer pointer is NULL for non-empty work  */
   ATTN_ERR_ALIGNMENT = 8,      /* q,k,v,out not 16-byte or lse not 4-byte aligned */
   ATTN_ERR_ALIAS = 9,          /* out or lse overlaps an input or each other   */
@@ -153,7 +155,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  *   NEGATIVE_SIZE (any size or n_splits < 0), HEAD_RATIO, HEAD_DIM,
  *   CAUSAL_FLAG, SCALE, SPLITS (n_splits > 256), CAUSAL_SHAPE (is_causal and
  *   N_q > N_kv), SIZE_OVERFLOW (N_q or N_kv > 2^24, N_kv * D * 2 > 2^31,
- *   B * H_q * N_q >= 2^31, N_q * H_q / H_kv > 2^30, grid >= 2^31), then empty work (B, H_q or N_q = 0) returns ATTN_OK, then
+ *   B * H_q * N_q >= 2^31, N_q * H_q / H_kv > 2^30, a launch past 2^32 work-items), then empty work (B, H_q or N_q = 0) returns ATTN_OK, then
  *   NO_KEYS (N_kv = 0), NULL_POINTER, ALIGNMENT, WORKSPACE, ALIAS (out, lse
  *   or the used workspace overlapping an input or each other), LAUNCH.
  */
@@ -257,7 +259,7 @@ size_t attn_splitkv_workspace_size(int64_t B, int64_t H_q, int64_t N_q, int64_t 
  *   NEGATIVE_SIZE (any size or n_splits < 0), HEAD_RATIO, HEAD_DIM,
  *   CAUSAL_FLAG, SCALE, SPLITS (n_splits > 64), CAUSAL_SHAPE, SIZE_OVERFLOW
  *   (N_q or N_kv > 2^24, N_kv*D*2 > 2^31, N_q*(H_q/H_kv)*D*2 > 2^31,
- *   B*H_q*N_q >= 2^31, grid >= 2^31), then empty work (B or H_q = 0, or
+ *   B*H_q*N_q >= 2^31, a launch past 2^32 work-items), then empty work (B or H_q = 0, or
  *   N_q = N_kv = 0) returns ATTN_OK, then NO_KEYS (N_kv = 0 < N_q),
  *   NULL_POINTER (q, out, dout, lse, dq may be NULL only when N_q = 0),
  *   ALIGNMENT (16 bytes, lse 4), WORKSPACE, ALIAS (dq, dk, dv or the workspace

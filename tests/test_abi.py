@@ -119,6 +119,10 @@ def call_split(lib, q=Q, k=K, v=V, o=O, l=L, B=1, H_q=4, H_kv=2, N_q=16, N_kv=40
     (dict(causal=1, N_q=41, N_kv=40), "ATTN_ERR_CAUSAL_SHAPE"),
     (dict(N_kv=(1 << 24) + 1), "ATTN_ERR_SIZE_OVERFLOW"),
     (dict(N_q=(1 << 24), H_q=128, H_kv=1), "ATTN_ERR_SIZE_OVERFLOW"),
+    # 2^20 one-wave decode workgroups times 256 forced splits: 2^34 work-items
+    (dict(B=1 << 14, H_q=64, H_kv=64, N_q=1, N_kv=1, n_splits=256), "ATTN_ERR_SIZE_OVERFLOW"),
+    # the same at 16 splits fits one dispatch; its workspace is what is short
+    (dict(B=1 << 14, H_q=64, H_kv=64, N_q=1, N_kv=1, n_splits=16), "ATTN_ERR_WORKSPACE"),
     (dict(N_kv=0), "ATTN_ERR_NO_KEYS"),
     (dict(v=0), "ATTN_ERR_NULL_POINTER"),
     (dict(q=Q + 4), "ATTN_ERR_ALIGNMENT"),
@@ -224,6 +228,10 @@ def call_bwd(lib, q=Q, k=K, v=V, o=O, do=DO, l=L, dq=DQ, dk=DK, dv=DV, B=1, H_q=
     (dict(causal=1, N_q=41), "ATTN_ERR_CAUSAL_SHAPE"),
     (dict(N_kv=(1 << 23) + 1, D=128), "ATTN_ERR_SIZE_OVERFLOW"),
     (dict(N_q=1 << 20, H_q=16, H_kv=1, D=128, N_kv=1 << 20), "ATTN_ERR_SIZE_OVERFLOW"),
+    # 2^29 query rows: the prep kernel's 8 threads per row pass one dispatch
+    (dict(N_q=1 << 24, N_kv=1 << 24, H_q=32, H_kv=32, D=64), "ATTN_ERR_SIZE_OVERFLOW"),
+    # 2^28 rows fit one dispatch; the workspace is what is short
+    (dict(N_q=1 << 24, N_kv=1 << 24, H_q=16, H_kv=16, D=64), "ATTN_ERR_WORKSPACE"),
     (dict(N_kv=0), "ATTN_ERR_NO_KEYS"),
     (dict(do=0), "ATTN_ERR_NULL_POINTER"),
     (dict(dv=0), "ATTN_ERR_NULL_POINTER"),
@@ -315,6 +323,9 @@ def call_mla(lib, q=QL, kv=KVC, o=OL, l=LL, B=1, H=16, S=1, T=100, d_c=512, d_r=
     (dict(n_splits=300), "ATTN_ERR_SPLITS"),
     (dict(S=101), "ATTN_ERR_CAUSAL_SHAPE"),
     (dict(T=(1 << 21)), "ATTN_ERR_SIZE_OVERFLOW"),
+    # 2^17 pair blocks times 128 splits: 2^24 workgroups of 256 work-items
+    (dict(B=1 << 16, H=128, n_splits=128), "ATTN_ERR_SIZE_OVERFLOW"),
+    (dict(B=1 << 16, H=128, n_splits=64), "ATTN_ERR_WORKSPACE"),
     (dict(scale=float("inf")), "ATTN_ERR_SCALE"),
     (dict(T=0, causal=0), "ATTN_ERR_NO_KEYS"),
     (dict(kv=0), "ATTN_ERR_NULL_POINTER"),
@@ -349,6 +360,11 @@ def test_mla_projection_arguments_rejected(lib):
     assert lib.mla_up_project(QL + 4, WM, OL, 1, 4, 1, 512, 128, None) == STATUS["ATTN_ERR_ALIGNMENT"]
     assert lib.mla_up_project(QL, WM, WM, 1, 4, 1, 512, 128, None) == STATUS["ATTN_ERR_ALIAS"]
     assert lib.mla_up_project(QL, WM, OL, -1, 4, 1, 512, 128, None) == STATUS["ATTN_ERR_NEGATIVE_SIZE"]
+    # 2^26 rows with d_v = 1024: 2^26 one-wave blocks, 2^32 work-items, past a
+    # dispatch's 32-bit work-item count
+    assert lib.mla_up_project(QL, WM, OL, 1 << 17, 512, 1, 512, 1024, None) == STATUS["ATTN_ERR_SIZE_OVERFLOW"]
+    # 2^25 blocks (d_v = 512) fit: the call gets past the size checks to the NULL output
+    assert lib.mla_up_project(QL, WM, 0, 1 << 17, 512, 1, 512, 512, None) == STATUS["ATTN_ERR_NULL_POINTER"]
     assert ok
 
 
