@@ -523,7 +523,7 @@ def main():
             roof = {"bound": "mfma", "achieved": round(tfs, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(mfma_frac, 4)}
         roof.update({"traffic": traffic, "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
-                     "kernel": "attn_mla_decode (attn_mla_kernel split pass + merge)",
+                     "kernel": "attn_mla_decode (latent-core split pass + merge)",
                      "median_launch_ms": round(r["core_ms"], 5), "n_splits": r["n_splits"],
                      "algorithmic_bytes_per_launch": mw.core_bytes(),
                      "algorithmic_flops_per_launch": mw.core_flops()})

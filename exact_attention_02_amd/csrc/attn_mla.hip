@@ -47,8 +47,21 @@ int mla_check_sizes(int64_t B, int64_t H, int64_t S, int64_t T, int64_t d_c, int
   return ATTN_OK;
 }
 
+// (token, head) pairs per workgroup of the latent core that serves this shape
+// (token, head) pairs per workgroup of the latent core that serves this
+// shape: the sixteen-pair kernel (128 per workgroup, two waves per SIMD) once
+// its workgroups, before any split, number at least an eighth of the CUs;
+// below that it would need twice the splits of the four-wave kernel (64 per
+// workgroup), whose partial outputs and re-read queries then cost more than
+// its latency saves (measured at B = 1 and 8 with H = 128, S = 1).
+int64_t mla_core_pairs(int64_t B, int64_t H, int64_t S) {
+  const int64_t wide_wgs = ((S * H + ea02::kMla16Pairs - 1) / ea02::kMla16Pairs) * B;
+  return 8 * wide_wgs >= device_cus() ? ea02::kMla16Pairs : kMlaPairs;
+}
+
 int64_t mla_choose_splits(int64_t B, int64_t H, int64_t S, int64_t T) {
-  const int64_t wgs = ((S * H + kMlaPairs - 1) / kMlaPairs) * B;
+  const int64_t pairs = mla_core_pairs(B, H, S);
+  const int64_t wgs = ((S * H + pairs - 1) / pairs) * B;
   const int64_t cus = device_cus();
   if (wgs <= 0 || wgs >= cus) return 1;
   const int64_t tiles = (T + 31) / 32;
@@ -109,7 +122,9 @@ extern "C" int attn_mla_decode(const void* q_lat, const void* kv, void* out_lat,
   p.T = static_cast<int>(T);
   p.n_pairs = static_cast<int>(S * H);
   p.causal_off = is_causal ? static_cast<int>(T - S) : 0;
-  p.n_pair_blocks = static_cast<int>((S * H + kMlaPairs - 1) / kMlaPairs);
+  const int64_t pairs = mla_core_pairs(B, H, S);
+  const bool wide = pairs == ea02::kMla16Pairs;
+  p.n_pair_blocks = static_cast<int>((S * H + pairs - 1) / pairs);
   p.n_splits = split ? static_cast<int>(ns) : 1;
   p.scale_log2 = std::fmax(std::fabs(sm_scale) * ea02::kLog2e, FLT_MIN);
   p.q_sign = (sm_scale < 0.f) ? 0x80008000u : 0u;
@@ -117,7 +132,11 @@ extern "C" int attn_mla_decode(const void* q_lat, const void* kv, void* out_lat,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(int64_t(p.n_pair_blocks) * B * p.n_splits));
-  if (split)
+  if (wide && split)
+    hipLaunchKernelGGL((ea02::attn_mla16_kernel<kMlaP, true>), grid, dim3(512), 0, s, p);
+  else if (wide)
+    hipLaunchKernelGGL((ea02::attn_mla16_kernel<kMlaP, false>), grid, dim3(512), 0, s, p);
+  else if (split)
     hipLaunchKernelGGL((ea02::attn_mla_kernel<kMlaP, true>), grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((ea02::attn_mla_kernel<kMlaP, false>), grid, dim3(256), 0, s, p);

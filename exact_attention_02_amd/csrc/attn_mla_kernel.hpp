@@ -22,6 +22,10 @@
 //    bf16-rounded S^T accumulator.
 // A wave thus holds 18 query k-steps and 256 value dims: 72 + 128 registers,
 // where all 36 k-steps and 512 dims of a pair block in one wave would not fit.
+//
+// attn_mla16_kernel (below): the same computation with 16 pairs per wave,
+// eight waves of two per SIMD and no exchange; the host takes it when the
+// batch fills at least an eighth of the CUs before any split.
 #pragma once
 
 #include "attn_fwd_kernel.hpp"
@@ -78,6 +82,21 @@ __device__ __forceinline__ void scale_agpr(f32x16& acc, float alpha) {
                  : "v"(alpha));
     acc[r] = x;
   }
+}
+
+// The sixteen-pair kernel's (pair block, batch element, split).  Workgroup
+// ids go round-robin over the 8 XCDs; they are renumbered so that each XCD
+// takes a contiguous run of items, pair block fastest, then split: the pair
+// blocks of one (batch, split) read the same cache tiles, and the splits of
+// one pair block the same queries, through one XCD's L2 (B = 32: 8 % faster
+// than the plain order).  The four-wave kernel keeps the plain order: this
+// one measured 11 % slower for it at B = 1, T = 16384.
+__device__ __forceinline__ int3 mla_item(const MlaParams& p) {
+  const int nwg = gridDim.x;
+  const int id = (nwg & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (nwg >> 3) + (int)(blockIdx.x >> 3);
+  const int pb = id % p.n_pair_blocks;
+  const int r = id / p.n_pair_blocks;
+  return int3{pb, r / p.n_splits, r % p.n_splits};
 }
 
 template <int P, bool SPLIT>
@@ -299,6 +318,224 @@ void attn_mla_kernel(MlaParams p) {
         *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4));
       }
     if (kh == 0 && half == 0) p.lse_part[slot] = seen ? m_used + __log2f(l_tot) : -INFINITY;
+  }
+}
+
+// ------------------------------------------------- sixteen-pair latent core
+// attn_mla16_kernel: the same latent attention with v_mfma_f32_16x16x32_bf16
+// and no exchange between waves.  A workgroup of eight waves (two per SIMD)
+// owns 128 (query token, head) pairs, 16 per wave, and streams 32-key tiles
+// through a 4-stage LDS ring.  Each wave holds all 576 score dims of its
+// pairs (18 k-steps of 32: 72 registers of queries) and all 512 value dims
+// (32 blocks of 16: 128 accumulator registers), so its softmax needs only
+// its own S^T and no barrier sits between the score and value products.
+// Against the four-wave form it reads twice the LDS operand bytes per MFMA,
+// and in exchange a second wave on each SIMD covers the latency of the
+// other's chain.
+//
+// Lane l owns pair 16 w + (l & 15) and k-group g = l >> 4.  S^T for key
+// block c (16 keys) is K Q^T with A = 16 key rows at dims 32 ks + 8 g .. +8
+// and B = the pair's query at the same dims; the accumulator holds keys
+// 16 c + 4 g + r.  P^T's B operand is then this lane's own 8 scores (keys
+// 4 g + r and 16 + 4 g + r), and V^T's A operand the two transpose reads of
+// rows 4 g + L / 4 and 16 + 4 g + L / 4 (L = l & 15) at dims 16 db + 4 (L & 3).
+//
+// Swizzle: chunk j of row r is stored at j ^ mla16_swz(r).  With rows 1152
+// bytes apart, rows of one parity share a 128-byte bank half, so the 16-row
+// K reads need the swizzle to be a bijection on row bits 1..3, the
+// transpose reads (a half wave: 8 aligned rows x 2 adjacent chunks) need bits
+// 1..2 of it distinct over the 4 rows of a parity, and rows r and r + 8
+// take chunks that differ in more than bit 0.
+__device__ __forceinline__ int mla16_swz(int row) {
+  const int a = (row >> 1) & 7;
+  return (2 * (a & 3) ^ (6 * (a >> 2))) | (a >> 2);
+}
+
+constexpr int kMla16Pairs = 128;  // (token, head) pairs per workgroup of attn_mla16_kernel
+
+template <int P, bool SPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void attn_mla16_kernel(MlaParams p) {
+  constexpr int NW = 8;
+  constexpr int BN = 32;
+  constexpr int TILE_BYTES = BN * kMlaRowBytes;          // 36 KiB
+  constexpr int LOADS = TILE_BYTES / 1024;               // 36 loads of 1 KiB per tile
+  constexpr int LPW = (LOADS + NW - 1) / NW;             // 5 per wave; the 4 spare ones move nothing
+  constexpr int KS = kMlaDqk / 32;                       // 18 score k-steps
+  constexpr int NDB = kMlaDc / 16;                       // 32 value blocks
+  constexpr int PPW = 16 * NW;                           // pairs per workgroup
+  constexpr int JUNK = P * TILE_BYTES;                   // landing area of the spare loads
+  static_assert(PPW == kMla16Pairs && (P - 1) * LPW <= 63, "load groups");
+  static_assert(JUNK + 1024 <= 160 * 1024, "LDS fits the 160 KiB of a CU");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[JUNK + 1024];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+
+  const int3 item = mla_item(p);
+  const int pb = item.x, b = item.y, split = SPLIT ? item.z : 0;
+  const int T = p.T;
+  const int off = p.causal_off;
+  const int last_pair = p.n_pairs - 1;
+  const int P0 = pb * PPW;
+  const int wp0 = P0 + 16 * wave;
+  const int wave_row0 = min(wp0, last_pair) / p.H;
+  const int row_end = min(P0 + PPW - 1, last_pair) / p.H + 1;
+
+  const int kv_end = p.causal ? min(row_end + off, T) : T;
+  int n_tiles = (kv_end + BN - 1) / BN;
+  int kbase = 0;
+  if constexpr (SPLIT) {
+    const int per = (n_tiles + p.n_splits - 1) / p.n_splits;
+    const int t0 = min(split * per, n_tiles);
+    n_tiles = min(per, n_tiles - t0);
+    kbase = t0 * BN;
+  }
+
+  const int pair = wp0 + col;
+  const bool valid = pair <= last_pair;
+  const int pc = min(pair, last_pair);
+  const int my_row = pc / p.H;
+  const int h = pc - my_row * p.H;
+  const size_t bhr = ((size_t)b * p.H + h) * (size_t)p.S + my_row;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int i = 0; i < KS; ++i) {
+    u32x4 x = *reinterpret_cast<const u32x4*>(p.q + bhr * kMlaDqk + 32 * i + 8 * kg);
+    x ^= p.q_sign;
+    qf[i] = as_bf16x8(x);
+  }
+
+  // Tile loads: load slot gi = LPW wave + i moves bytes [1024 gi, +1024) of
+  // the tile (lane -> row, stored chunk j; it fetches chunk j ^ swz(row)).
+  // The resource starts at the tile's first key and ends at the cache's last
+  // byte, so rows past T read as zeros (they are masked); slots gi >= LOADS
+  // and tiles past the last get an empty resource and land in the junk area.
+  const uint8_t* kv_b = reinterpret_cast<const uint8_t*>(p.kv + (size_t)b * T * kMlaDqk);
+  const u32x4 rsrc_none = make_rsrc(p.kv, 0u);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
+  int ld_off[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int e = min((wave * LPW + i) * 64 + lane, LOADS * 64 - 1);
+    const int row = e / kMlaChunks;
+    const int j = e - row * kMlaChunks;
+    ld_off[i] = row * kMlaRowBytes + ((j ^ mla16_swz(row)) << 4);
+  }
+  auto issue = [&](int t, int slot) {
+    const int key0 = kbase + t * BN;
+    const u32x4 rs = t < n_tiles ? make_rsrc(kv_b + (size_t)key0 * kMlaRowBytes, (uint32_t)(T - key0) * kMlaRowBytes)
+                                 : rsrc_none;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int gi = wave * LPW + i;
+      const bool real = gi < LOADS;
+      dma_16B(real ? rs : rsrc_none, ld_off[i], lds_base + (real ? slot * TILE_BYTES + gi * 1024 : JUNK));
+    }
+  };
+
+  // operand offsets inside a tile (the ring slot's base is added per tile)
+  const int ksw = mla16_swz(col);
+  int k_off[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) k_off[e] = col * kMlaRowBytes + (((4 * e + kg) ^ ksw) << 4);
+  const int vrow = 4 * kg + (col >> 2);
+  const int vsw = mla16_swz(vrow);
+  const int xlow = (col & 3) >> 1;
+  int v_off[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v_off[e] = vrow * kMlaRowBytes + (((2 * e + xlow) ^ vsw) << 4) + 8 * (col & 1);
+
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
+  float m_used = -INFINITY, l_run = 0.f;
+  const float sl2 = p.scale_log2;
+
+  auto compute = [&](int t, int slot) {
+    const uint8_t* kt = lds + slot * TILE_BYTES;
+    f32x4 s0 = f32x4{}, s1 = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint8_t* a = kt + k_off[ks & 1] + 128 * (ks >> 1);
+      const bf16x8 k0 = as_bf16x8(*reinterpret_cast<const u32x4*>(a));
+      const bf16x8 k1 = as_bf16x8(*reinterpret_cast<const u32x4*>(a + 16 * kMlaRowBytes));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s1, 0, 0, 0);
+    }
+    const int key0 = kbase + t * BN;
+    if ((p.causal && key0 + BN - 1 > wave_row0 + off) || key0 + BN > T) {
+      const int lim = (p.causal ? min(my_row + off + 1, T) : T) - key0 - 4 * kg;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r >= lim) s0[r] = -INFINITY;
+        if (16 + r >= lim) s1[r] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3]));
+    mx = fmaxf(mx, fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    const float mt = col_max<16>(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mt > m_used + kRescaleSlack)) {
+      const float m_new = fmaxf(m_used, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_used - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      m_used = m_new;
+    }
+    const float m_sub = (m_used == -INFINITY) ? 0.f : m_used;
+    f32x8 pf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pf[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], sl2, -m_sub));
+      pf[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], sl2, -m_sub));
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) l_run += pf[r];
+    const bf16x8 pbf = __builtin_convertvector(pf, bf16x8);
+    // O^T += V^T P^T over all 512 value dims
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint8_t* a = kt + v_off[db & 3] + 128 * (db >> 2);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + 16 * kMlaRowBytes));
+      const bf16x8 vT = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vT, pbf, acc[db], 0, 0, 0);
+    }
+  };
+
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int j = 0; j < P - 1; ++j) issue(j, j);
+    for (int t = 0; t < n_tiles; ++t) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((P - 2) * LPW) : "memory");
+      __syncthreads();  // tile t landed; every wave is done with tile t-1
+      issue(t + P - 1, (t + P - 1) % P);
+      compute(t, t % P);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  const float l_tot = col_sum<16>(l_run);
+  if (!valid) return;
+  const bool seen = l_tot > 0.f;
+  const float inv = SPLIT ? (seen ? 1.f / l_tot : 0.f) : 1.f / l_tot;
+  uint16_t* orow;
+  if constexpr (SPLIT) orow = p.o_part + ((size_t)split * ((size_t)p.B * p.H * p.S) + bhr) * kMlaDc;
+  else orow = p.o + bhr * kMlaDc;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const f32x4 f = {acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv};
+    *reinterpret_cast<u32x2*>(orow + 16 * db + 4 * kg) = __builtin_bit_cast(u32x2, __builtin_convertvector(f, bf16x4));
+  }
+  if (kg == 0) {
+    if constexpr (SPLIT)
+      p.lse_part[(size_t)split * ((size_t)p.B * p.H * p.S) + bhr] = seen ? m_used + __log2f(l_tot) : -INFINITY;
+    else
+      p.lse[bhr] = (m_used + __log2f(l_tot)) * kLn2;
   }
 }
 

@@ -121,16 +121,36 @@ def test_latent_core_heads_and_tokens(ea, H, S, T, n_splits):
         _check_attn(o, l, O, L, f"H{H} S{S} T{T} c{int(causal)}")
 
 
+# Shapes whose workgroups before any split (B times ceil(S H / 128)) number at
+# least an eighth of the CUs: on a 256-CU MI355X the latent core runs them
+# with its sixteen-pair kernel (128 pairs per workgroup), the others with the
+# four-wave kernel (64 pairs).
+@pytest.mark.parametrize("B,H,S,T,causal,n_splits,scale", [
+    (32, 16, 3, 65, True, 1, 0.07), (32, 16, 3, 65, False, 3, 0.07), (32, 128, 1, 31, True, 0, 0.07),
+    (40, 128, 2, 129, True, 0, 0.07), (33, 7, 5, 1000, True, 7, 0.07), (33, 7, 5, 1000, False, 0, -0.05),
+    (32, 40, 3, 300, True, 2, 0.3)])
+def test_latent_core_sixteen_pair_shapes(ea, B, H, S, T, causal, n_splits, scale):
+    """Ragged cache ends, several pair blocks per batch element, bottom-right
+    causal query tokens, forced and library split counts, grids that are and
+    are not a multiple of the 8 XCDs, a negative scale."""
+    q_lat, kv = _latent_inputs(B, H, S, T, seed=13700 + B + H + S + T)
+    o, l = _run_core(ea, q_lat, kv, scale, causal, n_splits)
+    O, L = oracle.mla_latent_attention(_f64(q_lat), _f64(kv), 512, is_causal=causal, sm_scale=scale)
+    _check_attn(o, l, O, L, f"B{B} H{H} S{S} T{T} c{int(causal)} s{n_splits}")
+
+
+@pytest.mark.parametrize("B", [1, 32])
 @pytest.mark.parametrize("n_splits", [1, 2])
-def test_latent_core_growing_scores(ea, n_splits):
+def test_latent_core_growing_scores(ea, n_splits, B):
     """Cache rows whose norm grows along T: the running max of a row rises
     by more than the lazy-rescale slack (8 in log2 units) on many tiles, so
     the accumulators are rescaled again and again.  The inputs are checked
     on the CPU to force at least 4 such rises for every row (the max over a
     32-key tile against the largest max so far plus 8, in fp64)."""
-    B, H, S, T = 1, 64, 1, 1024
+    H, S, T = 64, 1, 1024
     q_lat, kv = _latent_inputs(B, H, S, T, seed=13300)
-    ramp = torch.linspace(0.1, 6.0, T).view(1, T, 1)
+    # the steeper ramp at B = 32 gives every one of its rows the 4 rises too
+    ramp = torch.linspace(0.1, 6.0 if B == 1 else 8.0, T).view(1, T, 1)
     kv = (kv.float() * ramp).to(torch.bfloat16)
     sc = 0.3
     s2 = np.einsum("bhsd,btd->bhst", _f64(q_lat), _f64(kv)) * sc / math.log(2)
